@@ -1,0 +1,252 @@
+"""CPU oracle for tree-verify MLA-absorb attention (test infrastructure only).
+
+This module is the correctness reference for the HIP library.  It is plain,
+slow and written to be checked by eye: float64 numpy, one sequence at a time,
+no blocking, no fusion.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path never does.
+It shares no code with the HIP path (the only common module is the seeded input
+generator, which holds no attention arithmetic).
+
+Pages cited (titles of the four pages; sections in quotes):
+  [Checkpoint]   "The Checkpoint: Committing a Working Native DDTree Engine"
+  [Milestone]    "The Milestone Commit: Cementing a Native DDTree Inference Engine"
+  [Final]        "The Final Commit: Cementing a Native DDTree Inference Engine for Kimi K2.6"
+
+What is computed, and where it comes from:
+  * Visibility: each tree node's ancestor-or-self bitmask, built as
+    mask(node) = mask(parent) | bit(node), packed into 64-bit words with two
+    words covering up to 65 nodes [Milestone, "The Reasoning Behind the
+    Architecture", ancestor-bitmask visibility].
+  * Verify attention: the q_len = 1 + drafts tree tokens attend over the
+    cached prefix (all visible) followed by the tree itself (visible iff the
+    key node is an ancestor-or-self of the query node): mask = [ones |
+    visibility], prefix = cache length, and AR decoding is the q_len = 1 case
+    [Checkpoint, "The Message", KV-cache scheme].  Scores are in the absorbed
+    (latent) form: the query has been multiplied by w_kc upstream, so the
+    score of key j is scale * (q_lat . c_kv[j] + q_pe . k_pe[j]) and the
+    output is the latent context sum_j softmax_j * c_kv[j]; w_vc is applied
+    downstream [Final, "Input Knowledge Required", MLA absorb form;
+    Checkpoint, "The Message", absorb_qk/vc].  The per-row log-sum-exp is
+    returned beside it (natural log, scale included).
+  * Partial merge: attention over a key set split into chunks recombines from
+    per-chunk (normalised output, log-sum-exp) pairs by the log-sum-exp
+    identity.  The pages do not describe this step; it is the plain identity
+    that makes split-prefix attention exact.
+  * Accepted-path gather: after acceptance, the accepted path's latents are
+    gathered into the rows directly after the prefix ("after accept gather
+    accepted-path latents", post-verify compaction) [Checkpoint, "The
+    Message"].
+
+Readings where the pages are silent (each also listed in the design notes):
+  * Tree node t's latents sit in cache row L_b + t (node order); its position
+    L_b + depth(t) only matters to RoPE, which happens upstream.
+  * Parents are int32 with parent[0] = -1 and 0 <= parent[i] < i; anything
+    else is rejected here (the GPU side flags it per sequence instead).
+  * Bits at or above q_len in the last word are zero.
+  * The gather reads every source row before writing any destination row.
+
+Parity status: every function here is pinned by CPU tests against closed
+forms, brute force, library routines or invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Visibility  [Milestone, "The Reasoning Behind the Architecture"]
+# ----------------------------------------------------------------------------
+
+def words_for(q_len: int) -> int:
+    """Number of 64-bit words per node mask (two words for up to 128 nodes)."""
+    return (q_len + 63) // 64
+
+
+def check_parents(parents: np.ndarray) -> None:
+    """Raise ValueError unless ``parents`` is a topologically ordered tree."""
+    parents = np.asarray(parents)
+    if parents.ndim != 1 or parents.size == 0:
+        raise ValueError("parents must be a non-empty 1-D array")
+    if int(parents[0]) != -1:
+        raise ValueError("parent[0] must be -1 (node 0 is the verified token)")
+    for i in range(1, parents.size):
+        p = int(parents[i])
+        if not (0 <= p < i):
+            raise ValueError(f"parent[{i}] = {p} is not an earlier node")
+
+
+def ancestor_masks(parents: np.ndarray) -> list[int]:
+    """Ancestor-or-self sets as Python ints, built in node order:
+    mask(0) = bit 0;  mask(i) = mask(parent(i)) | bit(i)."""
+    check_parents(parents)
+    masks: list[int] = []
+    for i, p in enumerate(np.asarray(parents).tolist()):
+        own = 1 << i
+        masks.append(own if p < 0 else (masks[p] | own))
+    return masks
+
+
+def pack_mask(mask: int, n_words: int) -> np.ndarray:
+    """Split an integer bitmask into 64-bit words, least significant first."""
+    out = np.zeros(n_words, dtype=np.uint64)
+    for w in range(n_words):
+        out[w] = np.uint64((mask >> (64 * w)) & 0xFFFFFFFFFFFFFFFF)
+    return out
+
+
+def build_visibility(parents: np.ndarray):
+    """parents int [B, q] -> (vis uint64 [B, q, W], depth int32 [B, q]).
+
+    Bit j of row i (word j // 64, bit j % 64) is set iff node j is an
+    ancestor of node i or node i itself; depth(i) = |ancestors-or-self| - 1.
+    """
+    parents = np.asarray(parents)
+    B, q = parents.shape
+    W = words_for(q)
+    vis = np.zeros((B, q, W), dtype=np.uint64)
+    depth = np.zeros((B, q), dtype=np.int32)
+    for b in range(B):
+        masks = ancestor_masks(parents[b])
+        for i, m in enumerate(masks):
+            vis[b, i] = pack_mask(m, W)
+            depth[b, i] = bin(m).count("1") - 1
+    return vis, depth
+
+
+def unpack_row(vis_row: np.ndarray, q_len: int) -> np.ndarray:
+    """Boolean visibility of the q_len tree keys for one query node."""
+    bits = np.zeros(q_len, dtype=bool)
+    for j in range(q_len):
+        bits[j] = (int(vis_row[j // 64]) >> (j % 64)) & 1
+    return bits
+
+
+# ----------------------------------------------------------------------------
+# Verify attention  [Checkpoint, "The Message"; Final, "Input Knowledge Required"]
+# ----------------------------------------------------------------------------
+
+def key_mask(prefix_len: int, vis_row: np.ndarray, q_len: int) -> np.ndarray:
+    """[ones over the prefix | tree visibility] for one query node."""
+    return np.concatenate([np.ones(prefix_len, dtype=bool), unpack_row(vis_row, q_len)])
+
+
+def _attend(q_lat_row, q_pe_row, c_kv, k_pe, mask, scale):
+    """One query row against keys 0..N-1 (N = len(mask)); float64 throughout.
+    Returns (o[R], lse)."""
+    s = scale * (c_kv @ q_lat_row + k_pe @ q_pe_row)
+    s = np.where(mask, s, -np.inf)
+    m = np.max(s)
+    e = np.exp(s - m)                      # exactly 0 where masked
+    z = np.sum(e)
+    lse = m + math.log(z)
+    o = (e / z) @ c_kv
+    return o, lse
+
+
+def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, scale):
+    """Tree-verify attention, float64.
+
+    q_lat [B, q, H, R], q_pe [B, q, H, P], c_kv [B, S, R], k_pe [B, S, P]
+    (the tree's own latents already appended at rows L_b .. L_b+q-1),
+    prefix_lens [B], vis uint64 [B, q, W].
+    Returns o [B, q, H, R] and lse [B, q, H] (natural log, scale included).
+
+    One sequence at a time: scores for all (token, head) rows against keys
+    0 .. L_b+q-1 in one matrix product, the mask applied per token, then a
+    row-wise log-sum-exp and a weighted sum of the c_kv rows.
+    """
+    q_lat = np.asarray(q_lat, dtype=np.float64)
+    q_pe = np.asarray(q_pe, dtype=np.float64)
+    c_kv = np.asarray(c_kv, dtype=np.float64)
+    k_pe = np.asarray(k_pe, dtype=np.float64)
+    B, q, H, R = q_lat.shape
+    o = np.zeros((B, q, H, R), dtype=np.float64)
+    lse = np.zeros((B, q, H), dtype=np.float64)
+    for b in range(B):
+        L = int(prefix_lens[b])
+        N = L + q
+        if N > c_kv.shape[1]:
+            raise ValueError("prefix_len + q_len exceeds the cache capacity")
+        keys_lat = c_kv[b, :N]                          # [N, R]
+        keys_pe = k_pe[b, :N]                           # [N, P]
+        for t in range(q):
+            mask = key_mask(L, vis[b, t], q)            # [N]
+            s = scale * (q_lat[b, t] @ keys_lat.T + q_pe[b, t] @ keys_pe.T)   # [H, N]
+            s = np.where(mask[None, :], s, -np.inf)
+            m = np.max(s, axis=1, keepdims=True)
+            e = np.exp(s - m)
+            z = np.sum(e, axis=1, keepdims=True)
+            lse[b, t] = (m + np.log(z))[:, 0]
+            o[b, t] = (e / z) @ keys_lat
+    return o, lse
+
+
+def verify_attn_rows(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, scale, rows):
+    """The same definition for a list of (b, t, h) rows only (used where the
+    full output is too large to compute on the CPU).  Inputs may be float64
+    arrays or callables returning float64 rows; returns (o [n, R], lse [n])."""
+    out_o, out_lse = [], []
+    q = vis.shape[1]
+    for (b, t, h) in rows:
+        L = int(prefix_lens[b])
+        N = L + q
+        mask = key_mask(L, vis[b, t], q)
+        o, l = _attend(np.asarray(q_lat[b, t, h], np.float64), np.asarray(q_pe[b, t, h], np.float64),
+                       np.asarray(c_kv[b, :N], np.float64), np.asarray(k_pe[b, :N], np.float64),
+                       mask, scale)
+        out_o.append(o)
+        out_lse.append(l)
+    return np.stack(out_o), np.asarray(out_lse)
+
+
+# ----------------------------------------------------------------------------
+# Split-prefix partials and their merge (log-sum-exp identity)
+# ----------------------------------------------------------------------------
+
+def attend_chunk(q_lat_row, q_pe_row, c_kv, k_pe, mask, scale):
+    """Attention restricted to one chunk of keys: (normalised o, lse); an
+    empty or fully masked chunk gives (zeros, -inf)."""
+    if not np.any(mask):
+        return np.zeros(c_kv.shape[1], dtype=np.float64), -np.inf
+    return _attend(q_lat_row, q_pe_row, c_kv, k_pe, mask, scale)
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine per-chunk results over the chunk axis (axis 0).
+
+    lse = ln sum_k exp(lse_k);  o = sum_k exp(lse_k - lse) * o_k,
+    where each o_k is the chunk's normalised output.  Chunks with
+    lse_k = -inf carry no weight.  A row whose chunks are all empty gets
+    lse = -inf and o = 0.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = np.max(lse_parts, axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m_safe[None]), 0.0)
+    z = np.sum(w, axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, z, 1.0)), -np.inf)
+    zz = np.where(finite, z, 1.0)
+    o = np.sum(w[..., None] * o_parts, axis=0) / zz[..., None]
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Accepted-path gather  [Checkpoint, "The Message": post-verify compaction]
+# ----------------------------------------------------------------------------
+
+def gather_accepted(cache, prefix_lens, accepted, n_accepted):
+    """Return a copy of ``cache`` [B, S, C] in which, for every sequence b and
+    k < n_accepted[b], row L_b + k holds what row L_b + accepted[b, k] held
+    before the call.  All other rows are unchanged."""
+    old = np.array(cache, copy=True)
+    new = np.array(cache, copy=True)
+    B = old.shape[0]
+    for b in range(B):
+        L = int(prefix_lens[b])
+        for k in range(int(n_accepted[b])):
+            new[b, L + k] = old[b, L + int(accepted[b, k])]
+    return new
