@@ -1,0 +1,222 @@
+/*
+ * kdt.h — C ABI of libkdt.so: tree-verify MLA-absorb attention for AMD MI355X (gfx950).
+ *
+ * Pages cited (titles; sections in quotes):
+ *   [Checkpoint]  "The Checkpoint: Committing a Working Native DDTree Engine"
+ *   [Milestone]   "The Milestone Commit: Cementing a Native DDTree Inference Engine"
+ *   [Final]       "The Final Commit: Cementing a Native DDTree Inference Engine for Kimi K2.6"
+ *
+ * One DDTree verify step, as the pages describe it [Checkpoint, "The Message",
+ * KV-cache scheme]: the q_len = 1 + drafts tree tokens [verified_id, drafts]
+ * are processed at positions L + depth, the prefix is the cache length L, and
+ * the attention mask is [ones over the prefix | tree visibility]; ordinary AR
+ * decoding is the q_len = 1 case; after acceptance the accepted path's latents
+ * are gathered into place.  Attention runs in the absorbed MLA form [Final,
+ * "Input Knowledge Required"]: queries arrive already multiplied by w_kc
+ * (q_lat, kv_lora_rank R wide) plus their rope part q_pe (P wide); keys are the
+ * cached latents c_kv (R) and rope keys k_pe (P); the result is the latent
+ * context, to which w_vc is applied downstream.
+ *
+ * General rules for every entry point
+ *   - Pointers are DEVICE pointers unless stated otherwise.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *     enqueues work on `stream`: nothing is synchronised, nothing is allocated or
+ *     freed, and no pointer is kept after the call returns.  The library is
+ *     stateless; calls from several host threads are safe.
+ *   - The caller owns every buffer, including the verify workspace.
+ *   - Host-checkable faults (null pointers, non-positive sizes, unsupported
+ *     shapes or dtypes, misaligned buffers, a too-small workspace, capacity
+ *     below max_prefix_len + q_len) return a nonzero kdt_status and launch
+ *     nothing.  A failed kernel launch returns KDT_ERR_LAUNCH.
+ *   - Data-dependent faults visible only on the device never cause an access
+ *     out of bounds: the kernels clamp, skip the affected work, and OR a
+ *     KDT_SEQ_* flag into seq_status[b] when a seq_status array is given
+ *     (entry points never clear seq_status; the caller zeroes it).
+ */
+#ifndef KDT_H
+#define KDT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDT_ABI_VERSION 1
+#define KDT_MAX_Q_LEN 128           /* tree tokens per sequence (two 64-bit mask words) */
+
+typedef enum {
+  KDT_OK = 0,
+  KDT_ERR_INVALID_ARG = 1,   /* null pointer, bad size, aliasing that is not allowed */
+  KDT_ERR_UNSUPPORTED = 2,   /* dtype / (R, P) / q_len / alignment this build does not handle */
+  KDT_ERR_WORKSPACE = 3,     /* workspace missing or smaller than kdt_verify_get_plan reports */
+  KDT_ERR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch */
+} kdt_status;
+
+typedef enum { KDT_F32 = 0, KDT_BF16 = 1 } kdt_dtype;
+
+/* Per-sequence device status flags (OR-ed into seq_status[b]). */
+enum {
+  KDT_SEQ_OK = 0,
+  KDT_SEQ_BAD_TREE = 1,   /* parent[0] != -1 or parent[i] not in [0, i) */
+  KDT_SEQ_BAD_LEN = 2,    /* prefix_len < 0, > max_prefix_len, or prefix_len + q_len > capacity */
+  KDT_SEQ_BAD_INDEX = 4   /* an accepted index outside [0, q_len) or n_accepted outside [0, max_acc] */
+};
+
+int kdt_abi_version(void);
+const char* kdt_status_str(int code);            /* static string, never NULL */
+
+/* ------------------------------------------------------------------------
+ * kdt_build_visibility — ancestor-or-self bitmask of every tree node.
+ * [Milestone, "The Reasoning Behind the Architecture"]: a node's mask is its
+ * parent's mask plus its own bit; two 64-bit words cover up to 65 nodes.
+ *
+ *   parents  int32 [B, q_len], row-major.  parent[b][0] = -1 (the verified
+ *            token); 0 <= parent[b][i] < i otherwise (best-first node order).
+ *   vis      uint64 [B, q_len, W] out, W = (q_len + 63) / 64.  Bit (j % 64) of
+ *            word j / 64 in row i is set iff node j is node i or an ancestor of
+ *            it.  Bits at or above q_len are zero.  Every word is written.
+ *   depth    int32 [B, q_len] out, nullable: number of ancestors of node i.
+ *   seq_status int32 [B], nullable.
+ * A node whose parent is invalid is treated as a root (its row then holds
+ * itself and its valid ancestors only) and KDT_SEQ_BAD_TREE is flagged.
+ * Supported: 1 <= q_len <= KDT_MAX_Q_LEN, B >= 1.
+ * ---------------------------------------------------------------------- */
+int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
+                         uint64_t* vis, int32_t* depth, int32_t* seq_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kdt_verify_attn — tree-verify attention in latent space.
+ * [Checkpoint, "The Message"] KV-cache scheme; [Final, "Input Knowledge
+ * Required"] absorbed MLA form.
+ *
+ * For sequence b with prefix length L = prefix_lens[b], tree token t and head
+ * h, the visible keys are cache rows 0..L-1 (the prefix) and rows L+j for every
+ * node j with bit j set in vis[b][t] (tree node j's latents sit in row L+j).
+ * With s_j = softmax_scale * (q_lat[b,t,h,:] . c_kv[b,j,:] + q_pe[b,t,h,:] . k_pe[b,j,:]):
+ *     out[b,t,h,:] = sum_j softmax(s)_j * c_kv[b,j,:]
+ *     lse[b,t,h]   = ln sum_j exp(s_j)                (natural log, scale included)
+ * q_len = 1 with vis = {1} is one AR decode step.
+ *
+ * Layouts (strides are in ELEMENTS; the innermost dimension is contiguous):
+ *   q_lat [B, q_len, H, R]   strides q_lat_sb, q_lat_st, q_lat_sh
+ *   q_pe  [B, q_len, H, P]   strides q_pe_sb,  q_pe_st,  q_pe_sh
+ *   c_kv  [B, capacity, R]   strides c_kv_sb, c_kv_ss (row stride may be R+P for a fused [c_kv | k_pe] cache)
+ *   k_pe  [B, capacity, P]   strides k_pe_sb, k_pe_ss
+ *   vis   uint64 [B, q_len, W] contiguous (as written by kdt_build_visibility)
+ *   out   [B, q_len, H, R]   in `dtype`, strides out_sb, out_st, out_sh
+ *   lse   float32 [B, q_len, H] contiguous
+ * `dtype` is the element type of q_lat, q_pe, c_kv, k_pe and out.  Arithmetic:
+ * products accumulate in fp32 on the matrix cores; for bf16 the softmax
+ * weights are rounded to bf16 before the value contraction; out is rounded to
+ * `dtype` (round to nearest even) from fp32.
+ * Supported: (dtype, R, P) in {(bf16, 512, 64), (bf16, 64, 16), (f32, 64, 16)};
+ * 1 <= q_len <= KDT_MAX_Q_LEN; H >= 1; B >= 1; every input pointer and every
+ * row stride 16-byte aligned; capacity >= max_prefix_len + q_len.
+ * `max_prefix_len` is a HOST upper bound on prefix_lens[] (it sizes the grid);
+ * a sequence with prefix_lens[b] > max_prefix_len, < 0, or prefix_lens[b] +
+ * q_len > capacity is skipped (out rows zero, lse = -inf) and flagged
+ * KDT_SEQ_BAD_LEN.
+ *
+ * Split-prefix execution.  The key range of each sequence is cut into splits of
+ * `split_keys` keys (0 = the library's choice; otherwise a multiple of 64).
+ * Each split produces a normalised partial output and its log-sum-exp in the
+ * workspace; a second kernel merges the splits by the log-sum-exp identity.
+ * When every sequence fits in one split the merge is skipped and the first
+ * kernel writes out/lse directly.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t dtype;                       /* kdt_dtype */
+  int32_t B, q_len, H, R, P;
+  const void* q_lat; int64_t q_lat_sb, q_lat_st, q_lat_sh;
+  const void* q_pe;  int64_t q_pe_sb,  q_pe_st,  q_pe_sh;
+  const void* c_kv;  int64_t c_kv_sb,  c_kv_ss;
+  const void* k_pe;  int64_t k_pe_sb,  k_pe_ss;
+  int64_t capacity;                    /* cache rows per sequence */
+  const int32_t* prefix_lens;          /* device int32 [B] */
+  int32_t max_prefix_len;              /* host upper bound on prefix_lens[] */
+  const uint64_t* vis;                 /* device uint64 [B, q_len, W] */
+  float softmax_scale;
+  void* out; int64_t out_sb, out_st, out_sh;
+  float* lse;                          /* device float32 [B, q_len, H] */
+  int32_t* seq_status;                 /* device int32 [B], nullable */
+  int32_t split_keys;                  /* 0 = auto, else a multiple of 64 */
+} kdt_verify_desc;
+
+/* Host-only planning: no device access.  The partial buffers live in the
+ * workspace at the given byte offsets:
+ *   part_o   float32 [B, max_splits, q_len*H, R]   normalised partial outputs
+ *   part_lse float32 [B, max_splits, q_len*H]      natural-log partial LSE (-inf: empty split)
+ * Row index within a sequence is m = t*H + h.  Sequence b uses splits
+ * 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1. */
+typedef struct {
+  int32_t split_keys;          /* keys per split (multiple of 64) */
+  int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
+  int32_t rows;                /* q_len * H */
+  int32_t direct;              /* 1: max_splits == 1, no partials, no merge */
+  int64_t part_o_offset;       /* bytes into the workspace */
+  int64_t part_lse_offset;
+  size_t workspace_bytes;      /* 0 when direct */
+} kdt_verify_plan;
+
+int kdt_verify_get_plan(const kdt_verify_desc* d, kdt_verify_plan* plan);
+
+/* Full verify: split stage, then the merge (or direct output when one split
+ * suffices).  `workspace` may be NULL only when the plan says workspace_bytes == 0. */
+int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* Split stage only: always writes the partial buffers (part_o, part_lse) in the
+ * workspace, even when one split would do; `out`/`lse` are not touched. */
+int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kdt_merge_partials — cross-split log-sum-exp merge.
+ *   lse[b,m] = ln sum_k exp(part_lse[b,k,m]);
+ *   out[b,m,:] = sum_k exp(part_lse[b,k,m] - lse[b,m]) * part_o[b,k,m,:]
+ * over k < n_splits, where n_splits = max_splits when split_keys == 0, else
+ * ceil((prefix_lens[b] + q_len) / split_keys) clamped to [1, max_splits].
+ * Splits with part_lse = -inf carry no weight; a row with no finite split gets
+ * out = 0 and lse = -inf.  out is written in `dtype` (bf16: round to nearest
+ * even).  part_o / part_lse are contiguous with the layout given above; out has
+ * strides out_sb, out_st, out_sh (elements) over [B, q_len, H, R].
+ * prefix_lens may be NULL when split_keys == 0.
+ * ---------------------------------------------------------------------- */
+int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32_t R,
+                       const float* part_o, const float* part_lse, int32_t max_splits,
+                       const int32_t* prefix_lens, int32_t split_keys,
+                       void* out, int64_t out_sb, int64_t out_st, int64_t out_sh,
+                       float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kdt_gather_accepted — post-accept compaction of the accepted path's latents.
+ * [Checkpoint, "The Message"]: "after accept gather accepted-path latents"
+ * (cache append + post-verify compaction).
+ *
+ * For every layer l < num_layers, sequence b and k < n_accepted[b]:
+ *     row L_b + k  <-  (previous contents of) row L_b + accepted[b, k]
+ * where L_b = prefix_lens[b].  All rows are read before any is written, so
+ * overlapping source and destination rows are safe; no other row changes.
+ *   cache      base of layer 0; element (l, b, s, c) at
+ *              l*layer_stride + b*cache_sb + s*cache_ss + c   (elements of `dtype`)
+ *   row_elems  elements copied per row (e.g. R + P for a fused cache row)
+ *   accepted   int32 [B, max_acc] row-major; n_accepted int32 [B]
+ *   new_prefix_lens  int32 [B] out, nullable: L_b + n_accepted[b].  Must not
+ *              alias prefix_lens.
+ * Device checks: a sequence with L_b < 0 or L_b + q_len > capacity is skipped
+ * (KDT_SEQ_BAD_LEN); n_accepted outside [0, min(max_acc, q_len)] is clamped
+ * and an accepted index outside [0, q_len) skips that row (KDT_SEQ_BAD_INDEX).
+ * The copy is bit-exact.  Supported: 1 <= q_len <= KDT_MAX_Q_LEN, 1 <= max_acc <= q_len.
+ * ---------------------------------------------------------------------- */
+int kdt_gather_accepted(int32_t dtype, int32_t B, int32_t q_len, int32_t row_elems,
+                        void* cache, int64_t cache_sb, int64_t cache_ss, int64_t capacity,
+                        int32_t num_layers, int64_t layer_stride,
+                        const int32_t* prefix_lens, const int32_t* accepted,
+                        const int32_t* n_accepted, int32_t max_acc,
+                        int32_t* new_prefix_lens, int32_t* seq_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDT_H */

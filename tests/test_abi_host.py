@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/kdt.h declares, and its host-side checks and planning work without
+launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verify_mla_kdt_amd import kdt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdt.h")
+FAKE = 0x10000     # never dereferenced: these calls fail validation before any launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    names = declared_functions()
+    assert "kdt_verify_attn" in names and "kdt_gather_accepted" in names and "kdt_build_visibility" in names
+    L = kdt.lib()
+    for n in names:
+        assert hasattr(L, n), f"libkdt.so does not export {n}"
+
+
+def test_version_and_status_strings():
+    assert kdt.lib().kdt_abi_version() == 1
+    for code in range(5):
+        assert kdt.status_str(code)
+    assert kdt.status_str(99) == "unknown status"
+
+
+def _desc(**kw):
+    d = kdt.VerifyDesc()
+    d.dtype, d.B, d.q_len, d.H, d.R, d.P = 1, 1, 65, 16, 512, 64
+    for f in ("q_lat", "q_pe", "c_kv", "k_pe", "prefix_lens", "vis", "out", "lse"):
+        setattr(d, f, FAKE)
+    d.q_lat_sb, d.q_lat_st, d.q_lat_sh = 65 * 16 * 512, 16 * 512, 512
+    d.q_pe_sb, d.q_pe_st, d.q_pe_sh = 65 * 16 * 64, 16 * 64, 64
+    d.c_kv_sb, d.c_kv_ss, d.k_pe_sb, d.k_pe_ss = 4224 * 576, 576, 4224 * 576, 576
+    d.capacity, d.max_prefix_len, d.softmax_scale = 4224, 4096, 576 ** -0.5
+    d.out_sb, d.out_st, d.out_sh = 65 * 16 * 512, 16 * 512, 512
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _plan(d):
+    p = kdt.VerifyPlan()
+    rc = kdt.lib().kdt_verify_get_plan(ctypes.byref(d), ctypes.byref(p))
+    return rc, p
+
+
+def test_plan_sizes_and_layout():
+    rc, p = _plan(_desc())
+    assert rc == 0
+    M = 65 * 16
+    assert p.rows == M
+    assert p.split_keys % 64 == 0 and p.split_keys >= 256
+    assert p.max_splits == -(-(4096 + 65) // p.split_keys)
+    assert p.direct == (1 if p.max_splits == 1 else 0)
+    assert p.part_lse_offset >= 1 * p.max_splits * M * 512 * 4 and p.part_lse_offset % 256 == 0
+    assert p.workspace_bytes == p.part_lse_offset + p.max_splits * M * 4
+    rc, p = _plan(_desc(split_keys=128))
+    assert rc == 0 and p.split_keys == 128 and p.max_splits == 33
+    # a single split: no workspace
+    rc, p = _plan(_desc(split_keys=8192))
+    assert rc == 0 and p.direct == 1 and p.max_splits == 1
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("q_lat", 0, 1), ("lse", 0, 1), ("B", 0, 1), ("H", -1, 1),
+    ("capacity", 4100, 1),                 # below max_prefix_len + q_len
+    ("split_keys", 100, 1),                # not a multiple of 64
+    ("softmax_scale", 0.0, 1),
+    ("q_len", 129, 2),                     # beyond two mask words
+    ("R", 256, 2), ("dtype", 7, 2),
+    ("q_lat_sh", 500, 2),                  # stride not 16-byte aligned
+    ("q_lat", FAKE + 2, 2),                # pointer not 16-byte aligned
+])
+def test_plan_rejects_bad_descriptors(field, value, code):
+    kw = {field: value}
+    if field == "q_len":
+        kw["max_prefix_len"] = 1000        # keep the capacity check satisfied
+    rc, _ = _plan(_desc(**kw))
+    assert rc == code
+
+
+def test_fp32_large_rank_is_unsupported():
+    rc, _ = _plan(_desc(dtype=0))
+    assert rc == 2
+    d = _desc(dtype=0, R=64, P=16, q_lat_sh=64, q_lat_st=16 * 64, q_lat_sb=65 * 16 * 64,
+              q_pe_sh=16, q_pe_st=16 * 16, q_pe_sb=65 * 16 * 16, c_kv_ss=80, k_pe_ss=80,
+              c_kv_sb=4224 * 80, k_pe_sb=4224 * 80, out_sh=64, out_st=16 * 64, out_sb=65 * 16 * 64)
+    rc, p = _plan(d)
+    assert rc == 0
+
+
+def test_verify_needs_workspace_when_split():
+    d = _desc()
+    rc = kdt.lib().kdt_verify_attn(ctypes.byref(d), None, 0, None)
+    assert rc == 3
+
+
+def test_visibility_and_gather_argument_checks():
+    L = kdt.lib()
+    assert L.kdt_build_visibility(None, 1, 9, FAKE, None, None, None) == 1
+    assert L.kdt_build_visibility(FAKE, 0, 9, FAKE, None, None, None) == 1
+    assert L.kdt_build_visibility(FAKE, 1, 129, FAKE, None, None, None) == 2
+    g = L.kdt_gather_accepted
+    # dtype, B, q, row_elems, cache, sb, ss, capacity, layers, layer_stride, pl, acc, nacc, max_acc, npl, st, stream
+    assert g(1, 1, 9, 576, None, 0, 576, 64, 1, 0, FAKE, FAKE, FAKE, 9, None, None, None) == 1
+    assert g(1, 1, 9, 576, FAKE, 0, 576, 64, 1, 0, FAKE, FAKE, FAKE, 10, None, None, None) == 1   # max_acc > q
+    assert g(1, 1, 9, 576, FAKE, 0, 576, 64, 1, 0, FAKE, FAKE, FAKE, 9, FAKE, None, None) == 1    # npl aliases pl
+    assert g(5, 1, 9, 576, FAKE, 0, 576, 64, 1, 0, FAKE, FAKE, FAKE, 9, None, None, None) == 2    # dtype
+    assert g(1, 1, 200, 576, FAKE, 0, 576, 256, 1, 0, FAKE, FAKE, FAKE, 9, None, None, None) == 2
+    m = L.kdt_merge_partials
+    assert m(1, 1, 9, 4, 512, None, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 1
+    assert m(1, 1, 9, 4, 512, FAKE, FAKE, 2, None, 64, FAKE, 0, 0, 0, FAKE, None) == 1           # needs prefix_lens
+    assert m(1, 1, 9, 4, 2048, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2

@@ -1,0 +1,228 @@
+"""GPU tree-verify attention vs the float64 oracle.
+
+Full element-by-element comparisons at sizes the oracle finishes in seconds
+(several key tiles, ragged tails, several row tiles), every configuration at
+its full size (sampled rows where the full oracle would take too long), the
+AR (q_len = 1) case, forced split counts, and the invariants: masked keys get
+exactly zero weight (bit-identical output), chain == successive AR calls,
+prefix permutation, gather-then-AR == tree row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_verify_mla_kdt_amd import kdt, synth
+from gpu_util import (GpuInputs, check_close, oracle_full, oracle_rows, require_gpu, sample_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(g: GpuInputs, split_keys=0, vis=None, max_prefix_len=None, seq_status=None):
+    require_gpu()
+    if vis is None:
+        vis, _ = kdt.build_visibility(g.parents)
+    out, lse = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis, g.cfg.softmax_scale,
+                               max_prefix_len=g.max_prefix_len if max_prefix_len is None else max_prefix_len,
+                               split_keys=split_keys, seq_status=seq_status)
+    torch.cuda.synchronize()
+    return to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def small_cfg(dtype="bf16", B=2, H=16, R=512, P=64, q=17, prefix=("fixed", 200), tree="uniform", index=11):
+    return synth.Config(f"small_{dtype}_{R}_{q}", index, dtype, B=B, H=H, R=R, P=P, q_len=q, prefix=prefix,
+                        tree=tree)
+
+
+# ---------------------------------------------------------------- full parity, small sizes
+
+@pytest.mark.parametrize("split_keys", [0, 64])
+def test_tiny_fp32_config(split_keys):
+    inp = synth.generate(synth.CONFIGS["tiny_fp32"])
+    g = GpuInputs(inp)
+    o, l = run_gpu(g, split_keys=split_keys)
+    ro, rl = oracle_full(inp)
+    check_close("f32", o, ro, l, rl, "tiny_fp32")
+
+
+@pytest.mark.parametrize("q,tree", [(1, "chain"), (9, "uniform"), (17, "star"), (33, "deep_chain"),
+                                    (65, "best_first"), (65, "chain"), (100, "uniform"), (128, "uniform")])
+def test_bf16_full_parity_tree_shapes(q, tree):
+    cfg = small_cfg(q=q, tree=tree, prefix=("uniform", 0, 300), B=3, H=8, index=20 + q)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o, ro, l, rl, f"q={q} {tree}")
+
+
+@pytest.mark.parametrize("split_keys", [0, 64, 128, 192, 1024])
+def test_bf16_split_counts_agree(split_keys):
+    cfg = small_cfg(q=33, tree="deep_chain", prefix=("uniform", 40, 700), B=3, H=16, index=31)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g, split_keys=split_keys)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o, ro, l, rl, f"split_keys={split_keys}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_rank_shapes(dtype):
+    cfg = small_cfg(dtype=dtype, R=64, P=16, H=4, q=9, prefix=("uniform", 0, 130), B=4, index=41)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    for sk in (0, 64):
+        o, l = run_gpu(g, split_keys=sk)
+        ro, rl = oracle_full(inp)
+        check_close(dtype, o, ro, l, rl, f"{dtype} R=64 split={sk}")
+
+
+def test_heads_not_multiple_of_tile_and_empty_prefix():
+    # M = q*H = 7*3 = 21 rows: one partial row tile; prefix 0 for one sequence
+    cfg = small_cfg(q=7, H=3, prefix=("fixed", 0), B=2, index=51)
+    inp = synth.generate(cfg, prefix_override=[0, 77])
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o, ro, l, rl, "H=3 q=7")
+
+
+def test_strided_fused_and_separate_caches():
+    cfg = small_cfg(q=17, H=16, prefix=("fixed", 333), B=2, index=61)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o1, l1 = run_gpu(g)
+    # separate contiguous c_kv / k_pe buffers must give bit-identical results
+    g.c_kv = g.cache[..., :cfg.R].contiguous()
+    g.k_pe = g.cache[..., cfg.R:].contiguous()
+    o2, l2 = run_gpu(g)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------- full-size configurations
+
+def test_config_max_budget_full():
+    inp = synth.generate(synth.CONFIGS["max_budget"])
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o, ro, l, rl, "max_budget")
+
+
+def test_config_batched_full():
+    inp = synth.generate(synth.CONFIGS["batched"])
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o, ro, l, rl, "batched")
+
+
+@pytest.mark.parametrize("name", ["long_ctx", "ragged_deep"])
+def test_config_large_sampled_rows(name):
+    inp = synth.generate(synth.CONFIGS[name])
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    rows = sample_rows(inp, 48)
+    ro, rl = oracle_rows(inp, rows)
+    go = np.stack([o[b, t, h] for (b, t, h) in rows])
+    gl = np.asarray([l[b, t, h] for (b, t, h) in rows])
+    check_close("bf16", go, ro, gl, rl, name)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+@pytest.mark.parametrize("name", ["max_budget", "long_ctx"])
+def test_ar_degenerate_q1(name):
+    cfg = synth.config_variant(synth.CONFIGS[name], q_len=1)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    if name == "max_budget":
+        ro, rl = oracle_full(inp)
+        check_close("bf16", o, ro, l, rl, f"{name} q=1")
+    else:
+        rows = sample_rows(inp, 32)
+        ro, rl = oracle_rows(inp, rows)
+        check_close("bf16", np.stack([o[r] for r in rows]), ro, np.asarray([l[r] for r in rows]), rl, name)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_masked_keys_have_exactly_zero_weight():
+    cfg = small_cfg(q=33, tree="star", prefix=("fixed", 150), B=2, H=16, index=71)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o1, l1 = run_gpu(g, split_keys=64)
+    L, q = int(inp.prefix_lens[0]), cfg.q_len
+    # rows past the tree: invisible to every token
+    g.cache[:, L + q:] = 300.0
+    o2, l2 = run_gpu(g, split_keys=64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # in a star, node j >= 1 is seen only by token j
+    j = 5
+    g.cache[:, L + j] = -250.0
+    o3, l3 = run_gpu(g, split_keys=64)
+    others = [t for t in range(q) if t != j]
+    assert np.array_equal(o3[:, others], o1[:, others]) and np.array_equal(l3[:, others], l1[:, others])
+    assert not np.array_equal(o3[:, j], o1[:, j])
+
+
+def test_chain_equals_successive_ar_calls():
+    cfg = small_cfg(q=9, tree="chain", prefix=("fixed", 260), B=1, H=16, index=81)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    one = torch.ones((1, 1, 1), dtype=torch.int64, device=g.q_lat.device)
+    for t in range(cfg.q_len):
+        out, lse = kdt.verify_attn(g.q_lat[:, t:t + 1], g.q_pe[:, t:t + 1], g.c_kv, g.k_pe,
+                                   g.prefix_lens + t, one, cfg.softmax_scale, max_prefix_len=260 + t)
+        torch.cuda.synchronize()
+        check_close("bf16", to_f64(out)[0, 0], o[0, t], lse.cpu().numpy()[0, 0], l[0, t], f"AR step {t}")
+
+
+def test_prefix_permutation_invariance():
+    cfg = small_cfg(q=17, prefix=("fixed", 500), B=1, H=16, index=91)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o1, l1 = run_gpu(g)
+    perm = torch.from_numpy(synth.rng_for(3).permutation(500)).to(g.cache.device)
+    g.cache[:, :500] = g.cache[:, perm]
+    o2, l2 = run_gpu(g)
+    check_close("bf16", o2, o1, l2, l1, "prefix permutation")
+
+
+def test_gather_then_ar_equals_tree_row():
+    cfg = small_cfg(q=17, tree="uniform", prefix=("fixed", 123), B=1, H=16, index=95)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g)
+    _, depth = oracle.build_visibility(inp.parents)
+    one = torch.ones((1, 1, 1), dtype=torch.int64, device=g.q_lat.device)
+    for t in (0, 5, 16):
+        g2 = GpuInputs(inp)
+        path = synth.path_to(inp.parents[0], t)
+        acc = torch.zeros((1, cfg.q_len), dtype=torch.int32, device=g2.cache.device)
+        acc[0, :len(path)] = torch.from_numpy(path)
+        n = torch.tensor([len(path)], dtype=torch.int32, device=g2.cache.device)
+        kdt.gather_accepted(g2.cache, g2.prefix_lens, acc, n, cfg.q_len)
+        d = int(depth[0, t])
+        out, lse = kdt.verify_attn(g2.q_lat[:, t:t + 1], g2.q_pe[:, t:t + 1], g2.c_kv, g2.k_pe,
+                                   g2.prefix_lens + d, one, cfg.softmax_scale, max_prefix_len=123 + d)
+        torch.cuda.synchronize()
+        check_close("bf16", to_f64(out)[0, 0], o[0, t], lse.cpu().numpy()[0, 0], l[0, t], f"path to {t}")
+
+
+def test_bad_prefix_lengths_are_skipped_and_flagged():
+    cfg = small_cfg(q=9, prefix=("fixed", 100), B=3, H=4, index=97)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    st = torch.zeros(3, dtype=torch.int32, device=g.q_lat.device)
+    g.prefix_lens[1] = 150          # beyond the max_prefix_len bound passed below
+    g.prefix_lens[2] = -3
+    for sk in (0, 64):
+        st.zero_()
+        o, l = run_gpu(g, split_keys=sk, max_prefix_len=100, seq_status=st)
+        assert st.cpu().tolist() == [0, kdt.KDT_SEQ_BAD_LEN, kdt.KDT_SEQ_BAD_LEN]
+        assert np.all(o[1:] == 0) and np.all(np.isneginf(l[1:]))
+        ro, rl = oracle_full(synth.Inputs(cfg, inp.parents[:1], inp.prefix_lens[:1], inp.q_lat[:1],
+                                          inp.q_pe[:1], inp.cache[:1], inp.accepted[:1], inp.n_accepted[:1]))
+        check_close("bf16", o[:1], ro, l[:1], rl, f"good sequence, split={sk}")

@@ -1,0 +1,694 @@
+// Tree-verify MLA-absorb attention: split-prefix verify kernel + cross-split
+// log-sum-exp merge, for gfx950 (CDNA4, wave64, MFMA).
+//
+// What is computed ("The Checkpoint: Committing a Working Native DDTree
+// Engine", section "The Message", KV-cache scheme; "The Final Commit:
+// Cementing a Native DDTree Inference Engine for Kimi K2.6", section "Input
+// Knowledge Required", absorbed MLA): the q_len tree tokens of a sequence,
+// each with H heads, attend over the cached latent rows [prefix | tree] under
+// the mask [ones | ancestor-or-self visibility].  Score of key j for row
+// (t, h): scale * (q_lat . c_kv[j] + q_pe . k_pe[j]); output: softmax-weighted
+// sum of c_kv rows, plus the row's log-sum-exp.
+//
+// Design (gfx950-first; the pages give no kernel design for this step):
+// * The latent cache is shared by every head, so for one sequence the
+//   (token, head) rows form the M dimension of two dense contractions:
+//   S^T = K * Q^T over D = R + P, and O^T = V^T * P^T over keys (V = c_kv).
+//   Both run on v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32
+//   (fp32).
+// * A workgroup is 4 waves (one per SIMD) and owns a tile of 128 rows of one
+//   sequence and one split of its key range.  Each wave owns 32 rows: their Q
+//   fragments stay in registers for the whole key loop and their 32 x R fp32
+//   output accumulators live in the accumulation registers.
+// * Keys stream through LDS in tiles of 32 rows x (R + P); all four waves read
+//   the same tile, so each K/V byte crosses L2 -> LDS once per 128 query rows.
+// * Computing S^T (keys along the MFMA rows) leaves every lane holding 16
+//   scores of ONE query row.  The row max needs one cross-half exchange, the
+//   running sum needs none until the end, and the softmax weights are already
+//   laid out as the B operand of the value contraction: no shuffles.
+// * Online softmax in the log2 domain against a per-row reference max fixed at
+//   the first visible key.  Weights stay below 2^32 for any realistic score
+//   range, so the 32 x R accumulators are never rescaled (a rescale would need
+//   a read-modify-write of all 256 accumulation registers every tile).  A row
+//   whose max outgrows its reference by more than that makes its wave redo the
+//   split once against the exact max, which it has tracked meanwhile.
+// * K/V tiles are double-buffered and copied straight from HBM into LDS with
+//   buffer_load_dwordx4 ... lds, so staging costs no registers and overlaps the
+//   previous tile's MFMA work.  The value operand is read with the gfx950
+//   transposing LDS load (ds_read_b64_tr_b16) from the same key-major tile the
+//   score operand uses.
+// * Masking costs nothing on prefix tiles; only tiles that reach the tree
+//   segment or the end of the split test bits.
+// * Split-prefix: a sequence's keys are cut into splits of split_keys keys;
+//   each split writes a normalised partial and its log-sum-exp, and the merge
+//   kernel recombines them.  With a single split the verify kernel writes the
+//   final output directly.
+// * Workgroup indices are remapped so the workgroups on one XCD take
+//   consecutive work units (all row tiles of one key split), which keeps
+//   their shared K/V stream in that XCD's L2.
+#include <math.h>
+
+#include "kdt_common.hpp"
+
+namespace kdt {
+
+constexpr int kBM = 128;          // query rows per workgroup
+constexpr int kBN = 32;           // keys per LDS tile
+constexpr int kThreads = 256;     // 4 waves
+constexpr int kCU = 256;          // MI355X compute units (split heuristic)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRefSlack = 32.0f;    // max weight 2^32 against the reference (log2 units)
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  typedef bf16x8 frag;
+  static constexpr int KW = 8;     // operand elements per lane
+  static constexpr int KMF = 16;   // contraction depth of one MFMA
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag pack(const float* p) {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (__bf16)p[j];
+    return f;
+  }
+  __device__ static __forceinline__ frag zero() {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (__bf16)0.0f;
+    return f;
+  }
+};
+
+template <>
+struct Mfma<float> {
+  typedef float frag;
+  static constexpr int KW = 1;
+  static constexpr int KMF = 2;
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag pack(const float* p) { return p[0]; }
+  __device__ static __forceinline__ frag zero() { return 0.0f; }
+};
+
+struct VerifyArgs {
+  const void* q_lat; int64_t q_lat_sb, q_lat_st, q_lat_sh;
+  const void* q_pe;  int64_t q_pe_sb, q_pe_st, q_pe_sh;
+  const void* c_kv;  int64_t c_kv_sb, c_kv_ss;
+  const void* k_pe;  int64_t k_pe_sb, k_pe_ss;
+  int64_t capacity;
+  const int32_t* prefix_lens;
+  const uint64_t* vis;
+  void* out; int64_t out_sb, out_st, out_sh;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int32_t* seq_status;
+  float scale_log2;
+  int B, q, H, M, W, n_rt, max_splits, split_keys, max_prefix_len;
+};
+
+// The value of C-layout register v of a 32x32 MFMA result held by a lane in
+// half hh (lane / 32) sits in row 8*(v/4) + 4*hh + (v%4) of the 32-row block.
+__device__ __forceinline__ int c_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
+
+__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
+
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, const float* v);
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, const float* v) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16* dst, const float* v) {
+  *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
+// LDS image of one key tile.  Two regions: kBN rows of the c_kv part (RC
+// 16-byte chunks per row) followed by kBN rows of the k_pe part (PC chunks).
+// Within a region whose rows hold a multiple of 8 chunks, chunk c of row k is
+// stored at chunk position c ^ swz(k).  swz is a bijection on k % 8, so the
+// score-operand reads (8 consecutive keys, same chunk) hit 8 different 16-byte
+// bank groups, and its upper two bits differ for any 4 consecutive keys, so a
+// transposing read (4 keys x 2 adjacent chunks) also touches 8 distinct groups.
+__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
+
+template <int NCH>
+__device__ __forceinline__ int region_off(int row, int chunk) {
+  if constexpr (NCH % 8 == 0) return (row * NCH + (chunk ^ swz(row))) << 4;
+  else return (row * NCH + chunk) << 4;
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
+// (j % 4) of the 8-byte load issued by lane 4e + j / 4, for e = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, num_records in bytes
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Start the copy of one region of a key tile straight into LDS: every
+// buffer_load_dwordx4 ... lds writes 64 consecutive 16-byte LDS slots, one per
+// lane, so each lane fetches the global chunk that belongs in its slot.  Rows
+// at or past `nrows` (the end of the split) re-read row nrows-1: the softmax
+// gives them zero weight, and this keeps every LDS value a finite cache value.
+template <int ROWS, int NCH>
+__device__ __forceinline__ void stage_region(__amdgpu_buffer_rsrc_t rs, uint32_t ss, int nrows,
+                                             char* lds, int wave, int lane) {
+  constexpr int SLOTS = ROWS * NCH;
+  static_assert(SLOTS % 64 == 0, "tile region must be whole wave loads");
+  constexpr int WAVES = kThreads / 64;
+  constexpr int PER_WAVE = (SLOTS / 64 + WAVES - 1) / WAVES;
+#pragma unroll
+  for (int jj = 0; jj < PER_WAVE; ++jj) {
+    const int j = wave + jj * WAVES;
+    if ((SLOTS / 64) % WAVES != 0 && j >= SLOTS / 64) break;
+    const int slot = j * 64 + lane;
+    const int row = slot / NCH, pc = slot - row * NCH;
+    const int c = (NCH % 8 == 0) ? (pc ^ swz(row)) : pc;
+    const int src_row = row < nrows ? row : nrows - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + j * 1024), 16,
+                                             (uint32_t)src_row * ss + (uint32_t)c * 16, 0, 0, 0);
+  }
+}
+
+template <typename T, int R, int P, bool DIRECT>
+__global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a) {
+  typedef Mfma<T> MM;
+  typedef typename MM::frag frag;
+  constexpr int D = R + P;
+  constexpr int KW = MM::KW, KMF = MM::KMF;
+  constexpr int NCHUNK = D / KMF;             // MFMA steps of the score contraction
+  constexpr int NB = R / 32;                  // 32-wide output column blocks
+  constexpr int PV_STEPS = kBN / KMF;         // MFMA steps of the value contraction per tile
+  constexpr int RC = R * (int)sizeof(T) / 16; // 16-byte chunks of c_kv per key
+  constexpr int PC = P * (int)sizeof(T) / 16; // 16-byte chunks of k_pe per key
+  constexpr int LAT_BYTES = kBN * RC * 16;
+  constexpr int BUF_BYTES = LAT_BYTES + kBN * PC * 16;
+  static_assert(R % 32 == 0 && D % KMF == 0 && (P * sizeof(T)) % 16 == 0, "shape");
+  static_assert(KW != 8 || (RC % 8 == 0 && (PC % 8 == 0 || P <= 32)), "bf16 score addressing");
+
+  __shared__ __attribute__((aligned(1024))) char s_kv[2 * BUF_BYTES];
+  __shared__ int s_dead;
+
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  const int rt = u % a.n_rt;
+  const int split = (u / a.n_rt) % a.max_splits;
+  const int b = u / (a.n_rt * a.max_splits);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int m = rt * kBM + wave * 32 + r;     // this lane's query row
+  const bool row_ok = m < a.M;
+  const int t = row_ok ? m / a.H : 0;
+  const int h = row_ok ? m - t * a.H : 0;
+
+  const int L = a.prefix_lens[b];
+  const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
+  const int N = L + a.q;
+  const int k_begin = split * a.split_keys;
+
+  if (bad) {
+    // skipped sequence: zero output, lse = -inf (direct) or an empty partial
+    if (tid == 0 && rt == 0 && split == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_LEN);
+    if (row_ok && hh == 0) {
+      if (DIRECT) {
+        a.lse[(int64_t)b * a.M + m] = -INFINITY;
+        T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
+        for (int d = 0; d < R; ++d) o[d] = (T)0.0f;
+      } else {
+        a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = -INFINITY;
+      }
+    }
+    return;
+  }
+  if (k_begin >= N) return;                   // this split does not exist for sequence b
+  const int k_end = min(N, k_begin + a.split_keys);
+  const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
+
+  // Padding rows (m >= M) load token 0 / head 0: an output column of either
+  // contraction depends only on its own query column, and padding rows are
+  // never written, so no masking is needed.
+  frag qf[NCHUNK];
+  {
+    const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
+    const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+      if (c < R / KMF) qf[c] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
+      else qf[c] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
+    }
+  }
+  uint64_t vw0 = ~0ull, vw1 = ~0ull;
+  if (row_ok) {
+    const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
+    vw0 = vr[0];
+    vw1 = a.W > 1 ? vr[1] : 0ull;
+  }
+
+  const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
+  const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
+  const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
+  const uint32_t pe_ss = (uint32_t)(a.k_pe_ss * (int64_t)sizeof(T));
+
+  auto stage = [&](int tile, char* buf) {
+    const int kt = k_begin + tile * kBN;
+    const int nrows = min(kBN, k_end - kt);
+    stage_region<kBN, RC>(make_rsrc(kv_lat + (int64_t)kt * lat_ss, (uint32_t)nrows * lat_ss), lat_ss,
+                          nrows, buf, wave, lane);
+    stage_region<kBN, PC>(make_rsrc(kv_pe + (int64_t)kt * pe_ss, (uint32_t)nrows * pe_ss), pe_ss,
+                          nrows, buf + LAT_BYTES, wave, lane);
+  };
+
+  // Per-lane LDS byte offsets inside a tile buffer (bf16 only; the fp32 path
+  // computes its addresses inline).
+  //  * score operand, step c: chunk 2c + hh of key r.  Writing 2c + hh as
+  //    8 * (c / 4) + (2 * (c % 4) + hh), the swizzle only touches the low part,
+  //    so the address is qk_*[c % 4] + 128 * (c / 4).
+  //  * value operand, transposing read: in each 16-lane group, lane 4e + q
+  //    loads columns d0 + 4q .. d0 + 4q + 3 of key k_e and lane j then holds
+  //    column d0 + j of keys k_0..k_3.  Operand row d = 32 * db + r; slots 0-3
+  //    are keys c_row(8c + 0..3, hh), slots 4-7 keys c_row(8c + 4..7, hh).
+  //    The 16-byte chunk is 4 * db + x with x < 4, and (4 db + x) ^ s =
+  //    4 (db ^ s2) + (x ^ s01) for s2 = s >> 2, s01 = s & 3, so the address is
+  //    pv_base[c][half][db % 2] + 64 * db.
+  int qk_lat[4], qk_pe[4];
+  int pv_base[(PV_STEPS > 0 ? PV_STEPS : 1)][2][2];
+  if constexpr (KW == 8) {
+    const int sr = swz(r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qk_lat[j] = r * RC * 16 + (((2 * j + hh) ^ sr) << 4);
+      // rope region: chunk 2j + hh exists only while it is < PC
+      qk_pe[j] = LAT_BYTES + region_off<PC>(r, (2 * j + hh) < PC ? (2 * j + hh) : 0);
+    }
+    const int g = lane >> 4, sl = lane & 15;
+    const int e = sl >> 2, qd = sl & 3;
+    const int x = 2 * (g & 1) + (qd >> 1);
+#pragma unroll
+    for (int c = 0; c < PV_STEPS; ++c)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int k = c_row(c * 8 + 4 * half + e, hh);
+        const int sk = swz(k), s2 = sk >> 2, s01 = sk & 3;
+        const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
+        pv_base[c][half][0] = base + 64 * s2;     // even db: db ^ s2 = db + s2
+        pv_base[c][half][1] = base - 64 * s2;     // odd db:  db ^ s2 = db - s2
+      }
+  }
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+  // Softmax state of this lane's row (log2 domain).  m_ref is the reference
+  // the weights are taken against: fixed at the first tile with a visible key,
+  // it never moves while weights stay below 2^kRefSlack, so the accumulators
+  // are never rescaled.  m_max is the true running max.  If some row's max
+  // outgrows its reference by more than that, the wave stops accumulating
+  // ("dead"), keeps tracking m_max, and redoes the split once with
+  // m_ref = m_max (the exact max), which cannot trigger again.
+  float m_ref = -INFINITY, m_max = -INFINITY;
+  float l_run = 0.0f;           // this lane's share of sum_j exp2(s_j - m_ref)
+  bool dead = false;            // wave-uniform
+
+  if (tid == 0) s_dead = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      __syncthreads();
+      if (s_dead == 0) break;                 // common case: no redo
+      if (dead) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+        l_run = 0.0f;
+        m_ref = m_max;
+      }
+    }
+    const bool compute = (pass == 0) || dead;
+    dead = false;
+    stage(0, s_kv);
+#pragma unroll 1
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int kt = k_begin + tile * kBN;
+      char* buf = s_kv + (tile & 1) * BUF_BYTES;
+      wait_vmem();
+      __syncthreads();                        // tile `tile` is in LDS; the other buffer is free
+      if (tile + 1 < n_tiles) stage(tile + 1, s_kv + ((tile + 1) & 1) * BUF_BYTES);
+      if (!compute) continue;
+
+      // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T
+      f32x16 s;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCHUNK; ++c) {
+        const char* src;
+        if constexpr (KW == 8) {
+          // bf16: step c reads 16-byte chunk 2c + hh of the row; with the
+          // swizzle that is lane base qk_lat[c % 4] plus 128 * (c / 4)
+          if (c < R / KMF) src = buf + qk_lat[c & 3] + 128 * (c >> 2);
+          else src = buf + qk_pe[(c - R / KMF) & 3] + 128 * ((c - R / KMF) >> 2);
+        } else {
+          const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
+          if (c < R / KMF) src = buf + region_off<RC>(r, byte >> 4) + (byte & 15);
+          else src = buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
+        }
+        s = MM::mma(*reinterpret_cast<const frag*>(src), qf[c], s);
+      }
+
+      // ---- online softmax for this lane's row (16 of the tile's 32 keys)
+      float sv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = s[v] * a.scale_log2;
+      if (kt + kBN > L || kt + kBN > k_end) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = kt + c_row(v, hh);
+          const int uu = kk - L;                                  // tree node if >= 0
+          const uint64_t w = uu < 64 ? vw0 : vw1;
+          const bool tree_ok = uu < 0 || ((w >> (uu & 63)) & 1ull);
+          sv[v] = (kk < k_end && tree_ok) ? sv[v] : -INFINITY;
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+      mx = fmaxf(mx, xhalf(mx));
+      m_max = fmaxf(m_max, mx);
+      if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
+      if (!dead && __any(m_max > m_ref + kRefSlack)) {
+        dead = true;
+        s_dead = 1;
+      }
+      if (dead) continue;                     // keep tracking m_max only
+      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = exp2f(sv[v] - m_use);
+        l_run += p[v];
+      }
+
+      // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]
+#pragma unroll
+      for (int c = 0; c < PV_STEPS; ++c) {
+        const frag pf = MM::pack(p + c * KW);
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          frag va;
+          if constexpr (KW == 1) {
+            // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
+            const int col = (db * 32 + r) * (int)sizeof(T);
+            va = *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
+          } else {
+            // bf16: two transposing reads (lane bases computed before the loop)
+            const int o = 64 * db;
+            const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 1] + o);
+            const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 1] + o);
+            va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          acc[db] = MM::mma(va, pf, acc[db]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: normalise and write (direct) or write the partial
+  const float l_tot = l_run + xhalf(l_run);
+  const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_v = l_tot > 0.0f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (!row_ok) return;
+  if (DIRECT) {
+    T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
+        store4<T>(o + db * 32 + 8 * g + 4 * hh, v4);
+      }
+    if (hh == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
+  } else {
+    const int64_t prow = ((int64_t)b * a.max_splits + split) * a.M + m;
+    float* o = a.part_o + prow * R;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
+        store4<float>(o + db * 32 + 8 * g + 4 * hh, v4);
+      }
+    if (hh == 0) a.part_lse[prow] = lse_v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-split merge: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
+// One group of R/4 threads per row, each thread four consecutive columns;
+// splits with lse_k = -inf are skipped (their o_k is never read).
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
+    int B, int q, int H, int R, const int32_t* __restrict__ prefix_lens, int split_keys,
+    T* __restrict__ out, int64_t out_sb, int64_t out_st, int64_t out_sh, float* __restrict__ lse) {
+  const int tpr = R >> 2;
+  const int rows_per_wg = blockDim.x / tpr;
+  const int M = q * H;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + threadIdx.x / tpr;
+  const int cidx = threadIdx.x % tpr;
+  if (threadIdx.x >= rows_per_wg * tpr || row >= (int64_t)B * M) return;
+  const int b = (int)(row / M), m = (int)(row - (int64_t)b * M);
+  int ns = max_splits;
+  if (split_keys > 0) {
+    const int64_t n = (int64_t)prefix_lens[b] + q;
+    ns = (int)((n + split_keys - 1) / split_keys);
+    ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
+  }
+  const float* pl = part_lse + (int64_t)b * max_splits * M + m;
+  float mx = -INFINITY;
+  for (int k = 0; k < ns; ++k) mx = fmaxf(mx, pl[(int64_t)k * M]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float z = 0.0f;
+  if (mx != -INFINITY) {
+    for (int k = 0; k < ns; ++k) {
+      const float lk = pl[(int64_t)k * M];
+      if (lk == -INFINITY) continue;
+      const float w = __expf(lk - mx);
+      z += w;
+      const f32x4 o = *reinterpret_cast<const f32x4*>(
+          part_o + (((int64_t)b * max_splits + k) * M + m) * R + 4 * cidx);
+      acc[0] += w * o[0];
+      acc[1] += w * o[1];
+      acc[2] += w * o[2];
+      acc[3] += w * o[3];
+    }
+  }
+  const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+  float v4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v4[e] = acc[e] * inv;
+  const int t = m / H, h = m - (m / H) * H;
+  store4<T>(out + b * out_sb + t * out_st + h * out_sh + 4 * cidx, v4);
+  if (cidx == 0) lse[row] = z > 0.0f ? mx + logf(z) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+
+static int elem_size(int dtype) { return dtype == KDT_F32 ? 4 : dtype == KDT_BF16 ? 2 : 0; }
+
+static bool shape_supported(int dtype, int R, int P) {
+  if (dtype == KDT_BF16) return (R == 512 && P == 64) || (R == 64 && P == 16);
+  if (dtype == KDT_F32) return R == 64 && P == 16;
+  return false;
+}
+
+static int validate(const kdt_verify_desc* d) {
+  if (!d) return KDT_ERR_INVALID_ARG;
+  if (d->B <= 0 || d->q_len <= 0 || d->H <= 0 || d->R <= 0 || d->P <= 0) return KDT_ERR_INVALID_ARG;
+  if (!d->q_lat || !d->q_pe || !d->c_kv || !d->k_pe || !d->prefix_lens || !d->vis || !d->out || !d->lse)
+    return KDT_ERR_INVALID_ARG;
+  if (d->max_prefix_len < 0 || d->capacity < (int64_t)d->max_prefix_len + d->q_len)
+    return KDT_ERR_INVALID_ARG;
+  if (d->split_keys < 0 || (d->split_keys % 64) != 0) return KDT_ERR_INVALID_ARG;
+  if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
+  if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
+  if (!shape_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
+  const int64_t vec = 16 / elem_size(d->dtype);   // elements per 16 bytes
+  if (!aligned16(d->q_lat) || !aligned16(d->q_pe) || !aligned16(d->c_kv) || !aligned16(d->k_pe) ||
+      !aligned16(d->out))
+    return KDT_ERR_UNSUPPORTED;
+  const int64_t strides[] = {d->q_lat_sb, d->q_lat_st, d->q_lat_sh, d->q_pe_sb, d->q_pe_st, d->q_pe_sh,
+                             d->c_kv_sb, d->c_kv_ss, d->k_pe_sb, d->k_pe_ss,
+                             d->out_sb, d->out_st, d->out_sh};
+  for (int64_t s : strides)
+    if (s < 0 || s % vec) return KDT_ERR_UNSUPPORTED;
+  if ((int64_t)d->B * d->q_len * d->H > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
+  return KDT_OK;
+}
+
+static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
+  const int rc = validate(d);
+  if (rc != KDT_OK) return rc;
+  const int M = d->q_len * d->H;
+  const int n_rt = (M + kBM - 1) / kBM;
+  const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
+  int64_t sk = d->split_keys;
+  if (sk == 0) {
+    // Aim for about one workgroup per compute unit, but never let a split
+    // shrink below 256 keys (the partial it writes must stay small next to
+    // the work it does).
+    const int64_t base = (int64_t)d->B * n_rt;
+    const int64_t want = (kCU + base - 1) / base;
+    sk = (n_max + want - 1) / want;
+    sk = (sk + 63) / 64 * 64;
+    if (sk < 256) sk = 256;
+  }
+  const int64_t ns = (n_max + sk - 1) / sk;
+  if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
+  p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
+  p->max_splits = (int32_t)ns;
+  p->rows = M;
+  p->direct = ns == 1 ? 1 : 0;
+  const int64_t n_part_rows = (int64_t)d->B * ns * M;
+  const int64_t o_bytes = n_part_rows * d->R * 4;
+  p->part_o_offset = 0;
+  p->part_lse_offset = (o_bytes + 255) / 256 * 256;
+  p->workspace_bytes = (size_t)(p->part_lse_offset + n_part_rows * 4);
+  return KDT_OK;
+}
+
+static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, void* ws) {
+  VerifyArgs a;
+  a.q_lat = d->q_lat; a.q_lat_sb = d->q_lat_sb; a.q_lat_st = d->q_lat_st; a.q_lat_sh = d->q_lat_sh;
+  a.q_pe = d->q_pe; a.q_pe_sb = d->q_pe_sb; a.q_pe_st = d->q_pe_st; a.q_pe_sh = d->q_pe_sh;
+  a.c_kv = d->c_kv; a.c_kv_sb = d->c_kv_sb; a.c_kv_ss = d->c_kv_ss;
+  a.k_pe = d->k_pe; a.k_pe_sb = d->k_pe_sb; a.k_pe_ss = d->k_pe_ss;
+  a.capacity = d->capacity;
+  a.prefix_lens = d->prefix_lens;
+  a.vis = d->vis;
+  a.out = d->out; a.out_sb = d->out_sb; a.out_st = d->out_st; a.out_sh = d->out_sh;
+  a.lse = d->lse;
+  a.part_o = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_offset) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_lse_offset) : nullptr;
+  a.seq_status = d->seq_status;
+  a.scale_log2 = d->softmax_scale * kLog2e;
+  a.B = d->B; a.q = d->q_len; a.H = d->H; a.M = d->q_len * d->H; a.W = (d->q_len + 63) / 64;
+  a.n_rt = (a.M + kBM - 1) / kBM;
+  a.max_splits = p.max_splits;
+  a.split_keys = p.split_keys;
+  a.max_prefix_len = d->max_prefix_len;
+  return a;
+}
+
+template <typename T, int R, int P>
+static int launch_split(const VerifyArgs& a, bool direct, hipStream_t s) {
+  const int64_t grid = (int64_t)a.B * a.n_rt * a.max_splits;
+  if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
+  if (direct)
+    hipLaunchKernelGGL((verify_split_kernel<T, R, P, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((verify_split_kernel<T, R, P, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return launch_status();
+}
+
+static int dispatch_split(int dtype, int R, int P, const VerifyArgs& a, bool direct, hipStream_t s) {
+  if (dtype == KDT_BF16 && R == 512 && P == 64) return launch_split<__bf16, 512, 64>(a, direct, s);
+  if (dtype == KDT_BF16 && R == 64 && P == 16) return launch_split<__bf16, 64, 16>(a, direct, s);
+  if (dtype == KDT_F32 && R == 64 && P == 16) return launch_split<float, 64, 16>(a, direct, s);
+  return KDT_ERR_UNSUPPORTED;
+}
+
+static int launch_merge(int dtype, int B, int q, int H, int R, const float* po, const float* pl,
+                        int max_splits, const int32_t* prefix_lens, int split_keys, void* out,
+                        int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
+  const int tpr = R / 4;
+  const int rows_per_wg = 256 / tpr;
+  const int64_t rows = (int64_t)B * q * H;
+  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+  if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
+  if (dtype == KDT_BF16)
+    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3((unsigned)grid), dim3(rows_per_wg * tpr), 0, s, po, pl,
+                       max_splits, B, q, H, R, prefix_lens, split_keys, static_cast<__bf16*>(out), osb,
+                       ost, osh, lse);
+  else
+    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)grid), dim3(rows_per_wg * tpr), 0, s, po, pl,
+                       max_splits, B, q, H, R, prefix_lens, split_keys, static_cast<float*>(out), osb,
+                       ost, osh, lse);
+  return launch_status();
+}
+
+}  // namespace kdt
+
+extern "C" int kdt_verify_get_plan(const kdt_verify_desc* d, kdt_verify_plan* plan) {
+  if (!plan) return KDT_ERR_INVALID_ARG;
+  return kdt::make_plan(d, plan);
+}
+
+extern "C" int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+  kdt_verify_plan p;
+  const int rc = kdt::make_plan(d, &p);
+  if (rc != KDT_OK) return rc;
+  if (!p.direct && (!workspace || ws_bytes < p.workspace_bytes)) return KDT_ERR_WORKSPACE;
+  if (!p.direct && !kdt::aligned16(workspace)) return KDT_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const kdt::VerifyArgs a = kdt::make_args(d, p, p.direct ? nullptr : workspace);
+  int r = kdt::dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
+  if (r != KDT_OK || p.direct) return r;
+  return kdt::launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, a.part_o, a.part_lse, p.max_splits,
+                           d->prefix_lens, p.split_keys, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
+}
+
+extern "C" int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  kdt_verify_plan p;
+  const int rc = kdt::make_plan(d, &p);
+  if (rc != KDT_OK) return rc;
+  if (!workspace || ws_bytes < p.workspace_bytes || !kdt::aligned16(workspace)) return KDT_ERR_WORKSPACE;
+  const kdt::VerifyArgs a = kdt::make_args(d, p, workspace);
+  return kdt::dispatch_split(d->dtype, d->R, d->P, a, false, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32_t R,
+                                  const float* part_o, const float* part_lse, int32_t max_splits,
+                                  const int32_t* prefix_lens, int32_t split_keys, void* out,
+                                  int64_t out_sb, int64_t out_st, int64_t out_sh, float* lse,
+                                  void* stream) {
+  if (!part_o || !part_lse || !out || !lse) return KDT_ERR_INVALID_ARG;
+  if (B <= 0 || q_len <= 0 || H <= 0 || R <= 0 || max_splits <= 0 || split_keys < 0)
+    return KDT_ERR_INVALID_ARG;
+  if (split_keys > 0 && !prefix_lens) return KDT_ERR_INVALID_ARG;
+  if (dtype != KDT_F32 && dtype != KDT_BF16) return KDT_ERR_UNSUPPORTED;
+  if (R % 4 || R / 4 > 256) return KDT_ERR_UNSUPPORTED;
+  const int64_t vec = dtype == KDT_F32 ? 4 : 8;    // output elements per 16 bytes
+  if (!kdt::aligned16(part_o) || !kdt::aligned16(out) || (R % vec) || out_sb % vec || out_st % vec ||
+      out_sh % vec || out_sb < 0 || out_st < 0 || out_sh < 0)
+    return KDT_ERR_UNSUPPORTED;
+  return kdt::launch_merge(dtype, B, q_len, H, R, part_o, part_lse, max_splits, prefix_lens, split_keys,
+                           out, out_sb, out_st, out_sh, lse, static_cast<hipStream_t>(stream));
+}

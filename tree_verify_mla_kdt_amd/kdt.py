@@ -1,0 +1,248 @@
+"""ctypes binding of libkdt.so (the C ABI in include/kdt.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current HIP
+stream.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkdt.so")
+
+KDT_F32, KDT_BF16 = 0, 1
+KDT_SEQ_BAD_TREE, KDT_SEQ_BAD_LEN, KDT_SEQ_BAD_INDEX = 1, 2, 4
+MAX_Q_LEN = 128
+
+_c_i32, _c_i64, _c_p, _c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", _c_i32), ("B", _c_i32), ("q_len", _c_i32), ("H", _c_i32), ("R", _c_i32), ("P", _c_i32),
+        ("q_lat", _c_p), ("q_lat_sb", _c_i64), ("q_lat_st", _c_i64), ("q_lat_sh", _c_i64),
+        ("q_pe", _c_p), ("q_pe_sb", _c_i64), ("q_pe_st", _c_i64), ("q_pe_sh", _c_i64),
+        ("c_kv", _c_p), ("c_kv_sb", _c_i64), ("c_kv_ss", _c_i64),
+        ("k_pe", _c_p), ("k_pe_sb", _c_i64), ("k_pe_ss", _c_i64),
+        ("capacity", _c_i64),
+        ("prefix_lens", _c_p), ("max_prefix_len", _c_i32),
+        ("vis", _c_p),
+        ("softmax_scale", _c_f),
+        ("out", _c_p), ("out_sb", _c_i64), ("out_st", _c_i64), ("out_sh", _c_i64),
+        ("lse", _c_p),
+        ("seq_status", _c_p),
+        ("split_keys", _c_i32),
+    ]
+
+
+class VerifyPlan(ctypes.Structure):
+    _fields_ = [
+        ("split_keys", _c_i32), ("max_splits", _c_i32), ("rows", _c_i32), ("direct", _c_i32),
+        ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class KdtError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({status_str(code)})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkdt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tree_verify_mla_kdt_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kdt_abi_version.restype = ctypes.c_int
+        L.kdt_status_str.restype = ctypes.c_char_p
+        L.kdt_status_str.argtypes = [ctypes.c_int]
+        L.kdt_build_visibility.argtypes = [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]
+        L.kdt_verify_get_plan.argtypes = [ctypes.POINTER(VerifyDesc), ctypes.POINTER(VerifyPlan)]
+        L.kdt_verify_attn.argtypes = [ctypes.POINTER(VerifyDesc), _c_p, ctypes.c_size_t, _c_p]
+        L.kdt_verify_partials.argtypes = [ctypes.POINTER(VerifyDesc), _c_p, ctypes.c_size_t, _c_p]
+        L.kdt_merge_partials.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p,
+                                         _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]
+        L.kdt_gather_accepted.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
+                                          _c_i64, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p]
+        for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_partials",
+                   "kdt_merge_partials", "kdt_gather_accepted"):
+            getattr(L, fn).restype = ctypes.c_int
+        if L.kdt_abi_version() != 1:
+            raise RuntimeError("libkdt.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return lib().kdt_status_str(int(code)).decode()
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise KdtError(fn, code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDT_BF16
+    if t.dtype == torch.float32:
+        return KDT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+
+def build_visibility(parents: torch.Tensor, vis=None, depth=None, seq_status=None, stream=None):
+    """parents int32 [B, q] -> (vis int64 [B, q, W] holding uint64 bits, depth int32 [B, q])."""
+    assert parents.dtype == torch.int32 and parents.is_contiguous() and parents.dim() == 2
+    B, q = parents.shape
+    W = (q + 63) // 64
+    if vis is None:
+        vis = torch.empty((B, q, W), dtype=torch.int64, device=parents.device)
+    if depth is None:
+        depth = torch.empty((B, q), dtype=torch.int32, device=parents.device)
+    _check("kdt_build_visibility", lib().kdt_build_visibility(
+        _ptr(parents), B, q, _ptr(vis), _ptr(depth), _ptr(seq_status), _stream(stream)))
+    return vis, depth
+
+
+def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
+                 seq_status, split_keys):
+    B, q, H, R = q_lat.shape
+    P = q_pe.shape[-1]
+    d = VerifyDesc()
+    d.dtype = _dtype_code(q_lat)
+    d.B, d.q_len, d.H, d.R, d.P = B, q, H, R, P
+    d.q_lat = q_lat.data_ptr(); d.q_lat_sb, d.q_lat_st, d.q_lat_sh = q_lat.stride()[:3]
+    d.q_pe = q_pe.data_ptr(); d.q_pe_sb, d.q_pe_st, d.q_pe_sh = q_pe.stride()[:3]
+    d.c_kv = c_kv.data_ptr(); d.c_kv_sb, d.c_kv_ss = c_kv.stride()[:2]
+    d.k_pe = k_pe.data_ptr(); d.k_pe_sb, d.k_pe_ss = k_pe.stride()[:2]
+    d.capacity = c_kv.shape[1]
+    d.prefix_lens = prefix_lens.data_ptr()
+    d.max_prefix_len = int(max_prefix_len)
+    d.vis = vis.data_ptr()
+    d.softmax_scale = float(softmax_scale)
+    d.out = out.data_ptr(); d.out_sb, d.out_st, d.out_sh = out.stride()[:3]
+    d.lse = lse.data_ptr()
+    d.seq_status = 0 if seq_status is None else seq_status.data_ptr()
+    d.split_keys = int(split_keys)
+    return d
+
+
+def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
+                    seq_status, split_keys):
+    for t in (q_lat, q_pe, c_kv, k_pe):
+        if t.stride(-1) != 1:
+            raise ValueError("innermost dimension must be contiguous")
+    if not (q_lat.dtype == q_pe.dtype == c_kv.dtype == k_pe.dtype):
+        raise TypeError("q_lat, q_pe, c_kv and k_pe must share one dtype")
+    assert prefix_lens.dtype == torch.int32 and vis.dtype == torch.int64
+    B, q, H, R = q_lat.shape
+    if max_prefix_len is None:
+        max_prefix_len = c_kv.shape[1] - q        # always an upper bound on a valid prefix
+    if out is None:
+        out = torch.empty((B, q, H, R), dtype=q_lat.dtype, device=q_lat.device)
+    if lse is None:
+        lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
+    d = _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
+                     seq_status, split_keys)
+    return d, out, lse
+
+
+def verify_plan(desc: VerifyDesc) -> VerifyPlan:
+    p = VerifyPlan()
+    _check("kdt_verify_get_plan", lib().kdt_verify_get_plan(ctypes.byref(desc), ctypes.byref(p)))
+    return p
+
+
+def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
+                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None):
+    """Tree-verify attention.  c_kv [B, S, R] and k_pe [B, S, P] may be views of
+    one fused [B, S, R+P] cache.  Returns (out [B, q, H, R], lse [B, q, H])."""
+    d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
+                                  out, lse, seq_status, split_keys)
+    p = verify_plan(d)
+    if p.workspace_bytes and (workspace is None or workspace.numel() * workspace.element_size() < p.workspace_bytes):
+        workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("kdt_verify_attn", lib().kdt_verify_attn(ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None,
+                    workspace=None, seq_status=None, split_keys=0, stream=None):
+    """Split stage only.  Returns (part_o [B, S, M, R], part_lse [B, S, M], plan)."""
+    d, _, _ = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
+                              None, None, seq_status, split_keys)
+    p = verify_plan(d)
+    need = max(int(p.workspace_bytes), 1)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        B, M, R, S = q_lat.shape[0], p.rows, q_lat.shape[3], p.max_splits
+        rows = B * S * M
+        need = max(need, p.part_lse_offset + rows * 4)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("kdt_verify_partials", lib().kdt_verify_partials(ctypes.byref(d), _ptr(workspace), ws_bytes,
+                                                           _stream(stream)))
+    B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
+    part_o = workspace[p.part_o_offset:p.part_o_offset + B * S * M * R * 4].view(torch.float32).view(B, S, M, R)
+    part_lse = workspace[p.part_lse_offset:p.part_lse_offset + B * S * M * 4].view(torch.float32).view(B, S, M)
+    return part_o, part_lse, p
+
+
+def merge_partials(part_o, part_lse, q_len, H, out_dtype, prefix_lens=None, split_keys=0, out=None, lse=None,
+                   stream=None):
+    """part_o float32 [B, S, q*H, R], part_lse float32 [B, S, q*H] -> (out [B, q, H, R], lse [B, q, H])."""
+    B, S, M, R = part_o.shape
+    assert M == q_len * H and part_o.is_contiguous() and part_lse.is_contiguous()
+    if out is None:
+        out = torch.empty((B, q_len, H, R), dtype=out_dtype, device=part_o.device)
+    if lse is None:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=part_o.device)
+    code = KDT_BF16 if out.dtype == torch.bfloat16 else KDT_F32
+    sb, st, sh = out.stride()[:3]
+    _check("kdt_merge_partials", lib().kdt_merge_partials(
+        code, B, q_len, H, R, _ptr(part_o), _ptr(part_lse), S, _ptr(prefix_lens), int(split_keys), _ptr(out),
+        sb, st, sh, _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def gather_accepted(cache, prefix_lens, accepted, n_accepted, q_len, row_elems=None, num_layers=1,
+                    layer_stride=0, new_prefix_lens=None, seq_status=None, stream=None):
+    """In-place accepted-path gather on cache [B, S, C] (or the layer-0 view of
+    a [layers, B, S, C] cache with layer_stride in elements)."""
+    assert accepted.dtype == torch.int32 and n_accepted.dtype == torch.int32 and accepted.is_contiguous()
+    B = cache.shape[0]
+    if row_elems is None:
+        row_elems = cache.shape[2]
+    sb, ss = cache.stride()[:2]
+    _check("kdt_gather_accepted", lib().kdt_gather_accepted(
+        _dtype_code(cache), B, int(q_len), int(row_elems), _ptr(cache), sb, ss, cache.shape[1], int(num_layers),
+        int(layer_stride), _ptr(prefix_lens), _ptr(accepted), _ptr(n_accepted), accepted.shape[1],
+        _ptr(new_prefix_lens), _ptr(seq_status), _stream(stream)))
+    return cache
+
+
+def softmax_scale_for(R: int, P: int) -> float:
+    return 1.0 / math.sqrt(R + P)
