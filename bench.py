@@ -1,0 +1,276 @@
+"""Benchmark: tree-verify MLA-absorb attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload max_budget]
+
+One step = the whole hot path over one batch: visibility masks from parent
+pointers, split-prefix verify attention + log-sum-exp merge, and the
+accepted-path gather.  Inputs are seeded synthetic tensors of the workload's
+shape, resident in HBM before timing starts; the step rotates over enough input
+copies (> 256 MB) that the Infinity Cache cannot hold them all.
+
+Printed: one JSON line (metric, tree-tokens/s, ms per step, ...) with
+  roofline     the verify-split kernel: algorithmic flops per launch / its mean
+               launch time, timed with HIP events on the stream it runs on,
+               against the MI355X dense bf16 MFMA peak;
+  cpu_baseline the float64 CPU oracle timed on the same workload (rank 0, N=1).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "verify-attn tree-tokens/sec + MFMA util % and HBM GB/s at q_len=65, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="max_budget",
+                    help="max_budget | batched | long_ctx | ragged_deep | tiny_fp32 (optionally :q1)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only run the verify-split kernel in the loop (for counter collection)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="run a plain device copy of MB megabytes --steps times (counter calibration)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_verify_mla_kdt_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(parents: np.ndarray, prefix_lens: np.ndarray, H: int) -> int:
+    """Number of visible (query row, key) pairs: prefix keys plus ancestors-or-self."""
+    B, q = parents.shape
+    total = 0
+    for b in range(B):
+        depth = np.zeros(q, dtype=np.int64)
+        for i in range(1, q):
+            depth[i] = depth[parents[b, i]] + 1
+        total += H * (q * int(prefix_lens[b]) + int(np.sum(depth + 1)))
+    return total
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tree_verify_mla_kdt_amd import kdt, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": args.steps}))
+        return
+
+    name, _, variant = args.workload.partition(":")
+    cfg = synth.CONFIGS[name]
+    if variant == "q1":
+        cfg = synth.config_variant(cfg, q_len=1)
+    inp = synth.generate(cfg)
+    B, q, H, R, P = cfg.B, cfg.q_len, cfg.H, cfg.R, cfg.P
+
+    def t_of(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # --- resident inputs, rotated over > Infinity Cache size
+    per_copy = inp.cache.nbytes + inp.q_lat.nbytes + inp.q_pe.nbytes
+    n_copies = max(2, min(64, -(-(INFINITY_CACHE_BYTES + (32 << 20)) // per_copy)))
+    base = {"cache": t_of(inp.cache), "q_lat": t_of(inp.q_lat), "q_pe": t_of(inp.q_pe)}
+    copies = [{k: v.clone() for k, v in base.items()} for _ in range(n_copies)]
+    parents = torch.from_numpy(inp.parents).to(dev)
+    prefix_lens = torch.from_numpy(inp.prefix_lens).to(dev)
+    accepted = torch.from_numpy(inp.accepted).to(dev)
+    n_acc = torch.from_numpy(inp.n_accepted).to(dev)
+    max_prefix = int(inp.prefix_lens.max())
+    W = (q + 63) // 64
+    vis = torch.empty((B, q, W), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, q), dtype=torch.int32, device=dev)
+    out = torch.empty((B, q, H, R), dtype=base["q_lat"].dtype, device=dev)
+    lse = torch.empty((B, q, H), dtype=torch.float32, device=dev)
+    new_pl = torch.empty_like(prefix_lens)
+
+    c0 = copies[0]
+    desc, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
+                                     prefix_lens, vis, cfg.softmax_scale, max_prefix, out, lse, None, 0)
+    plan = kdt.verify_plan(desc)
+    ws_bytes = max(int(plan.workspace_bytes), int(plan.part_lse_offset + B * plan.max_splits * plan.rows * 4))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        c = copies[i % n_copies]
+        kdt.build_visibility(parents, vis=vis, depth=depth)
+        kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
+                        cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws)
+        kdt.gather_accepted(c["cache"], prefix_lens, accepted, n_acc, q, new_prefix_lens=new_pl)
+
+    def split_only(i):
+        c = copies[i % n_copies]
+        kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
+                            cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws)
+
+    # Launches are replayed from HIP graphs: one graph runs the step once per
+    # input copy, so host launch overhead stays out of the measured step time.
+    def capture(fn, idx):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in idx:
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in idx:
+                fn(i)
+        return g
+
+    kdt.build_visibility(parents, vis=vis, depth=depth)
+    fn = split_only if args.kernel_only else step
+    g_all = capture(fn, range(n_copies))
+    g_one = [capture(fn, [i]) for i in range(max(args.steps % n_copies, args.warmup % n_copies, 1))]
+
+    def run_steps(k):
+        full, rem = divmod(k, n_copies)
+        for _ in range(full):
+            g_all.replay()
+        for i in range(rem):
+            g_one[i].replay()
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+
+    # --- timed region: exactly K steps
+    t0 = time.perf_counter()
+    run_steps(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # --- the dominant kernel alone, HIP events on the stream the graph runs on
+    g_split = g_all if args.kernel_only else capture(split_only, range(n_copies))
+    reps = max(1, -(-max(args.steps, 50) // n_copies))
+    g_split.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    for _ in range(reps):
+        g_split.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    split_ms = e0.elapsed_time(e1) / (reps * n_copies)
+
+    pairs = visible_pairs(inp.parents, inp.prefix_lens, H)
+    flops = pairs * 2 * (R + P + R)                       # score over R+P, value over R
+    esz = 2 if cfg.dtype == "bf16" else 4
+    kv_bytes = int(np.sum(inp.prefix_lens.astype(np.int64) + q)) * (R + P) * esz
+    alg_bytes = (kv_bytes + B * q * H * (R + P) * esz + B * q * H * R * esz + B * q * H * 4
+                 + B * q * W * 8 + B * q * 4)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    achieved = flops / (split_ms * 1e-3) / 1e12
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_verify_split_{args.workload.replace(':', '_')}.json")
+    if os.path.exists(tfile):
+        rec = json.load(open(tfile))
+        if rec.get("source_hash") == source_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    tokens = B * q
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tensors and random trees of the workload's shape)",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": B, "heads": H, "kv_lora_rank": R,
+                   "rope_dim": P, "q_len": q, "prefix_len_max": max_prefix,
+                   "split_keys": plan.split_keys, "splits": plan.max_splits,
+                   "step": "build_visibility + verify (split + merge) + gather_accepted",
+                   "input_copies": n_copies, "kernel_only": bool(args.kernel_only)},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "verify_split_kernel", "kernel_ms": split_ms,
+                     "flops_per_launch": flops, "visible_pairs": pairs},
+        "mfma_util": flops / (ms_per_step * 1e-3) / 1e12 / peak,
+        "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": alg_bytes,
+    }
+
+    if not args.no_cpu and not args.kernel_only:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the float64 oracle (as it stands) on the same workload: masks,
+    verify attention and gather, repeated until ~budget_s of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:      # threadpoolctl missing: numpy's BLAS uses every core by default
+        threads = os.cpu_count() or 1
+    cfg = inp.cfg
+    R = cfg.R
+    cache = inp.f64("cache")
+    ql, qp = inp.f64("q_lat"), inp.f64("q_pe")
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        vis, _ = oracle.build_visibility(inp.parents)
+        oracle.verify_attn(ql, qp, cache[..., :R], cache[..., R:], inp.prefix_lens, vis, cfg.softmax_scale)
+        oracle.gather_accepted(inp.cache, inp.prefix_lens, inp.accepted, inp.n_accepted)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    per = el / n
+    return {"value": cfg.B * cfg.q_len / per, "unit": "tree-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full {cfg.name} workload (masks + verify + gather), {n} repetitions, {el:.1f} s",
+            "seconds_per_step": per}
+
+
+if __name__ == "__main__":
+    main()
