@@ -167,6 +167,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // lane, so each lane fetches the global chunk that belongs in its slot.  Rows
 // at or past `nrows` (the end of the split) re-read row nrows-1: the softmax
 // gives them zero weight, and this keeps every LDS value a finite cache value.
+// `wave` must be wave-uniform (an SGPR): the LDS destination and, for regions
+// of 64 chunks per row, the source row are then scalar and each load needs a
+// single per-lane offset register.
 template <int ROWS, int NCH>
 __device__ __forceinline__ void stage_region(__amdgpu_buffer_rsrc_t rs, uint32_t ss, int nrows,
                                              char* lds, int wave, int lane) {
@@ -178,12 +181,22 @@ __device__ __forceinline__ void stage_region(__amdgpu_buffer_rsrc_t rs, uint32_t
   for (int jj = 0; jj < PER_WAVE; ++jj) {
     const int j = wave + jj * WAVES;
     if ((SLOTS / 64) % WAVES != 0 && j >= SLOTS / 64) break;
-    const int slot = j * 64 + lane;
-    const int row = slot / NCH, pc = slot - row * NCH;
-    const int c = (NCH % 8 == 0) ? (pc ^ swz(row)) : pc;
-    const int src_row = row < nrows ? row : nrows - 1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + j * 1024), 16,
-                                             (uint32_t)src_row * ss + (uint32_t)c * 16, 0, 0, 0);
+    uint32_t voff, soff;
+    if constexpr (NCH == 64) {
+      // one row per instruction: the row (and its swizzle) is wave-uniform
+      const int row = j;
+      const int src_row = row < nrows ? row : nrows - 1;
+      voff = (uint32_t)(lane ^ swz(row)) * 16;
+      soff = (uint32_t)src_row * ss;
+    } else {
+      const int slot = j * 64 + lane;
+      const int row = slot / NCH, pc = slot - row * NCH;
+      const int c = (NCH % 8 == 0) ? (pc ^ swz(row)) : pc;
+      const int src_row = row < nrows ? row : nrows - 1;
+      voff = (uint32_t)src_row * ss + (uint32_t)c * 16;
+      soff = 0;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + j * 1024), 16, voff, soff, 0, 0);
   }
 }
 
@@ -203,8 +216,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   static_assert(R % 32 == 0 && D % KMF == 0 && (P * sizeof(T)) % 16 == 0, "shape");
   static_assert(KW != 8 || (RC % 8 == 0 && (PC % 8 == 0 || P <= 32)), "bf16 score addressing");
 
-  __shared__ __attribute__((aligned(1024))) char s_kv[2 * BUF_BYTES];
+  // Two distinct LDS objects (not one array indexed at run time) so the
+  // compiler can tell the DMA into one buffer from the reads of the other and
+  // does not wait for the prefetch before computing.
+  __shared__ __attribute__((aligned(1024))) char s_buf0[BUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_buf1[BUF_BYTES];
   __shared__ int s_dead;
+  // One accumulator block per lane parks here while the score tile is alive
+  // (all 512 registers are otherwise taken: 256 accumulators, Q, scores).
+  constexpr bool STASH = (NB == 16);
+  __shared__ __attribute__((aligned(16))) f32x4 s_stash[STASH ? kThreads * 4 : 1];
 
   const int u = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = u % a.n_rt;
@@ -212,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int b = u / (a.n_rt * a.max_splits);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int m = rt * kBM + wave * 32 + r;     // this lane's query row
   const bool row_ok = m < a.M;
@@ -329,6 +350,102 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   float l_run = 0.0f;           // this lane's share of sum_j exp2(s_j - m_ref)
   bool dead = false;            // wave-uniform
 
+  // One key tile: scores, softmax, value contraction.  `buf` is one of the
+  // two LDS buffers; the tile's first key is kt.
+  auto tile_body = [&](const int tile, const char* buf) {
+    const int kt = k_begin + tile * kBN;
+    if constexpr (STASH) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        s_stash[g * kThreads + tid] = f32x4{acc[NB - 1][4 * g], acc[NB - 1][4 * g + 1], acc[NB - 1][4 * g + 2],
+                                            acc[NB - 1][4 * g + 3]};
+    }
+    // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+      const char* src;
+      if constexpr (KW == 8) {
+        // bf16: step c reads 16-byte chunk 2c + hh of the row; with the
+        // swizzle that is lane base qk_lat[c % 4] plus 128 * (c / 4)
+        if (c < R / KMF) src = buf + qk_lat[c & 3] + 128 * (c >> 2);
+        else src = buf + qk_pe[(c - R / KMF) & 3] + 128 * ((c - R / KMF) >> 2);
+      } else {
+        const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
+        if (c < R / KMF) src = buf + region_off<RC>(r, byte >> 4) + (byte & 15);
+        else src = buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
+      }
+      s = MM::mma(*reinterpret_cast<const frag*>(src), qf[c], s);
+    }
+
+    // ---- online softmax for this lane's row (16 of the tile's 32 keys)
+    float sv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = s[v] * a.scale_log2;
+    if (kt + kBN > L || kt + kBN > k_end) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = kt + c_row(v, hh);
+        const int uu = kk - L;                                  // tree node if >= 0
+        const uint64_t w = uu < 64 ? vw0 : vw1;
+        const bool tree_ok = uu < 0 || ((w >> (uu & 63)) & 1ull);
+        sv[v] = (kk < k_end && tree_ok) ? sv[v] : -INFINITY;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+    mx = fmaxf(mx, xhalf(mx));
+    m_max = fmaxf(m_max, mx);
+    if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
+    if (!dead && __any(m_max > m_ref + kRefSlack)) {
+      dead = true;
+      s_dead = 1;
+    }
+    if constexpr (STASH) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = s_stash[g * kThreads + tid];
+        acc[NB - 1][4 * g] = v[0];
+        acc[NB - 1][4 * g + 1] = v[1];
+        acc[NB - 1][4 * g + 2] = v[2];
+        acc[NB - 1][4 * g + 3] = v[3];
+      }
+    }
+    if (dead) return;                       // keep tracking m_max only
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(sv[v] - m_use);
+      l_run += p[v];
+    }
+
+    // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]
+#pragma unroll
+    for (int c = 0; c < PV_STEPS; ++c) {
+      const frag pf = MM::pack(p + c * KW);
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        frag va;
+        if constexpr (KW == 1) {
+          // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
+          const int col = (db * 32 + r) * (int)sizeof(T);
+          va = *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
+        } else {
+          // bf16: two transposing reads (lane bases computed before the loop)
+          const int o = 64 * db;
+          const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 1] + o);
+          const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 1] + o);
+          va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        acc[db] = MM::mma(va, pf, acc[db]);
+      }
+    }
+  };
+
   if (tid == 0) s_dead = 0;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
@@ -346,90 +463,21 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     }
     const bool compute = (pass == 0) || dead;
     dead = false;
-    stage(0, s_kv);
+    stage(0, s_buf0);
+    // Tiles alternate between the two buffers; each step waits for its own
+    // tile, then starts the DMA of the next tile into the other buffer and
+    // computes while that copy is in flight.
 #pragma unroll 1
-    for (int tile = 0; tile < n_tiles; ++tile) {
-      const int kt = k_begin + tile * kBN;
-      char* buf = s_kv + (tile & 1) * BUF_BYTES;
+    for (int tile = 0; tile < n_tiles; tile += 2) {
       wait_vmem();
-      __syncthreads();                        // tile `tile` is in LDS; the other buffer is free
-      if (tile + 1 < n_tiles) stage(tile + 1, s_kv + ((tile + 1) & 1) * BUF_BYTES);
-      if (!compute) continue;
-
-      // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T
-      f32x16 s;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NCHUNK; ++c) {
-        const char* src;
-        if constexpr (KW == 8) {
-          // bf16: step c reads 16-byte chunk 2c + hh of the row; with the
-          // swizzle that is lane base qk_lat[c % 4] plus 128 * (c / 4)
-          if (c < R / KMF) src = buf + qk_lat[c & 3] + 128 * (c >> 2);
-          else src = buf + qk_pe[(c - R / KMF) & 3] + 128 * ((c - R / KMF) >> 2);
-        } else {
-          const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
-          if (c < R / KMF) src = buf + region_off<RC>(r, byte >> 4) + (byte & 15);
-          else src = buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
-        }
-        s = MM::mma(*reinterpret_cast<const frag*>(src), qf[c], s);
-      }
-
-      // ---- online softmax for this lane's row (16 of the tile's 32 keys)
-      float sv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sv[v] = s[v] * a.scale_log2;
-      if (kt + kBN > L || kt + kBN > k_end) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = kt + c_row(v, hh);
-          const int uu = kk - L;                                  // tree node if >= 0
-          const uint64_t w = uu < 64 ? vw0 : vw1;
-          const bool tree_ok = uu < 0 || ((w >> (uu & 63)) & 1ull);
-          sv[v] = (kk < k_end && tree_ok) ? sv[v] : -INFINITY;
-        }
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-      mx = fmaxf(mx, xhalf(mx));
-      m_max = fmaxf(m_max, mx);
-      if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
-      if (!dead && __any(m_max > m_ref + kRefSlack)) {
-        dead = true;
-        s_dead = 1;
-      }
-      if (dead) continue;                     // keep tracking m_max only
-      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-      float p[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = exp2f(sv[v] - m_use);
-        l_run += p[v];
-      }
-
-      // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]
-#pragma unroll
-      for (int c = 0; c < PV_STEPS; ++c) {
-        const frag pf = MM::pack(p + c * KW);
-#pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          frag va;
-          if constexpr (KW == 1) {
-            // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
-            const int col = (db * 32 + r) * (int)sizeof(T);
-            va = *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
-          } else {
-            // bf16: two transposing reads (lane bases computed before the loop)
-            const int o = 64 * db;
-            const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 1] + o);
-            const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 1] + o);
-            va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-          acc[db] = MM::mma(va, pf, acc[db]);
-        }
-      }
+      __syncthreads();
+      if (tile + 1 < n_tiles) stage(tile + 1, s_buf1);
+      if (compute) tile_body(tile, s_buf0);
+      if (tile + 1 >= n_tiles) break;
+      wait_vmem();
+      __syncthreads();
+      if (tile + 2 < n_tiles) stage(tile + 2, s_buf0);
+      if (compute) tile_body(tile + 1, s_buf1);
     }
   }
 
