@@ -118,7 +118,22 @@ struct VerifyArgs {
 // half hh (lane / 32) sits in row 8*(v/4) + 4*hh + (v%4) of the 32-row block.
 __device__ __forceinline__ int c_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
 
-__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by the lane 32 away.  v_permlane32_swap
+// (called with the same register twice) returns, in some order, the lane's
+// own value and its partner's, so a symmetric operation of the pair is the
+// same on both lanes; it is a plain VALU instruction, unlike a DS permute.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Scheduling fence: MFMAs and LDS accesses keep their program order around it,
+// while VALU, SALU and transcendental instructions may still move across.
+__device__ __forceinline__ void fence_mem_mfma() { __builtin_amdgcn_sched_barrier(0x0406); }
 
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const float* v);
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 
   // One key tile: scores, softmax, value contraction.  `buf` is one of the
   // two LDS buffers; the tile's first key is kt.
-  auto tile_body = [&](const int tile, const char* buf) {
+  auto tile_body = [&](const int tile, const char* buf) __attribute__((always_inline)) {
     const int kt = k_begin + tile * kBN;
     if constexpr (STASH) {
 #pragma unroll
@@ -360,31 +375,40 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         s_stash[g * kThreads + tid] = f32x4{acc[NB - 1][4 * g], acc[NB - 1][4 * g + 1], acc[NB - 1][4 * g + 2],
                                             acc[NB - 1][4 * g + 3]};
     }
-    // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T
+    // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T.
+    // The K fragments are read QPF steps ahead of the MFMA chain.
+    auto score_src = [&](int c) __attribute__((always_inline)) -> const char* {
+      if constexpr (KW == 8) {
+        // bf16: step c reads 16-byte chunk 2c + hh of the row; with the
+        // swizzle that is lane base qk_lat[c % 4] plus 128 * (c / 4)
+        if (c < R / KMF) return buf + qk_lat[c & 3] + 128 * (c >> 2);
+        return buf + qk_pe[(c - R / KMF) & 3] + 128 * ((c - R / KMF) >> 2);
+      } else {
+        const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
+        if (c < R / KMF) return buf + region_off<RC>(r, byte >> 4) + (byte & 15);
+        return buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
+      }
+    };
+    constexpr int QPF = NCHUNK < 4 ? NCHUNK : 4;
+    frag kf[QPF];
+#pragma unroll
+    for (int c = 0; c < QPF; ++c) kf[c] = *reinterpret_cast<const frag*>(score_src(c));
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCHUNK; ++c) {
-      const char* src;
-      if constexpr (KW == 8) {
-        // bf16: step c reads 16-byte chunk 2c + hh of the row; with the
-        // swizzle that is lane base qk_lat[c % 4] plus 128 * (c / 4)
-        if (c < R / KMF) src = buf + qk_lat[c & 3] + 128 * (c >> 2);
-        else src = buf + qk_pe[(c - R / KMF) & 3] + 128 * ((c - R / KMF) >> 2);
-      } else {
-        const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
-        if (c < R / KMF) src = buf + region_off<RC>(r, byte >> 4) + (byte & 15);
-        else src = buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
-      }
-      s = MM::mma(*reinterpret_cast<const frag*>(src), qf[c], s);
+      const frag cur = kf[c % QPF];
+      if (c + QPF < NCHUNK) kf[c % QPF] = *reinterpret_cast<const frag*>(score_src(c + QPF));
+      s = MM::mma(cur, qf[c], s);
+      fence_mem_mfma();
     }
 
     // ---- online softmax for this lane's row (16 of the tile's 32 keys)
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = s[v] * a.scale_log2;
-    if (kt + kBN > L || kt + kBN > k_end) {
+    if (kt + kBN > L || kt + kBN > k_end) {   // only tiles reaching the tree or the split end
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kk = kt + c_row(v, hh);
@@ -397,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     float mx = sv[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = fmaxf(mx, xhalf(mx));
+    mx = xhalf_max(mx);
     m_max = fmaxf(m_max, mx);
     if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
     if (!dead && __any(m_max > m_ref + kRefSlack)) {
@@ -423,26 +447,35 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       l_run += p[v];
     }
 
-    // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]
-#pragma unroll
-    for (int c = 0; c < PV_STEPS; ++c) {
-      const frag pf = MM::pack(p + c * KW);
-#pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        frag va;
-        if constexpr (KW == 1) {
-          // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
-          const int col = (db * 32 + r) * (int)sizeof(T);
-          va = *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
-        } else {
-          // bf16: two transposing reads (lane bases computed before the loop)
-          const int o = 64 * db;
-          const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 1] + o);
-          const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 1] + o);
-          va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        acc[db] = MM::mma(va, pf, acc[db]);
+    // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]; the value operand of
+    // step i + VPF is read while step i's MFMA is issued.
+    auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
+      if constexpr (KW == 1) {
+        // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
+        const int col = (db * 32 + r) * (int)sizeof(T);
+        return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
+      } else {
+        // bf16: two transposing reads (lane bases computed before the loop)
+        const int o = 64 * db;
+        const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 1] + o);
+        const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 1] + o);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+    };
+    frag pfr[PV_STEPS];
+#pragma unroll
+    for (int c = 0; c < PV_STEPS; ++c) pfr[c] = MM::pack(p + c * KW);
+    constexpr int STEPS = PV_STEPS * NB;
+    constexpr int VPF = STEPS < 2 ? STEPS : 2;
+    frag vq[VPF + 1];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NB, i % NB);
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      const int c = i / NB, db = i % NB;
+      if (i + VPF < STEPS) vq[(i + VPF) % (VPF + 1)] = value_frag((i + VPF) / NB, (i + VPF) % NB);
+      acc[db] = MM::mma(vq[i % (VPF + 1)], pfr[c], acc[db]);
+      fence_mem_mfma();
     }
   };
 
@@ -482,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   }
 
   // ---- epilogue: normalise and write (direct) or write the partial
-  const float l_tot = l_run + xhalf(l_run);
+  const float l_tot = xhalf_sum(l_run);
   const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
