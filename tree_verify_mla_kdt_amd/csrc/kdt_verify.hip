@@ -58,7 +58,15 @@ constexpr int kThreads = 256;     // 4 waves
 constexpr int kCU = 256;          // MI355X compute units (split heuristic)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRefSlack = 32.0f;    // max weight 2^32 against the reference (log2 units)
+constexpr float kRefSlack = 32.0f;
+// LDS operand fragments kept in flight ahead of the MFMA that consumes them
+// (LDS latency under load is a few hundred cycles, one MFMA about forty).
+#ifndef KDT_SCORE_PREFETCH
+#define KDT_SCORE_PREFETCH 4
+#endif
+#ifndef KDT_VALUE_PREFETCH
+#define KDT_VALUE_PREFETCH 2
+#endif    // max weight 2^32 against the reference (log2 units)
 
 template <typename T>
 struct Mfma;
@@ -148,17 +156,29 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const float* v) {
 
 // LDS image of one key tile.  Two regions: kBN rows of the c_kv part (RC
 // 16-byte chunks per row) followed by kBN rows of the k_pe part (PC chunks).
-// Within a region whose rows hold a multiple of 8 chunks, chunk c of row k is
-// stored at chunk position c ^ swz(k).  swz is a bijection on k % 8, so the
-// score-operand reads (8 consecutive keys, same chunk) hit 8 different 16-byte
-// bank groups, and its upper two bits differ for any 4 consecutive keys, so a
-// transposing read (4 keys x 2 adjacent chunks) also touches 8 distinct groups.
-__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
+// Chunk c of row k is stored at chunk position c ^ swz_of<NCH>(k).  The LDS
+// serves 64 banks x 4 bytes, i.e. one 256-byte window (16 chunks) per cycle:
+//  * rows of a multiple of 16 chunks start on the same banks, so the swizzle
+//    s16(k) = ((k & 3) << 2) | ((k >> 2) & 3) permutes 16-chunk groups.  It is
+//    a bijection on k % 16 (16 consecutive keys reading one chunk for the
+//    score operand hit 16 different chunks), and for 4 consecutive keys 4j..4j+3
+//    its upper two bits are 0, 1, 2, 3, so a transposing read (4 keys x 4
+//    adjacent chunks) covers all 16 chunks of the window;
+//  * rows of 8 chunks (128 bytes) pair up in one window; s8(k) = (k >> 1) & 7
+//    makes the 16 (key, chunk) reads of 16 consecutive keys distinct.
+__device__ __forceinline__ int swz16(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+__device__ __forceinline__ int swz8(int k) { return (k >> 1) & 7; }
+
+template <int NCH>
+__device__ __forceinline__ int swz_of(int row) {
+  if constexpr (NCH % 16 == 0) return swz16(row);
+  else if constexpr (NCH % 8 == 0) return swz8(row);
+  else return 0;
+}
 
 template <int NCH>
 __device__ __forceinline__ int region_off(int row, int chunk) {
-  if constexpr (NCH % 8 == 0) return (row * NCH + (chunk ^ swz(row))) << 4;
-  else return (row * NCH + chunk) << 4;
+  return (row * NCH + (chunk ^ swz_of<NCH>(row))) << 4;
 }
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -201,12 +221,12 @@ __device__ __forceinline__ void stage_region(__amdgpu_buffer_rsrc_t rs, uint32_t
       // one row per instruction: the row (and its swizzle) is wave-uniform
       const int row = j;
       const int src_row = row < nrows ? row : nrows - 1;
-      voff = (uint32_t)(lane ^ swz(row)) * 16;
+      voff = (uint32_t)(lane ^ swz_of<NCH>(row)) * 16;
       soff = (uint32_t)src_row * ss;
     } else {
       const int slot = j * 64 + lane;
       const int row = slot / NCH, pc = slot - row * NCH;
-      const int c = (NCH % 8 == 0) ? (pc ^ swz(row)) : pc;
+      const int c = pc ^ swz_of<NCH>(row);
       const int src_row = row < nrows ? row : nrows - 1;
       voff = (uint32_t)src_row * ss + (uint32_t)c * 16;
       soff = 0;
@@ -229,7 +249,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int LAT_BYTES = kBN * RC * 16;
   constexpr int BUF_BYTES = LAT_BYTES + kBN * PC * 16;
   static_assert(R % 32 == 0 && D % KMF == 0 && (P * sizeof(T)) % 16 == 0, "shape");
-  static_assert(KW != 8 || (RC % 8 == 0 && (PC % 8 == 0 || P <= 32)), "bf16 score addressing");
 
   // Two distinct LDS objects (not one array indexed at run time) so the
   // compiler can tell the DMA into one buffer from the reads of the other and
@@ -314,26 +333,30 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 
   // Per-lane LDS byte offsets inside a tile buffer (bf16 only; the fp32 path
   // computes its addresses inline).
-  //  * score operand, step c: chunk 2c + hh of key r.  Writing 2c + hh as
-  //    8 * (c / 4) + (2 * (c % 4) + hh), the swizzle only touches the low part,
-  //    so the address is qk_*[c % 4] + 128 * (c / 4).
+  //  * score operand, step c: chunk 2c + hh of key r.  With a swizzle over LSW
+  //    chunks, 2c + hh = LSW * (c / QB) + (2 * (c % QB) + hh) for QB = LSW / 2
+  //    and the swizzle only touches the second part, so the address is
+  //    qk_lat[c % QB] + 16 * LSW * (c / QB).
   //  * value operand, transposing read: in each 16-lane group, lane 4e + q
   //    loads columns d0 + 4q .. d0 + 4q + 3 of key k_e and lane j then holds
   //    column d0 + j of keys k_0..k_3.  Operand row d = 32 * db + r; slots 0-3
   //    are keys c_row(8c + 0..3, hh), slots 4-7 keys c_row(8c + 4..7, hh).
   //    The 16-byte chunk is 4 * db + x with x < 4, and (4 db + x) ^ s =
-  //    4 (db ^ s2) + (x ^ s01) for s2 = s >> 2, s01 = s & 3, so the address is
-  //    pv_base[c][half][db % 2] + 64 * db.
-  int qk_lat[4], qk_pe[4];
-  int pv_base[(PV_STEPS > 0 ? PV_STEPS : 1)][2][2];
+  //    4 (db ^ s2) + (x ^ s01) for s2 = s >> 2, s01 = s & 3; db ^ s2 only
+  //    changes the low two bits of db, so the address is
+  //    pv_base[c][half][db % 4] + 64 * db.
+  constexpr int LSW = (RC % 16 == 0) ? 16 : 8;
+  constexpr int QB = LSW / 2;
+  int qk_lat[QB], qk_pe[4];
+  int pv_base[(PV_STEPS > 0 ? PV_STEPS : 1)][2][4];
   if constexpr (KW == 8) {
-    const int sr = swz(r);
+    static_assert(P / KMF <= 4 && RC % 8 == 0, "bf16 score addressing");
+    const int sr = swz_of<RC>(r);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qk_lat[j] = r * RC * 16 + (((2 * j + hh) ^ sr) << 4);
-      // rope region: chunk 2j + hh exists only while it is < PC
+    for (int j = 0; j < QB; ++j) qk_lat[j] = r * RC * 16 + (((2 * j + hh) ^ sr) << 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // rope region: chunk 2j + hh exists only while it is < PC
       qk_pe[j] = LAT_BYTES + region_off<PC>(r, (2 * j + hh) < PC ? (2 * j + hh) : 0);
-    }
     const int g = lane >> 4, sl = lane & 15;
     const int e = sl >> 2, qd = sl & 3;
     const int x = 2 * (g & 1) + (qd >> 1);
@@ -342,10 +365,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int k = c_row(c * 8 + 4 * half + e, hh);
-        const int sk = swz(k), s2 = sk >> 2, s01 = sk & 3;
+        const int sk = swz_of<RC>(k), s2 = sk >> 2, s01 = sk & 3;
         const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
-        pv_base[c][half][0] = base + 64 * s2;     // even db: db ^ s2 = db + s2
-        pv_base[c][half][1] = base - 64 * s2;     // odd db:  db ^ s2 = db - s2
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) pv_base[c][half][d4] = base + 64 * ((d4 ^ s2) - d4);
       }
   }
 
@@ -379,17 +402,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     // The K fragments are read QPF steps ahead of the MFMA chain.
     auto score_src = [&](int c) __attribute__((always_inline)) -> const char* {
       if constexpr (KW == 8) {
-        // bf16: step c reads 16-byte chunk 2c + hh of the row; with the
-        // swizzle that is lane base qk_lat[c % 4] plus 128 * (c / 4)
-        if (c < R / KMF) return buf + qk_lat[c & 3] + 128 * (c >> 2);
-        return buf + qk_pe[(c - R / KMF) & 3] + 128 * ((c - R / KMF) >> 2);
+        // bf16: step c reads 16-byte chunk 2c + hh of the row
+        if (c < R / KMF) return buf + qk_lat[c % QB] + 16 * LSW * (c / QB);
+        return buf + qk_pe[c - R / KMF];
       } else {
         const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
         if (c < R / KMF) return buf + region_off<RC>(r, byte >> 4) + (byte & 15);
         return buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
       }
     };
-    constexpr int QPF = NCHUNK < 4 ? NCHUNK : 4;
+    constexpr int QPF = NCHUNK < KDT_SCORE_PREFETCH ? NCHUNK : KDT_SCORE_PREFETCH;
     frag kf[QPF];
 #pragma unroll
     for (int c = 0; c < QPF; ++c) kf[c] = *reinterpret_cast<const frag*>(score_src(c));
@@ -457,8 +479,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       } else {
         // bf16: two transposing reads (lane bases computed before the loop)
         const int o = 64 * db;
-        const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 1] + o);
-        const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 1] + o);
+        const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 3] + o);
+        const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 3] + o);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
@@ -466,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
     for (int c = 0; c < PV_STEPS; ++c) pfr[c] = MM::pack(p + c * KW);
     constexpr int STEPS = PV_STEPS * NB;
-    constexpr int VPF = STEPS < 2 ? STEPS : 2;
+    constexpr int VPF = STEPS < KDT_VALUE_PREFETCH ? STEPS : KDT_VALUE_PREFETCH;
     frag vq[VPF + 1];
 #pragma unroll
     for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NB, i % NB);
