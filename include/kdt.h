@@ -146,9 +146,14 @@ typedef struct {
 
 /* Host-only planning: no device access.  The partial buffers live in the
  * workspace at the given byte offsets:
- *   part_o   float32 [B, max_splits, q_len*H, R]   normalised partial outputs
+ *   part_o   float32 [B, max_splits, NBLK, 32*R]   normalised partial outputs, tiled
  *   part_lse float32 [B, max_splits, q_len*H]      natural-log partial LSE (-inf: empty split)
- * Row index within a sequence is m = t*H + h.  Sequence b uses splits
+ * Row index within a sequence is m = t*H + h.  NBLK = ceil(q_len*H / 32): rows
+ * are grouped in blocks of 32, and inside block m / 32 element (m, c) sits at
+ *   256*(c/8) + 128*((c/4)%2) + 4*(m%32) + c%4
+ * which is the register order of a 32x32 matrix-core accumulator, so the split
+ * kernel writes whole cache lines.  Padding rows of the last block hold
+ * unspecified values.  Sequence b uses splits
  * 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1. */
 typedef struct {
   int32_t split_keys;          /* keys per split (multiple of 64) */
@@ -178,8 +183,9 @@ int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_byt
  * ceil((prefix_lens[b] + q_len) / split_keys) clamped to [1, max_splits].
  * Splits with part_lse = -inf carry no weight; a row with no finite split gets
  * out = 0 and lse = -inf.  out is written in `dtype` (bf16: round to nearest
- * even).  part_o / part_lse are contiguous with the layout given above; out has
- * strides out_sb, out_st, out_sh (elements) over [B, q_len, H, R].
+ * even).  part_o / part_lse are contiguous with the layout given above (tiled
+ * part_o); out has strides out_sb, out_st, out_sh (elements) over
+ * [B, q_len, H, R].  R must be a multiple of 8.
  * prefix_lens may be NULL when split_keys == 0.
  * ---------------------------------------------------------------------- */
 int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32_t R,

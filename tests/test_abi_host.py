@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from tree_verify_mla_kdt_amd import kdt
@@ -61,10 +62,11 @@ def test_plan_sizes_and_layout():
     assert rc == 0
     M = 65 * 16
     assert p.rows == M
-    assert p.split_keys % 64 == 0 and p.split_keys >= 256
+    assert p.split_keys % 64 == 0 and p.split_keys >= 64
     assert p.max_splits == -(-(4096 + 65) // p.split_keys)
     assert p.direct == (1 if p.max_splits == 1 else 0)
-    assert p.part_lse_offset >= 1 * p.max_splits * M * 512 * 4 and p.part_lse_offset % 256 == 0
+    nblk = -(-M // 32)
+    assert p.part_lse_offset >= 1 * p.max_splits * nblk * 32 * 512 * 4 and p.part_lse_offset % 256 == 0
     assert p.workspace_bytes == p.part_lse_offset + p.max_splits * M * 4
     rc, p = _plan(_desc(split_keys=128))
     assert rc == 0 and p.split_keys == 128 and p.max_splits == 33
@@ -122,4 +124,28 @@ def test_visibility_and_gather_argument_checks():
     m = L.kdt_merge_partials
     assert m(1, 1, 9, 4, 512, None, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 1
     assert m(1, 1, 9, 4, 512, FAKE, FAKE, 2, None, 64, FAKE, 0, 0, 0, FAKE, None) == 1           # needs prefix_lens
-    assert m(1, 1, 9, 4, 2048, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2
+    assert m(1, 1, 9, 4, 36, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2             # R % 8
+
+
+def test_auto_split_counts_follow_the_launch_model():
+    # batch 64 x 3 row tiles already fill the chip: one split, no merge
+    rc, p = _plan(_desc(B=64, q_len=17, max_prefix_len=2048, capacity=2048 + 17))
+    assert rc == 0 and p.max_splits == 1 and p.direct == 1
+    # batch 4 x 33 row tiles of a 32K prefix: several splits (more than two,
+    # so the grid does not end with a nearly empty second round)
+    rc, p = _plan(_desc(B=4, H=64, max_prefix_len=32768, capacity=32768 + 65))
+    assert rc == 0 and p.max_splits > 2
+
+
+def test_partial_tiling_round_trip():
+    import torch
+    rng = np.random.default_rng(3)
+    for M, R in ((1040, 512), (21, 64), (32, 64)):
+        x = torch.from_numpy(rng.standard_normal((2, 3, M, R)).astype(np.float32))
+        t = kdt.tile_partials(x)
+        assert t.shape == (2, 3, kdt.partial_blocks(M), 32 * R)
+        assert torch.equal(kdt.untile_partials(t, M), x)
+        # spot-check the documented position of (m, c)
+        m, c = M - 1, R - 3
+        flat = t[1, 2, m // 32]
+        assert flat[256 * (c // 8) + 128 * ((c // 4) % 2) + 4 * (m % 32) + c % 4] == x[1, 2, m, c]

@@ -22,7 +22,9 @@ def test_merge_matches_oracle_with_empty_splits(out_dtype):
     pl[rng.random((B, S, M)) < 0.3] = -np.inf
     pl[0, :, 3] = -np.inf                      # a row with no finite split
     po[pl == -np.inf] = np.nan                 # never read
-    out, lse = kdt.merge_partials(torch.from_numpy(po).to(dev()), torch.from_numpy(pl).to(dev()), q, H, out_dtype)
+    po_tiled = kdt.tile_partials(torch.from_numpy(po).to(dev()))
+    assert np.array_equal(kdt.untile_partials(po_tiled, M).cpu().numpy(), po, equal_nan=True)
+    out, lse = kdt.merge_partials(po_tiled, torch.from_numpy(pl).to(dev()), q, H, out_dtype)
     torch.cuda.synchronize()
     ro, rl = oracle.merge_partials(np.moveaxis(np.nan_to_num(po, nan=0.0), 1, 0).astype(np.float64),
                                    np.moveaxis(pl, 1, 0).astype(np.float64))
@@ -49,7 +51,7 @@ def test_partials_merge_to_full_result():
     vis_np, _ = oracle.build_visibility(inp.parents)
     cache = inp.f64("cache")
     ql, qp = inp.f64("q_lat"), inp.f64("q_pe")
-    po = part_o.cpu().numpy()
+    po = kdt.untile_partials(part_o, cfg.q_len * cfg.H).cpu().numpy()
     pl = part_lse.cpu().numpy()
     for b in range(cfg.B):
         L = int(inp.prefix_lens[b])

@@ -119,7 +119,7 @@ struct VerifyArgs {
   float* part_lse;
   int32_t* seq_status;
   float scale_log2;
-  int B, q, H, M, W, n_rt, max_splits, split_keys, max_prefix_len;
+  int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len;
 };
 
 // The value of C-layout register v of a 32x32 MFMA result held by a lane in
@@ -274,6 +274,28 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int t = row_ok ? m / a.H : 0;
   const int h = row_ok ? m - t * a.H : 0;
 
+  // The query fragments and visibility words are requested before the prefix
+  // length arrives, so the two memory latencies overlap.  Padding rows
+  // (m >= M) load token 0 / head 0: an output column of either contraction
+  // depends only on its own query column, and padding rows are never written,
+  // so no masking is needed.
+  frag qf[NCHUNK];
+  {
+    const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
+    const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+      if (c < R / KMF) qf[c] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
+      else qf[c] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
+    }
+  }
+  uint64_t vw0 = ~0ull, vw1 = ~0ull;
+  if (row_ok) {
+    const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
+    vw0 = vr[0];
+    vw1 = a.W > 1 ? vr[1] : 0ull;
+  }
+
   const int L = a.prefix_lens[b];
   const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
   const int N = L + a.q;
@@ -296,26 +318,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if (k_begin >= N) return;                   // this split does not exist for sequence b
   const int k_end = min(N, k_begin + a.split_keys);
   const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
-
-  // Padding rows (m >= M) load token 0 / head 0: an output column of either
-  // contraction depends only on its own query column, and padding rows are
-  // never written, so no masking is needed.
-  frag qf[NCHUNK];
-  {
-    const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
-    const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
-#pragma unroll
-    for (int c = 0; c < NCHUNK; ++c) {
-      if (c < R / KMF) qf[c] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
-      else qf[c] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
-    }
-  }
-  uint64_t vw0 = ~0ull, vw1 = ~0ull;
-  if (row_ok) {
-    const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
-    vw0 = vr[0];
-    vw1 = a.W > 1 ? vr[1] : 0ull;
-  }
 
   const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
   const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
@@ -555,8 +557,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       }
     if (hh == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
   } else {
-    const int64_t prow = ((int64_t)b * a.max_splits + split) * a.M + m;
-    float* o = a.part_o + prow * R;
+    // Partials stay in accumulator order: the wave's 32 rows form one block
+    // of 32 x R floats in which register group (db, g) of every lane is one
+    // contiguous 1 KB run, so each store instruction writes whole lines.
+    const int blk = rt * (kBM / 32) + wave;
+    float* o = a.part_o + (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R) + 4 * lane;
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -564,28 +569,37 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         float v4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
-        store4<float>(o + db * 32 + 8 * g + 4 * hh, v4);
+        store4<float>(o + 256 * (4 * db + g), v4);
       }
-    if (hh == 0) a.part_lse[prow] = lse_v;
+    if (hh == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Cross-split merge: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
-// One group of R/4 threads per row, each thread four consecutive columns;
-// splits with lse_k = -inf are skipped (their o_k is never read).
+// Partials are in accumulator order (32-row blocks; column c of block row r at
+// 256 (c / 8) + 128 ((c / 4) % 2) + 4 r + c % 4), so one wave handles one
+// (sequence, block, 8-column group): every lane reads one float4 per split and
+// the wave's reads are one contiguous 1 KB run.  Splits are consumed eight at a
+// time with a running maximum, so eight loads per lane are in flight.  Splits
+// with lse_k = -inf are skipped by selection, never by multiplication: their
+// partial output may never have been written.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
-    int B, int q, int H, int R, const int32_t* __restrict__ prefix_lens, int split_keys,
+    int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys,
     T* __restrict__ out, int64_t out_sb, int64_t out_st, int64_t out_sh, float* __restrict__ lse) {
-  const int tpr = R >> 2;
-  const int rows_per_wg = blockDim.x / tpr;
+  constexpr int U = 8;
+  const int n_c8 = R >> 3;
+  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hh = lane >> 5;
+  if (wid >= (int64_t)B * n_blk * n_c8) return;
+  const int c8 = (int)(wid % n_c8);
+  const int64_t bblk = wid / n_c8;
+  const int blk = (int)(bblk % n_blk), b = (int)(bblk / n_blk);
   const int M = q * H;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + threadIdx.x / tpr;
-  const int cidx = threadIdx.x % tpr;
-  if (threadIdx.x >= rows_per_wg * tpr || row >= (int64_t)B * M) return;
-  const int b = (int)(row / M), m = (int)(row - (int64_t)b * M);
+  const int m = blk * 32 + (lane & 31);
+  if (m >= M) return;
   int ns = max_splits;
   if (split_keys > 0) {
     const int64_t n = (int64_t)prefix_lens[b] + q;
@@ -593,31 +607,41 @@ __global__ __launch_bounds__(256) void merge_kernel(
     ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
   }
   const float* pl = part_lse + (int64_t)b * max_splits * M + m;
-  float mx = -INFINITY;
-  for (int k = 0; k < ns; ++k) mx = fmaxf(mx, pl[(int64_t)k * M]);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float z = 0.0f;
-  if (mx != -INFINITY) {
-    for (int k = 0; k < ns; ++k) {
-      const float lk = pl[(int64_t)k * M];
-      if (lk == -INFINITY) continue;
-      const float w = __expf(lk - mx);
+  const int64_t split_stride = (int64_t)n_blk * 32 * R;
+  const float* po = part_o + ((int64_t)b * max_splits * n_blk + blk) * (32 * R) + 256 * c8 + 4 * lane;
+  float mx = -INFINITY, z = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < ns; k0 += U) {
+    float lk[U];
+    f32x4 ok[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int k = k0 + j;
+      lk[j] = k < ns ? pl[(int64_t)k * M] : -INFINITY;
+      ok[j] = k < ns ? *reinterpret_cast<const f32x4*>(po + k * split_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float cm = lk[0];
+#pragma unroll
+    for (int j = 1; j < U; ++j) cm = fmaxf(cm, lk[j]);
+    if (cm > mx) {
+      const float sc = __expf(mx - cm);   // 0 while mx is still -inf
+      z *= sc;
+      acc *= sc;
+      mx = cm;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const bool live = lk[j] != -INFINITY;
+      const float w = live ? __expf(lk[j] - mx) : 0.0f;
       z += w;
-      const f32x4 o = *reinterpret_cast<const f32x4*>(
-          part_o + (((int64_t)b * max_splits + k) * M + m) * R + 4 * cidx);
-      acc[0] += w * o[0];
-      acc[1] += w * o[1];
-      acc[2] += w * o[2];
-      acc[3] += w * o[3];
+      acc = live ? acc + w * ok[j] : acc;
     }
   }
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-  float v4[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v4[e] = acc[e] * inv;
-  const int t = m / H, h = m - (m / H) * H;
-  store4<T>(out + b * out_sb + t * out_st + h * out_sh + 4 * cidx, v4);
-  if (cidx == 0) lse[row] = z > 0.0f ? mx + logf(z) : -INFINITY;
+  const float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  const int t = m / H, h = m - t * H;
+  store4<T>(out + b * out_sb + t * out_st + h * out_sh + 8 * c8 + 4 * hh, v4);
+  if (c8 == 0 && hh == 0) lse[(int64_t)b * M + m] = z > 0.0f ? mx + logf(z) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -655,6 +679,36 @@ static int validate(const kdt_verify_desc* d) {
   return KDT_OK;
 }
 
+// Split size chosen by a small time model of one launch.  Workgroups run one
+// per compute unit, so a grid of G workgroups takes ceil(G / kCU) rounds; a
+// round costs its key tiles plus a fixed start-up (query load, first-tile
+// latency); every partial then costs its write and its read in the merge at
+// the HBM rate, and splitting at all adds the merge launch.  Constants are in
+// microseconds for one 128-row x 32-key tile at R = 512, P = 64 and scale with
+// the contraction depth 2R + P; they need only be right in ratio.
+static int64_t auto_split_keys(int64_t base, int64_t n_max, int R, int P) {
+  const double t_tile = 1.3 * (2.0 * R + P) / 1088.0;
+  const double t_start = 4.0;
+  const double t_part = (double)kBM * R * 4 * 2 / 5.0e6;
+  const double t_merge = 5.0;
+  const int64_t n_tiles = (n_max + kBN - 1) / kBN;
+  int64_t best_sk = (n_max + 63) / 64 * 64;
+  double best = 1e300;
+  for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
+    int64_t sk = (n_max + s - 1) / s;
+    sk = (sk + 63) / 64 * 64;
+    const int64_t ns = (n_max + sk - 1) / sk;
+    if (ns != s) continue;                    // covered by a smaller s
+    const int64_t rounds = (ns * base + kCU - 1) / kCU;
+    const double cost = rounds * ((sk / kBN) * t_tile + t_start) + (ns > 1 ? ns * base * t_part + t_merge : 0.0);
+    if (cost < best * 0.999) {                // ties go to fewer splits
+      best = cost;
+      best_sk = sk;
+    }
+  }
+  return best_sk;
+}
+
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int rc = validate(d);
   if (rc != KDT_OK) return rc;
@@ -662,16 +716,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int n_rt = (M + kBM - 1) / kBM;
   const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
   int64_t sk = d->split_keys;
-  if (sk == 0) {
-    // Aim for about one workgroup per compute unit, but never let a split
-    // shrink below 256 keys (the partial it writes must stay small next to
-    // the work it does).
-    const int64_t base = (int64_t)d->B * n_rt;
-    const int64_t want = (kCU + base - 1) / base;
-    sk = (n_max + want - 1) / want;
-    sk = (sk + 63) / 64 * 64;
-    if (sk < 256) sk = 256;
-  }
+  if (sk == 0) sk = auto_split_keys((int64_t)d->B * n_rt, n_max, d->R, d->P);
   const int64_t ns = (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
@@ -679,7 +724,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   p->rows = M;
   p->direct = ns == 1 ? 1 : 0;
   const int64_t n_part_rows = (int64_t)d->B * ns * M;
-  const int64_t o_bytes = n_part_rows * d->R * 4;
+  const int64_t o_bytes = (int64_t)d->B * ns * ((M + 31) / 32) * 32 * d->R * 4;
   p->part_o_offset = 0;
   p->part_lse_offset = (o_bytes + 255) / 256 * 256;
   p->workspace_bytes = (size_t)(p->part_lse_offset + n_part_rows * 4);
@@ -703,6 +748,7 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.scale_log2 = d->softmax_scale * kLog2e;
   a.B = d->B; a.q = d->q_len; a.H = d->H; a.M = d->q_len * d->H; a.W = (d->q_len + 63) / 64;
   a.n_rt = (a.M + kBM - 1) / kBM;
+  a.n_blk = (a.M + 31) / 32;
   a.max_splits = p.max_splits;
   a.split_keys = p.split_keys;
   a.max_prefix_len = d->max_prefix_len;
@@ -730,19 +776,16 @@ static int dispatch_split(int dtype, int R, int P, const VerifyArgs& a, bool dir
 static int launch_merge(int dtype, int B, int q, int H, int R, const float* po, const float* pl,
                         int max_splits, const int32_t* prefix_lens, int split_keys, void* out,
                         int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
-  const int tpr = R / 4;
-  const int rows_per_wg = 256 / tpr;
-  const int64_t rows = (int64_t)B * q * H;
-  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+  const int n_blk = (q * H + 31) / 32;
+  const int64_t waves = (int64_t)B * n_blk * (R / 8);
+  const int64_t grid = (waves + 3) / 4;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
   if (dtype == KDT_BF16)
-    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3((unsigned)grid), dim3(rows_per_wg * tpr), 0, s, po, pl,
-                       max_splits, B, q, H, R, prefix_lens, split_keys, static_cast<__bf16*>(out), osb,
-                       ost, osh, lse);
+    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, H,
+                       R, n_blk, prefix_lens, split_keys, static_cast<__bf16*>(out), osb, ost, osh, lse);
   else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)grid), dim3(rows_per_wg * tpr), 0, s, po, pl,
-                       max_splits, B, q, H, R, prefix_lens, split_keys, static_cast<float*>(out), osb,
-                       ost, osh, lse);
+    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, H,
+                       R, n_blk, prefix_lens, split_keys, static_cast<float*>(out), osb, ost, osh, lse);
   return launch_status();
 }
 
@@ -787,7 +830,7 @@ extern "C" int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32
     return KDT_ERR_INVALID_ARG;
   if (split_keys > 0 && !prefix_lens) return KDT_ERR_INVALID_ARG;
   if (dtype != KDT_F32 && dtype != KDT_BF16) return KDT_ERR_UNSUPPORTED;
-  if (R % 4 || R / 4 > 256) return KDT_ERR_UNSUPPORTED;
+  if (R % 8) return KDT_ERR_UNSUPPORTED;
   const int64_t vec = dtype == KDT_F32 ? 4 : 8;    // output elements per 16 bytes
   if (!kdt::aligned16(part_o) || !kdt::aligned16(out) || (R % vec) || out_sb % vec || out_st % vec ||
       out_sh % vec || out_sb < 0 || out_st < 0 || out_sh < 0)

@@ -190,32 +190,64 @@ def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_pr
     return out, lse
 
 
+def partial_blocks(rows: int) -> int:
+    """Number of 32-row blocks of the partial layout for q_len*H = rows."""
+    return (rows + 31) // 32
+
+
+def untile_partials(part_o, rows: int):
+    """Row-major view of tiled partials: [B, S, NBLK, 32*R] -> [B, S, rows, R].
+
+    In the tiled layout, column c of row r of a 32-row block sits at
+    256*(c//8) + 128*((c//4)%2) + 4*r + c%4 (the order of a 32x32 matrix-core
+    accumulator)."""
+    B, S, nblk, w = part_o.shape
+    R = w // 32
+    t = part_o.reshape(B, S, nblk, R // 8, 2, 32, 4).permute(0, 1, 2, 5, 3, 4, 6)
+    return t.reshape(B, S, nblk * 32, R)[:, :, :rows]
+
+
+def tile_partials(rows_major):
+    """Inverse of untile_partials: [B, S, rows, R] -> contiguous [B, S, NBLK, 32*R]
+    (padding rows zero)."""
+    B, S, M, R = rows_major.shape
+    nblk = partial_blocks(M)
+    pad = rows_major.new_zeros((B, S, nblk * 32, R))
+    pad[:, :, :M] = rows_major
+    t = pad.reshape(B, S, nblk, 32, R // 8, 2, 4).permute(0, 1, 2, 4, 5, 3, 6)
+    return t.contiguous().reshape(B, S, nblk, 32 * R)
+
+
 def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None,
                     workspace=None, seq_status=None, split_keys=0, stream=None):
-    """Split stage only.  Returns (part_o [B, S, M, R], part_lse [B, S, M], plan)."""
+    """Split stage only.  Returns (part_o, part_lse, plan): part_o float32
+    [B, S, NBLK, 32*R] in the tiled layout (see untile_partials), part_lse
+    float32 [B, S, q*H]."""
     d, _, _ = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
                               None, None, seq_status, split_keys)
     p = verify_plan(d)
-    need = max(int(p.workspace_bytes), 1)
+    B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
+    need = max(int(p.workspace_bytes), p.part_lse_offset + B * S * M * 4, 1)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
-        B, M, R, S = q_lat.shape[0], p.rows, q_lat.shape[3], p.max_splits
-        rows = B * S * M
-        need = max(need, p.part_lse_offset + rows * 4)
         workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("kdt_verify_partials", lib().kdt_verify_partials(ctypes.byref(d), _ptr(workspace), ws_bytes,
                                                            _stream(stream)))
-    B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
-    part_o = workspace[p.part_o_offset:p.part_o_offset + B * S * M * R * 4].view(torch.float32).view(B, S, M, R)
+    nblk = partial_blocks(M)
+    n_o = B * S * nblk * 32 * R
+    part_o = workspace[p.part_o_offset:p.part_o_offset + n_o * 4].view(torch.float32).view(B, S, nblk, 32 * R)
     part_lse = workspace[p.part_lse_offset:p.part_lse_offset + B * S * M * 4].view(torch.float32).view(B, S, M)
     return part_o, part_lse, p
 
 
 def merge_partials(part_o, part_lse, q_len, H, out_dtype, prefix_lens=None, split_keys=0, out=None, lse=None,
                    stream=None):
-    """part_o float32 [B, S, q*H, R], part_lse float32 [B, S, q*H] -> (out [B, q, H, R], lse [B, q, H])."""
-    B, S, M, R = part_o.shape
-    assert M == q_len * H and part_o.is_contiguous() and part_lse.is_contiguous()
+    """part_o float32 [B, S, NBLK, 32*R] (tiled), part_lse float32 [B, S, q*H]
+    -> (out [B, q, H, R], lse [B, q, H])."""
+    B, S, nblk, w = part_o.shape
+    R = w // 32
+    assert nblk == partial_blocks(q_len * H) and part_lse.shape == (B, S, q_len * H)
+    assert part_o.is_contiguous() and part_lse.is_contiguous()
     if out is None:
         out = torch.empty((B, q_len, H, R), dtype=out_dtype, device=part_o.device)
     if lse is None:
