@@ -32,9 +32,9 @@
 //   a read-modify-write of all 256 accumulation registers every tile).  A row
 //   whose max outgrows its reference by more than that makes its wave redo the
 //   split once against the exact max, which it has tracked meanwhile.
-// * K/V tiles are double-buffered and copied straight from HBM into LDS with
-//   buffer_load_dwordx4 ... lds, so staging costs no registers and overlaps the
-//   previous tile's MFMA work.  The value operand is read with the gfx950
+// * K/V tiles rotate through three LDS buffers and are copied straight from
+//   HBM into LDS with buffer_load_dwordx4 ... lds, so staging costs no
+//   registers and two tile copies are in flight while one tile is computed.  The value operand is read with the gfx950
 //   transposing LDS load (ds_read_b64_tr_b16) from the same key-major tile the
 //   score operand uses.
 // * Masking costs nothing on prefix tiles; only tiles that reach the tree
@@ -190,12 +190,55 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer: stride 0, num_records in bytes
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, num_records in bytes), wave-uniform.
+// Loads at or past num_records return zero instead of faulting.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// buffer_load_dwordx4 ... lds: the 16 bytes of lane i land at LDS byte
+// address m0 + 16 i.  Issued as inline asm on purpose: the compiler does not
+// track these LDS writes, so it neither delays later reads of the other tile
+// buffers for them nor drains them at barriers; the kernel orders them itself
+// (s_waitcnt vmcnt, then a workgroup barrier, before a tile buffer is read).
+// Nothing else in the kernel uses m0.
+__device__ __forceinline__ void dma16_to_lds(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+      : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (N < 16): this wave's older tile copies have
+// landed in LDS and its own LDS reads have returned.
+template <int N>
+__device__ __forceinline__ void wait_vmem_lds() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load, including tile copies meant to stay in
+// flight).  The memory clobber keeps the compiler from moving any access
+// across it; the wait above provides the ordering the tile ring needs.
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Loads one wave issues for a region of SLOTS 16-byte chunks when wave-loads
+// are dealt round-robin to the four waves: the minimum over the waves.
+constexpr int min_wave_loads(int slots) { return (slots / 64) / (kThreads / 64); }
 
 // Start the copy of one region of a key tile straight into LDS: every
 // buffer_load_dwordx4 ... lds writes 64 consecutive 16-byte LDS slots, one per
@@ -206,8 +249,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // of 64 chunks per row, the source row are then scalar and each load needs a
 // single per-lane offset register.
 template <int ROWS, int NCH>
-__device__ __forceinline__ void stage_region(__amdgpu_buffer_rsrc_t rs, uint32_t ss, int nrows,
-                                             char* lds, int wave, int lane) {
+__device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, char* lds, int wave, int lane) {
   constexpr int SLOTS = ROWS * NCH;
   static_assert(SLOTS % 64 == 0, "tile region must be whole wave loads");
   constexpr int WAVES = kThreads / 64;
@@ -231,7 +273,8 @@ __device__ __forceinline__ void stage_region(__amdgpu_buffer_rsrc_t rs, uint32_t
       voff = (uint32_t)src_row * ss + (uint32_t)c * 16;
       soff = 0;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + j * 1024), 16, voff, soff, 0, 0);
+    dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds_addr(lds + j * 1024)), voff,
+                 __builtin_amdgcn_readfirstlane(soff));
   }
 }
 
@@ -250,11 +293,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int BUF_BYTES = LAT_BYTES + kBN * PC * 16;
   static_assert(R % 32 == 0 && D % KMF == 0 && (P * sizeof(T)) % 16 == 0, "shape");
 
-  // Two distinct LDS objects (not one array indexed at run time) so the
-  // compiler can tell the DMA into one buffer from the reads of the other and
-  // does not wait for the prefetch before computing.
+  // Three distinct LDS objects (not one array indexed at run time) so the
+  // compiler can tell the DMA into one buffer from the reads of another and
+  // does not wait for the prefetches before computing.
   __shared__ __attribute__((aligned(1024))) char s_buf0[BUF_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_buf1[BUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_buf2[BUF_BYTES];
+  // vmcnt that leaves exactly one (the newest) tile copy in flight on every
+  // wave (a wave that issued more waits a little longer, which is safe).
+  constexpr int STAGE_LOADS = min_wave_loads(kBN * RC) + min_wave_loads(kBN * PC);
   __shared__ int s_dead;
   // One accumulator block per lane parks here while the score tile is alive
   // (all 512 registers are otherwise taken: 256 accumulators, Q, scores).
@@ -345,12 +392,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   //    are keys c_row(8c + 0..3, hh), slots 4-7 keys c_row(8c + 4..7, hh).
   //    The 16-byte chunk is 4 * db + x with x < 4, and (4 db + x) ^ s =
   //    4 (db ^ s2) + (x ^ s01) for s2 = s >> 2, s01 = s & 3; db ^ s2 only
-  //    changes the low two bits of db, so the address is
-  //    pv_base[c][half][db % 4] + 64 * db.
+  //    changes the low two bits of db.  The keys are 16c + (8 half + 4 hh +
+  //    e) and the swizzle depends on the key modulo 16 only, so c moves the
+  //    address by whole 16-key blocks: pv_base[half][db % 4] + 64 * db +
+  //    c * (16 rows of the region).
   constexpr int LSW = (RC % 16 == 0) ? 16 : 8;
   constexpr int QB = LSW / 2;
   int qk_lat[QB], qk_pe[4];
-  int pv_base[(PV_STEPS > 0 ? PV_STEPS : 1)][2][4];
+  int pv_base[2][4];
   if constexpr (KW == 8) {
     static_assert(P / KMF <= 4 && RC % 8 == 0, "bf16 score addressing");
     const int sr = swz_of<RC>(r);
@@ -363,15 +412,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     const int e = sl >> 2, qd = sl & 3;
     const int x = 2 * (g & 1) + (qd >> 1);
 #pragma unroll
-    for (int c = 0; c < PV_STEPS; ++c)
+    for (int half = 0; half < 2; ++half) {
+      const int k = c_row(4 * half + e, hh);
+      const int sk = swz_of<RC>(k), s2 = sk >> 2, s01 = sk & 3;
+      const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int k = c_row(c * 8 + 4 * half + e, hh);
-        const int sk = swz_of<RC>(k), s2 = sk >> 2, s01 = sk & 3;
-        const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) pv_base[c][half][d4] = base + 64 * ((d4 ^ s2) - d4);
-      }
+      for (int d4 = 0; d4 < 4; ++d4) pv_base[half][d4] = base + 64 * ((d4 ^ s2) - d4);
+    }
   }
 
   f32x16 acc[NB];
@@ -447,7 +494,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
     mx = xhalf_max(mx);
     m_max = fmaxf(m_max, mx);
-    if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
+    // Only tiles where some row of the wave still lacks its reference take
+    // this (uniform) branch; elsewhere the weights below depend on the fixed
+    // reference alone and need not wait for the row max, which then only
+    // feeds the check that follows.
+    if (__any(m_ref == -INFINITY)) {
+      if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
+    }
     if (!dead && __any(m_max > m_ref + kRefSlack)) {
       dead = true;
       s_dead = 1;
@@ -480,9 +533,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
       } else {
         // bf16: two transposing reads (lane bases computed before the loop)
-        const int o = 64 * db;
-        const bf16x4 lo = lds_read_tr16(buf + pv_base[c][0][db & 3] + o);
-        const bf16x4 hi = lds_read_tr16(buf + pv_base[c][1][db & 3] + o);
+        const int o = 64 * db + c * 16 * RC * 16;
+        const bf16x4 lo = lds_read_tr16(buf + pv_base[0][db & 3] + o);
+        const bf16x4 hi = lds_read_tr16(buf + pv_base[1][db & 3] + o);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
@@ -520,21 +573,34 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     }
     const bool compute = (pass == 0) || dead;
     dead = false;
+    // Tiles rotate through the three buffers with two copies in flight: each
+    // step waits for its own tile (the copy of the following tile may still
+    // run), then starts the copy of the tile two ahead into the buffer the
+    // previous step has finished reading, and computes.
+    auto wait_tile = [&](bool newer_in_flight) __attribute__((always_inline)) {
+      if (newer_in_flight) wait_vmem_lds<STAGE_LOADS>();
+      else wait_vmem_lds<0>();
+      tile_barrier();
+    };
+    // The first tile, the query fragments and the visibility words are all
+    // waited for here, visibly to the compiler, so that it places no wait for
+    // them inside the loop (where it would also drain the tile copies).
     stage(0, s_buf0);
-    // Tiles alternate between the two buffers; each step waits for its own
-    // tile, then starts the DMA of the next tile into the other buffer and
-    // computes while that copy is in flight.
+    wait_vmem_lds<0>();
+    if (n_tiles > 1) stage(1, s_buf1);
 #pragma unroll 1
-    for (int tile = 0; tile < n_tiles; tile += 2) {
-      wait_vmem();
-      __syncthreads();
-      if (tile + 1 < n_tiles) stage(tile + 1, s_buf1);
+    for (int tile = 0; tile < n_tiles; tile += 3) {
+      wait_tile(tile + 1 < n_tiles);
+      if (tile + 2 < n_tiles) stage(tile + 2, s_buf2);
       if (compute) tile_body(tile, s_buf0);
       if (tile + 1 >= n_tiles) break;
-      wait_vmem();
-      __syncthreads();
-      if (tile + 2 < n_tiles) stage(tile + 2, s_buf0);
+      wait_tile(tile + 2 < n_tiles);
+      if (tile + 3 < n_tiles) stage(tile + 3, s_buf0);
       if (compute) tile_body(tile + 1, s_buf1);
+      if (tile + 2 >= n_tiles) break;
+      wait_tile(tile + 3 < n_tiles);
+      if (tile + 4 < n_tiles) stage(tile + 4, s_buf1);
+      if (compute) tile_body(tile + 2, s_buf2);
     }
   }
 
