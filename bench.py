@@ -48,7 +48,60 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="run a plain device copy of MB megabytes --steps times (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step directly instead of replaying HIP graphs (for counter runs)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB", "CAL_WRITE_DB"),
+                    help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases of a --kernel-only "
+                         "--eager run and of a --copy-calibration run into "
+                         "profiles/traffic_verify_split_<workload>.json")
+    ap.add_argument("--calibration-mb", type=int, default=256,
+                    help="size of the --copy-calibration run that --write-traffic reads")
     return ap.parse_args()
+
+
+def pmc_kib_per_dispatch(db: str, counter: str, kernel_substr: str) -> float:
+    """Mean of a rocprofv3 --pmc counter (summed over instances) per dispatch
+    of the kernels whose name contains kernel_substr."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    names = {r[0]: r[1] for r in con.execute("select dispatch_id, name from kernels")}
+    per = {}
+    for cn, did, v in con.execute("select counter_name, dispatch_id, counter_value from pmc_events"):
+        if cn == counter and kernel_substr in names.get(did, ""):
+            per[did] = per.get(did, 0.0) + float(v)
+    if not per:
+        raise SystemExit(f"{db}: no {counter} values for kernels matching {kernel_substr!r}")
+    return sum(per.values()) / len(per)
+
+
+def write_traffic(args):
+    """HBM bytes per launch of the split kernel from counter databases.
+    FETCH_SIZE and WRITE_SIZE are in KiB; each is scaled by the ratio between
+    the bytes a plain device copy of known size moves and what the same
+    counter reports for it."""
+    fetch_db, write_db, cal_fetch_db, cal_write_db = args.write_traffic
+    n = args.calibration_mb << 20
+    kernel = "verify_split_kernel"
+    copy_kernel = "copyBuffer"
+    cal_f = n / (pmc_kib_per_dispatch(cal_fetch_db, "FETCH_SIZE", copy_kernel) * 1024.0)
+    cal_w = n / (pmc_kib_per_dispatch(cal_write_db, "WRITE_SIZE", copy_kernel) * 1024.0)
+    fetch = pmc_kib_per_dispatch(fetch_db, "FETCH_SIZE", kernel) * 1024.0 * cal_f
+    write = pmc_kib_per_dispatch(write_db, "WRITE_SIZE", kernel) * 1024.0 * cal_w
+    rec = {"workload": args.workload, "kernel": kernel, "source_hash": source_hash(),
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "bytes_per_launch": fetch + write,
+           "fetch_calibration": cal_f, "write_calibration": cal_w, "calibration_copy_bytes": n,
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --workload {args.workload} --kernel-only --eager --no-cpu --steps 5 --warmup 1",
+               f"rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --workload {args.workload} --kernel-only --eager --no-cpu --steps 5 --warmup 1",
+               f"rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --copy-calibration {args.calibration_mb} --steps 5",
+               f"rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --copy-calibration {args.calibration_mb} --steps 5",
+               f"python3 bench.py --workload {args.workload} --write-traffic FETCH.db WRITE.db CAL_FETCH.db CAL_WRITE.db"]}
+    out = os.path.join(ROOT, "profiles", f"traffic_verify_split_{args.workload.replace(':', '_')}.json")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def source_hash() -> str:
@@ -73,6 +126,9 @@ def visible_pairs(parents: np.ndarray, prefix_lens: np.ndarray, H: int) -> int:
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -160,6 +216,14 @@ def main():
 
     kdt.build_visibility(parents, vis=vis, depth=depth)
     fn = split_only if args.kernel_only else step
+    if args.eager:
+        # counter runs: plain launches, no graphs, no timing report
+        for i in range(args.warmup + args.steps):
+            fn(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_steps": args.steps, "warmup": args.warmup, "workload": args.workload,
+                          "kernel_only": bool(args.kernel_only)}), flush=True)
+        return
     g_all = capture(fn, range(n_copies))
     g_one = [capture(fn, [i]) for i in range(max(args.steps % n_copies, args.warmup % n_copies, 1))]
 
@@ -264,7 +328,7 @@ def cpu_baseline(inp, budget_s: float):
         oracle.gather_accepted(inp.cache, inp.prefix_lens, inp.accepted, inp.n_accepted)
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s:
             break
     per = el / n
     return {"value": cfg.B * cfg.q_len / per, "unit": "tree-tokens/s", "cores": threads, "kind": "oracle",
