@@ -321,8 +321,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int t = row_ok ? m / a.H : 0;
   const int h = row_ok ? m - t * a.H : 0;
 
-  // The query fragments and visibility words are requested before the prefix
-  // length arrives, so the two memory latencies overlap.  Padding rows
+  // The prefix length is requested first; the query fragments, the
+  // visibility words and (below) the first two key tiles are requested while
+  // it is in flight, so their memory latencies overlap.
+  const int L = a.prefix_lens[b];
+  // The query fragments and visibility words do not depend on it.  Padding rows
   // (m >= M) load token 0 / head 0: an output column of either contraction
   // depends only on its own query column, and padding rows are never written,
   // so no masking is needed.
@@ -343,11 +346,34 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     vw1 = a.W > 1 ? vr[1] : 0ull;
   }
 
-  const int L = a.prefix_lens[b];
+  const int k_begin = split * a.split_keys;
+  const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
+  const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
+  const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
+  const uint32_t pe_ss = (uint32_t)(a.k_pe_ss * (int64_t)sizeof(T));
+  // Copy of key tile `tile` (first key k_begin + tile * kBN) with its first
+  // `nrows` rows real; later rows repeat row nrows - 1.
+  auto stage_rows = [&](int tile, char* buf, int nrows) {
+    const int kt = k_begin + tile * kBN;
+    stage_region<kBN, RC>(make_rsrc(kv_lat + (int64_t)kt * lat_ss, (uint32_t)nrows * lat_ss), lat_ss,
+                          nrows, buf, wave, lane);
+    stage_region<kBN, PC>(make_rsrc(kv_pe + (int64_t)kt * pe_ss, (uint32_t)nrows * pe_ss), pe_ss,
+                          nrows, buf + LAT_BYTES, wave, lane);
+  };
+  // Speculative copies of the first two tiles as if the split were full:
+  // rows below the cache capacity are always inside the caller's buffer, so
+  // this is safe before the prefix length is known; it is right whenever the
+  // split really covers both tiles (every split but a sequence's last).
+  const bool spec = (int64_t)k_begin + 2 * kBN <= a.capacity;
+  if (spec) {
+    stage_rows(0, s_buf0, kBN);
+    stage_rows(1, s_buf1, kBN);
+  }
+
   const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
   const int N = L + a.q;
-  const int k_begin = split * a.split_keys;
 
+  if (bad || k_begin >= N) wait_vmem_lds<0>();   // no copy may outlive the workgroup
   if (bad) {
     // skipped sequence: zero output, lse = -inf (direct) or an empty partial
     if (tid == 0 && rt == 0 && split == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_LEN);
@@ -365,20 +391,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if (k_begin >= N) return;                   // this split does not exist for sequence b
   const int k_end = min(N, k_begin + a.split_keys);
   const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
+  const bool spec_ok = spec && k_begin + 2 * kBN <= k_end;
 
-  const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
-  const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
-  const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
-  const uint32_t pe_ss = (uint32_t)(a.k_pe_ss * (int64_t)sizeof(T));
+  auto stage = [&](int tile, char* buf) { stage_rows(tile, buf, min(kBN, k_end - (k_begin + tile * kBN))); };
 
-  auto stage = [&](int tile, char* buf) {
-    const int kt = k_begin + tile * kBN;
-    const int nrows = min(kBN, k_end - kt);
-    stage_region<kBN, RC>(make_rsrc(kv_lat + (int64_t)kt * lat_ss, (uint32_t)nrows * lat_ss), lat_ss,
-                          nrows, buf, wave, lane);
-    stage_region<kBN, PC>(make_rsrc(kv_pe + (int64_t)kt * pe_ss, (uint32_t)nrows * pe_ss), pe_ss,
-                          nrows, buf + LAT_BYTES, wave, lane);
-  };
 
   // Per-lane LDS byte offsets inside a tile buffer (bf16 only; the fp32 path
   // computes its addresses inline).
@@ -474,11 +490,34 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       s = MM::mma(cur, qf[c], s);
       fence_mem_mfma();
     }
+    // Value operand of contraction step c (16 keys), output block db.
+    auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
+      if constexpr (KW == 1) {
+        // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
+        const int col = (db * 32 + r) * (int)sizeof(T);
+        return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
+      } else {
+        // bf16: two transposing reads (lane bases computed before the loop)
+        const int o = 64 * db + c * 16 * RC * 16;
+        const bf16x4 lo = lds_read_tr16(buf + pv_base[0][db & 3] + o);
+        const bf16x4 hi = lds_read_tr16(buf + pv_base[1][db & 3] + o);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    constexpr int STEPS = PV_STEPS * NB;
+    constexpr int VPF = STEPS < KDT_VALUE_PREFETCH ? STEPS : KDT_VALUE_PREFETCH;
+    // The first value operands are requested now, so their LDS latency
+    // passes during the softmax instead of stalling the first value MFMA.
+    frag vq[VPF + 1];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NB, i % NB);
 
     // ---- online softmax for this lane's row (16 of the tile's 32 keys)
+    // Raw scores; the scale (positive) is applied to the row max and folded
+    // into each weight's exponent, one fused multiply-add per weight.
     float sv[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sv[v] = s[v] * a.scale_log2;
+    for (int v = 0; v < 16; ++v) sv[v] = s[v];
     if (kt + kBN > L || kt + kBN > k_end) {   // only tiles reaching the tree or the split end
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -492,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     float mx = sv[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = xhalf_max(mx);
+    mx = xhalf_max(mx) * a.scale_log2;
     m_max = fmaxf(m_max, mx);
     // Only tiles where some row of the wave still lacks its reference take
     // this (uniform) branch; elsewhere the weights below depend on the fixed
@@ -520,33 +559,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(sv[v] - m_use);
+      p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], a.scale_log2, -m_use));
       l_run += p[v];
     }
 
     // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]; the value operand of
-    // step i + VPF is read while step i's MFMA is issued.
-    auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
-      if constexpr (KW == 1) {
-        // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
-        const int col = (db * 32 + r) * (int)sizeof(T);
-        return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
-      } else {
-        // bf16: two transposing reads (lane bases computed before the loop)
-        const int o = 64 * db + c * 16 * RC * 16;
-        const bf16x4 lo = lds_read_tr16(buf + pv_base[0][db & 3] + o);
-        const bf16x4 hi = lds_read_tr16(buf + pv_base[1][db & 3] + o);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    };
+    // step i + VPF is read while step i's MFMA is issued (the first VPF were
+    // requested before the softmax).
     frag pfr[PV_STEPS];
 #pragma unroll
     for (int c = 0; c < PV_STEPS; ++c) pfr[c] = MM::pack(p + c * KW);
-    constexpr int STEPS = PV_STEPS * NB;
-    constexpr int VPF = STEPS < KDT_VALUE_PREFETCH ? STEPS : KDT_VALUE_PREFETCH;
-    frag vq[VPF + 1];
-#pragma unroll
-    for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NB, i % NB);
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
       const int c = i / NB, db = i % NB;
@@ -585,9 +607,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     // The first tile, the query fragments and the visibility words are all
     // waited for here, visibly to the compiler, so that it places no wait for
     // them inside the loop (where it would also drain the tile copies).
-    stage(0, s_buf0);
-    wait_vmem_lds<0>();
-    if (n_tiles > 1) stage(1, s_buf1);
+    if (pass == 0 && spec_ok) {
+      wait_vmem_lds<0>();                     // the speculative copies were right
+    } else {
+      wait_vmem_lds<0>();                     // speculative copies land before their buffers are reused
+      stage(0, s_buf0);
+      wait_vmem_lds<0>();
+      if (n_tiles > 1) stage(1, s_buf1);
+    }
 #pragma unroll 1
     for (int tile = 0; tile < n_tiles; tile += 3) {
       wait_tile(tile + 1 < n_tiles);
