@@ -226,3 +226,17 @@ def test_bad_prefix_lengths_are_skipped_and_flagged():
         ro, rl = oracle_full(synth.Inputs(cfg, inp.parents[:1], inp.prefix_lens[:1], inp.q_lat[:1],
                                           inp.q_pe[:1], inp.cache[:1], inp.accepted[:1], inp.n_accepted[:1]))
         check_close("bf16", o[:1], ro, l[:1], rl, f"good sequence, split={sk}")
+
+
+@pytest.mark.parametrize("q,H", [(3, 16), (4, 16), (65, 1)])
+@pytest.mark.parametrize("split_keys", [0, 64, 4096])
+def test_short_row_counts_all_split_modes(q, H, split_keys):
+    # q*H = 48 (second 32-row block half filled), 64 (exactly two blocks: the
+    # column-split layout of a workgroup) and 65 (just past it, the full
+    # layout); forced small splits, automatic, and one split (direct output)
+    cfg = small_cfg(q=q, H=H, tree="uniform", prefix=("uniform", 100, 700), B=3, index=101 + q + H)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g, split_keys=split_keys)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o, ro, l, rl, f"q={q} H={H} split_keys={split_keys}")

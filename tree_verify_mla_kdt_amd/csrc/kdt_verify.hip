@@ -222,12 +222,13 @@ __device__ __forceinline__ void dma16_to_lds(i32x4 rs, uint32_t lds, uint32_t vo
       : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (N < 16): this wave's older tile copies have
-// landed in LDS and its own LDS reads have returned.
+// s_waitcnt vmcnt(N) lgkmcnt(0) (N < 64): this wave's older tile copies have
+// landed in LDS and its own LDS reads have returned.  The 6-bit vmcnt field
+// is split: bits 3:0 of the immediate and bits 15:14.
 template <int N>
 __device__ __forceinline__ void wait_vmem_lds() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (which would
@@ -278,7 +279,14 @@ __device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, c
   }
 }
 
-template <typename T, int R, int P, bool DIRECT>
+// CS (column split) = 1: the four waves own 32 rows each, all R output
+// columns.  CS = 2, for sequences of at most 64 rows (AR decoding and small
+// trees): two row blocks of 32, each owned by a pair of waves that compute the
+// same scores and softmax and split the R output columns between them.  Each
+// wave then holds half the accumulators (no stash) and does half the value
+// MFMAs; the duplicated score MFMAs are spare capacity when the memory stream
+// is the bound.
+template <typename T, int R, int P, bool DIRECT, int CS>
 __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a) {
   typedef Mfma<T> MM;
   typedef typename MM::frag frag;
@@ -286,6 +294,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int KW = MM::KW, KMF = MM::KMF;
   constexpr int NCHUNK = D / KMF;             // MFMA steps of the score contraction
   constexpr int NB = R / 32;                  // 32-wide output column blocks
+  static_assert(CS == 1 || CS == 2, "column split");
+  constexpr int NBL = NB / CS;                // output column blocks of one wave
+  constexpr int BM = kBM / CS;                // query rows per workgroup
   constexpr int PV_STEPS = kBN / KMF;         // MFMA steps of the value contraction per tile
   constexpr int RC = R * (int)sizeof(T) / 16; // 16-byte chunks of c_kv per key
   constexpr int PC = P * (int)sizeof(T) / 16; // 16-byte chunks of k_pe per key
@@ -293,19 +304,21 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int BUF_BYTES = LAT_BYTES + kBN * PC * 16;
   static_assert(R % 32 == 0 && D % KMF == 0 && (P * sizeof(T)) % 16 == 0, "shape");
 
-  // Three distinct LDS objects (not one array indexed at run time) so the
-  // compiler can tell the DMA into one buffer from the reads of another and
-  // does not wait for the prefetches before computing.
-  __shared__ __attribute__((aligned(1024))) char s_buf0[BUF_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_buf1[BUF_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_buf2[BUF_BYTES];
-  // vmcnt that leaves exactly one (the newest) tile copy in flight on every
-  // wave (a wave that issued more waits a little longer, which is safe).
+  // Ring of NBUF key-tile buffers, NBUF - 1 copies in flight: three where
+  // the accumulator stash also needs LDS, four otherwise.  The copies are
+  // inline asm the compiler does not track, so one array indexed with
+  // constants serves.
+  constexpr bool STASH_LDS = (NBL == 16);
+  constexpr int NBUF = STASH_LDS ? 3 : 4;
+  __shared__ __attribute__((aligned(1024))) char s_tiles[NBUF][BUF_BYTES];
+  // vmcnt per tile copy on every wave (a wave that issued more waits a
+  // little longer, which is safe).
   constexpr int STAGE_LOADS = min_wave_loads(kBN * RC) + min_wave_loads(kBN * PC);
+  static_assert(STAGE_LOADS * (NBUF - 2) < 64, "vmcnt range");
   __shared__ int s_dead;
   // One accumulator block per lane parks here while the score tile is alive
   // (all 512 registers are otherwise taken: 256 accumulators, Q, scores).
-  constexpr bool STASH = (NB == 16);
+  constexpr bool STASH = STASH_LDS;
   __shared__ __attribute__((aligned(16))) f32x4 s_stash[STASH ? kThreads * 4 : 1];
 
   const int u = xcd_remap(blockIdx.x, gridDim.x);
@@ -316,7 +329,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int m = rt * kBM + wave * 32 + r;     // this lane's query row
+  const int rb = wave / CS, chalf = wave % CS;   // row block, output column half
+  const int m = rt * BM + rb * 32 + r;        // this lane's query row
   const bool row_ok = m < a.M;
   const int t = row_ok ? m / a.H : 0;
   const int h = row_ok ? m - t * a.H : 0;
@@ -366,8 +380,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // split really covers both tiles (every split but a sequence's last).
   const bool spec = (int64_t)k_begin + 2 * kBN <= a.capacity;
   if (spec) {
-    stage_rows(0, s_buf0, kBN);
-    stage_rows(1, s_buf1, kBN);
+    stage_rows(0, s_tiles[0], kBN);
+    stage_rows(1, s_tiles[1], kBN);
   }
 
   const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if (bad) {
     // skipped sequence: zero output, lse = -inf (direct) or an empty partial
     if (tid == 0 && rt == 0 && split == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_LEN);
-    if (row_ok && hh == 0) {
+    if (row_ok && hh == 0 && chalf == 0) {
       if (DIRECT) {
         a.lse[(int64_t)b * a.M + m] = -INFINITY;
         T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
@@ -394,6 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const bool spec_ok = spec && k_begin + 2 * kBN <= k_end;
 
   auto stage = [&](int tile, char* buf) { stage_rows(tile, buf, min(kBN, k_end - (k_begin + tile * kBN))); };
+
 
 
   // Per-lane LDS byte offsets inside a tile buffer (bf16 only; the fp32 path
@@ -437,9 +452,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     }
   }
 
-  f32x16 acc[NB];
+  f32x16 acc[NBL];
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i = 0; i < NBL; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
   // Softmax state of this lane's row (log2 domain).  m_ref is the reference
@@ -460,8 +475,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     if constexpr (STASH) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        s_stash[g * kThreads + tid] = f32x4{acc[NB - 1][4 * g], acc[NB - 1][4 * g + 1], acc[NB - 1][4 * g + 2],
-                                            acc[NB - 1][4 * g + 3]};
+        s_stash[g * kThreads + tid] = f32x4{acc[NBL - 1][4 * g], acc[NBL - 1][4 * g + 1], acc[NBL - 1][4 * g + 2],
+                                            acc[NBL - 1][4 * g + 3]};
     }
     // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T.
     // The K fragments are read QPF steps ahead of the MFMA chain.
@@ -494,23 +509,24 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
       if constexpr (KW == 1) {
         // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
-        const int col = (db * 32 + r) * (int)sizeof(T);
+        const int col = ((chalf * NBL + db) * 32 + r) * (int)sizeof(T);
         return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
       } else {
         // bf16: two transposing reads (lane bases computed before the loop)
-        const int o = 64 * db + c * 16 * RC * 16;
-        const bf16x4 lo = lds_read_tr16(buf + pv_base[0][db & 3] + o);
-        const bf16x4 hi = lds_read_tr16(buf + pv_base[1][db & 3] + o);
+        const int dg = chalf * NBL + db;      // global output column block
+        const int o = 64 * dg + c * 16 * RC * 16;
+        const bf16x4 lo = lds_read_tr16(buf + pv_base[0][dg & 3] + o);
+        const bf16x4 hi = lds_read_tr16(buf + pv_base[1][dg & 3] + o);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
-    constexpr int STEPS = PV_STEPS * NB;
+    constexpr int STEPS = PV_STEPS * NBL;
     constexpr int VPF = STEPS < KDT_VALUE_PREFETCH ? STEPS : KDT_VALUE_PREFETCH;
     // The first value operands are requested now, so their LDS latency
     // passes during the softmax instead of stalling the first value MFMA.
     frag vq[VPF + 1];
 #pragma unroll
-    for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NB, i % NB);
+    for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NBL, i % NBL);
 
     // ---- online softmax for this lane's row (16 of the tile's 32 keys)
     // Raw scores; the scale (positive) is applied to the row max and folded
@@ -548,10 +564,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 v = s_stash[g * kThreads + tid];
-        acc[NB - 1][4 * g] = v[0];
-        acc[NB - 1][4 * g + 1] = v[1];
-        acc[NB - 1][4 * g + 2] = v[2];
-        acc[NB - 1][4 * g + 3] = v[3];
+        acc[NBL - 1][4 * g] = v[0];
+        acc[NBL - 1][4 * g + 1] = v[1];
+        acc[NBL - 1][4 * g + 2] = v[2];
+        acc[NBL - 1][4 * g + 3] = v[3];
       }
     }
     if (dead) return;                       // keep tracking m_max only
@@ -571,8 +587,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     for (int c = 0; c < PV_STEPS; ++c) pfr[c] = MM::pack(p + c * KW);
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
-      const int c = i / NB, db = i % NB;
-      if (i + VPF < STEPS) vq[(i + VPF) % (VPF + 1)] = value_frag((i + VPF) / NB, (i + VPF) % NB);
+      const int c = i / NBL, db = i % NBL;
+      if (i + VPF < STEPS) vq[(i + VPF) % (VPF + 1)] = value_frag((i + VPF) / NBL, (i + VPF) % NBL);
       acc[db] = MM::mma(vq[i % (VPF + 1)], pfr[c], acc[db]);
       fence_mem_mfma();
     }
@@ -586,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       if (s_dead == 0) break;                 // common case: no redo
       if (dead) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NBL; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
         l_run = 0.0f;
@@ -595,12 +611,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     }
     const bool compute = (pass == 0) || dead;
     dead = false;
-    // Tiles rotate through the three buffers with two copies in flight: each
-    // step waits for its own tile (the copy of the following tile may still
-    // run), then starts the copy of the tile two ahead into the buffer the
-    // previous step has finished reading, and computes.
-    auto wait_tile = [&](bool newer_in_flight) __attribute__((always_inline)) {
-      if (newer_in_flight) wait_vmem_lds<STAGE_LOADS>();
+    // Tiles rotate through the NBUF buffers: the step for tile t waits for its
+    // copy (the copies of the following tiles may still run), starts the copy
+    // of tile t + NBUF - 1 into the buffer the previous step has finished
+    // reading, and computes.
+    auto wait_tile = [&](int newer) __attribute__((always_inline)) {
+      // copies of tiles t + 1 .. t + newer may stay in flight
+      if (newer >= 2 && NBUF > 3) wait_vmem_lds<STAGE_LOADS * (NBUF > 3 ? 2 : 1)>();
+      else if (newer >= 1) wait_vmem_lds<STAGE_LOADS>();
       else wait_vmem_lds<0>();
       tile_barrier();
     };
@@ -611,23 +629,23 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       wait_vmem_lds<0>();                     // the speculative copies were right
     } else {
       wait_vmem_lds<0>();                     // speculative copies land before their buffers are reused
-      stage(0, s_buf0);
+      stage(0, s_tiles[0]);
       wait_vmem_lds<0>();
-      if (n_tiles > 1) stage(1, s_buf1);
+      if (n_tiles > 1) stage(1, s_tiles[1]);
     }
+#pragma unroll
+    for (int k = 2; k < NBUF - 1; ++k)
+      if (k < n_tiles) stage(k, s_tiles[k]);
 #pragma unroll 1
-    for (int tile = 0; tile < n_tiles; tile += 3) {
-      wait_tile(tile + 1 < n_tiles);
-      if (tile + 2 < n_tiles) stage(tile + 2, s_buf2);
-      if (compute) tile_body(tile, s_buf0);
-      if (tile + 1 >= n_tiles) break;
-      wait_tile(tile + 2 < n_tiles);
-      if (tile + 3 < n_tiles) stage(tile + 3, s_buf0);
-      if (compute) tile_body(tile + 1, s_buf1);
-      if (tile + 2 >= n_tiles) break;
-      wait_tile(tile + 3 < n_tiles);
-      if (tile + 4 < n_tiles) stage(tile + 4, s_buf1);
-      if (compute) tile_body(tile + 2, s_buf2);
+    for (int tile = 0; tile < n_tiles; tile += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        const int t = tile + k;
+        if (t >= n_tiles) break;
+        wait_tile(min(NBUF - 2, n_tiles - 1 - t));
+        if (t + NBUF - 1 < n_tiles) stage(t + NBUF - 1, s_tiles[(k + NBUF - 1) % NBUF]);
+        if (compute) tile_body(t, s_tiles[k]);
+      }
     }
   }
 
@@ -640,31 +658,31 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if (DIRECT) {
     T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
 #pragma unroll
-    for (int db = 0; db < NB; ++db)
+    for (int db = 0; db < NBL; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float v4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
-        store4<T>(o + db * 32 + 8 * g + 4 * hh, v4);
+        store4<T>(o + (chalf * NBL + db) * 32 + 8 * g + 4 * hh, v4);
       }
-    if (hh == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
+    if (hh == 0 && chalf == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
   } else {
     // Partials stay in accumulator order: the wave's 32 rows form one block
     // of 32 x R floats in which register group (db, g) of every lane is one
     // contiguous 1 KB run, so each store instruction writes whole lines.
-    const int blk = rt * (kBM / 32) + wave;
+    const int blk = rt * (BM / 32) + rb;
     float* o = a.part_o + (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R) + 4 * lane;
 #pragma unroll
-    for (int db = 0; db < NB; ++db)
+    for (int db = 0; db < NBL; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float v4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
-        store4<float>(o + 256 * (4 * db + g), v4);
+        store4<float>(o + 256 * (4 * (chalf * NBL + db) + g), v4);
       }
-    if (hh == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
+    if (hh == 0 && chalf == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
   }
 }
 
@@ -779,10 +797,11 @@ static int validate(const kdt_verify_desc* d) {
 // the HBM rate, and splitting at all adds the merge launch.  Constants are in
 // microseconds for one 128-row x 32-key tile at R = 512, P = 64 and scale with
 // the contraction depth 2R + P; they need only be right in ratio.
-static int64_t auto_split_keys(int64_t base, int64_t n_max, int R, int P) {
-  const double t_tile = 1.3 * (2.0 * R + P) / 1088.0;
+static int64_t auto_split_keys(int64_t base, int64_t n_max, int R, int P, int cs) {
+  // a wave's per-tile MFMA work: the score chain plus its share of values
+  const double t_tile = 1.3 * (R + P + (double)R / cs) / 1088.0;
   const double t_start = 4.0;
-  const double t_part = (double)kBM * R * 4 * 2 / 5.0e6;
+  const double t_part = (double)(kBM / cs) * R * 4 * 2 / 5.0e6;
   const double t_merge = 5.0;
   const int64_t n_tiles = (n_max + kBN - 1) / kBN;
   int64_t best_sk = (n_max + 63) / 64 * 64;
@@ -802,14 +821,18 @@ static int64_t auto_split_keys(int64_t base, int64_t n_max, int R, int P) {
   return best_sk;
 }
 
+// Column split of a workgroup's waves (see verify_split_kernel).
+static int col_split(int64_t M) { return M <= kBM / 2 ? 2 : 1; }
+
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int rc = validate(d);
   if (rc != KDT_OK) return rc;
   const int M = d->q_len * d->H;
-  const int n_rt = (M + kBM - 1) / kBM;
+  const int cs = col_split(M);
+  const int n_rt = (M + kBM / cs - 1) / (kBM / cs);
   const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
   int64_t sk = d->split_keys;
-  if (sk == 0) sk = auto_split_keys((int64_t)d->B * n_rt, n_max, d->R, d->P);
+  if (sk == 0) sk = auto_split_keys((int64_t)d->B * n_rt, n_max, d->R, d->P, cs);
   const int64_t ns = (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
@@ -840,7 +863,7 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.seq_status = d->seq_status;
   a.scale_log2 = d->softmax_scale * kLog2e;
   a.B = d->B; a.q = d->q_len; a.H = d->H; a.M = d->q_len * d->H; a.W = (d->q_len + 63) / 64;
-  a.n_rt = (a.M + kBM - 1) / kBM;
+  a.n_rt = (a.M + kBM / col_split(a.M) - 1) / (kBM / col_split(a.M));
   a.n_blk = (a.M + 31) / 32;
   a.max_splits = p.max_splits;
   a.split_keys = p.split_keys;
@@ -852,10 +875,15 @@ template <typename T, int R, int P>
 static int launch_split(const VerifyArgs& a, bool direct, hipStream_t s) {
   const int64_t grid = (int64_t)a.B * a.n_rt * a.max_splits;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
-  if (direct)
-    hipLaunchKernelGGL((verify_split_kernel<T, R, P, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const bool cs2 = col_split(a.M) == 2;
+  if (direct && cs2)
+    hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else if (direct)
+    hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else if (cs2)
+    hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((verify_split_kernel<T, R, P, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return launch_status();
 }
 
