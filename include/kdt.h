@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDT_ABI_VERSION 1
+#define KDT_ABI_VERSION 2
 #define KDT_MAX_Q_LEN 128           /* tree tokens per sequence (two 64-bit mask words) */
 
 typedef enum {
@@ -125,6 +125,13 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  * workspace; a second kernel merges the splits by the log-sum-exp identity.
  * When every sequence fits in one split the merge is skipped and the first
  * kernel writes out/lse directly.
+ *
+ * Workgroup layout (`layout`): 1 = a workgroup owns 128 rows (q_len*H rows of
+ * one sequence), each of its four waves 32 rows and all R output columns;
+ * 2 = a workgroup owns 64 rows, each pair of waves shares 32 rows and splits
+ * the output columns (half the value work per wave, the score work done by
+ * both).  0 lets the library choose (and the split size) by modelling the
+ * launch; results agree between layouts to rounding.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t dtype;                       /* kdt_dtype */
@@ -142,6 +149,7 @@ typedef struct {
   float* lse;                          /* device float32 [B, q_len, H] */
   int32_t* seq_status;                 /* device int32 [B], nullable */
   int32_t split_keys;                  /* 0 = auto, else a multiple of 64 */
+  int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split */
 } kdt_verify_desc;
 
 /* Host-only planning: no device access.  The partial buffers live in the
@@ -160,6 +168,7 @@ typedef struct {
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
   int32_t rows;                /* q_len * H */
   int32_t direct;              /* 1: max_splits == 1, no partials, no merge */
+  int32_t layout;              /* workgroup layout used: 1 or 2 */
   int64_t part_o_offset;       /* bytes into the workspace */
   int64_t part_lse_offset;
   size_t workspace_bytes;      /* 0 when direct */

@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
 
 
 def test_version_and_status_strings():
-    assert kdt.lib().kdt_abi_version() == 1
+    assert kdt.lib().kdt_abi_version() == 2
     for code in range(5):
         assert kdt.status_str(code)
     assert kdt.status_str(99) == "unknown status"
@@ -149,3 +149,20 @@ def test_partial_tiling_round_trip():
         m, c = M - 1, R - 3
         flat = t[1, 2, m // 32]
         assert flat[256 * (c // 8) + 128 * ((c // 4) % 2) + 4 * (m % 32) + c % 4] == x[1, 2, m, c]
+
+
+def test_layout_forcing_and_validation():
+    for layout in (1, 2):
+        rc, p = _plan(_desc(layout=layout))
+        assert rc == 0 and p.layout == layout
+        rows = 128 if layout == 1 else 64
+        assert p.rows == 65 * 16 and rows in (64, 128)
+    rc, p = _plan(_desc())
+    assert rc == 0 and p.layout in (1, 2)
+    rc, p = _plan(_desc(layout=3))
+    assert rc == kdt.KDT_ERR_INVALID_ARG if hasattr(kdt, "KDT_ERR_INVALID_ARG") else rc == 1
+    rc, p = _plan(_desc(layout=-1))
+    assert rc == 1
+    # AR decoding (64 rows) plans the column-split layout
+    rc, p = _plan(_desc(q_len=1, H=64, max_prefix_len=32768, capacity=32769))
+    assert rc == 0 and p.layout == 2

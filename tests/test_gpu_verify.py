@@ -18,13 +18,13 @@ from gpu_util import (GpuInputs, check_close, oracle_full, oracle_rows, require_
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(g: GpuInputs, split_keys=0, vis=None, max_prefix_len=None, seq_status=None):
+def run_gpu(g: GpuInputs, split_keys=0, vis=None, max_prefix_len=None, seq_status=None, layout=0):
     require_gpu()
     if vis is None:
         vis, _ = kdt.build_visibility(g.parents)
     out, lse = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis, g.cfg.softmax_scale,
                                max_prefix_len=g.max_prefix_len if max_prefix_len is None else max_prefix_len,
-                               split_keys=split_keys, seq_status=seq_status)
+                               split_keys=split_keys, seq_status=seq_status, layout=layout)
     torch.cuda.synchronize()
     return to_f64(out), lse.cpu().numpy().astype(np.float64)
 
@@ -240,3 +240,26 @@ def test_short_row_counts_all_split_modes(q, H, split_keys):
     o, l = run_gpu(g, split_keys=split_keys)
     ro, rl = oracle_full(inp)
     check_close("bf16", o, ro, l, rl, f"q={q} H={H} split_keys={split_keys}")
+
+
+@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("q,H,tree", [(1, 16, "chain"), (17, 16, "uniform"), (65, 16, "best_first"),
+                                      (33, 3, "deep_chain")])
+def test_forced_layouts_match_oracle(layout, q, H, tree):
+    cfg = small_cfg(q=q, H=H, tree=tree, prefix=("uniform", 50, 900), B=2, index=140 + q + H)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    ro, rl = oracle_full(inp)
+    for sk in (0, 128):
+        o, l = run_gpu(g, split_keys=sk, layout=layout)
+        check_close("bf16", o, ro, l, rl, f"layout={layout} q={q} H={H} split_keys={sk}")
+
+
+def test_config_max_budget_both_layouts_agree():
+    inp = synth.generate(synth.CONFIGS["max_budget"])
+    g = GpuInputs(inp)
+    o1, l1 = run_gpu(g, layout=1)
+    o2, l2 = run_gpu(g, layout=2)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o1, ro, l1, rl, "max_budget layout 1")
+    check_close("bf16", o2, ro, l2, rl, "max_budget layout 2")

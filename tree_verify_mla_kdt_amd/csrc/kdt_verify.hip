@@ -119,7 +119,7 @@ struct VerifyArgs {
   float* part_lse;
   int32_t* seq_status;
   float scale_log2;
-  int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len;
+  int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len, layout;
 };
 
 // The value of C-layout register v of a 32x32 MFMA result held by a lane in
@@ -774,6 +774,7 @@ static int validate(const kdt_verify_desc* d) {
   if (d->max_prefix_len < 0 || d->capacity < (int64_t)d->max_prefix_len + d->q_len)
     return KDT_ERR_INVALID_ARG;
   if (d->split_keys < 0 || (d->split_keys % 64) != 0) return KDT_ERR_INVALID_ARG;
+  if (d->layout < 0 || d->layout > 2) return KDT_ERR_INVALID_ARG;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
   if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
   if (!shape_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
@@ -790,49 +791,56 @@ static int validate(const kdt_verify_desc* d) {
   return KDT_OK;
 }
 
-// Split size chosen by a small time model of one launch.  Workgroups run one
-// per compute unit, so a grid of G workgroups takes ceil(G / kCU) rounds; a
-// round costs its key tiles plus a fixed start-up (query load, first-tile
-// latency); every partial then costs its write and its read in the merge at
-// the HBM rate, and splitting at all adds the merge launch.  Constants are in
-// microseconds for one 128-row x 32-key tile at R = 512, P = 64 and scale with
-// the contraction depth 2R + P; they need only be right in ratio.
-static int64_t auto_split_keys(int64_t base, int64_t n_max, int R, int P, int cs) {
-  // a wave's per-tile MFMA work: the score chain plus its share of values
-  const double t_tile = 1.3 * (R + P + (double)R / cs) / 1088.0;
-  const double t_start = 4.0;
-  const double t_part = (double)(kBM / cs) * R * 4 * 2 / 5.0e6;
-  const double t_merge = 5.0;
-  const int64_t n_tiles = (n_max + kBN - 1) / kBN;
-  int64_t best_sk = (n_max + 63) / 64 * 64;
-  double best = 1e300;
-  for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
-    int64_t sk = (n_max + s - 1) / s;
-    sk = (sk + 63) / 64 * 64;
-    const int64_t ns = (n_max + sk - 1) / sk;
-    if (ns != s) continue;                    // covered by a smaller s
-    const int64_t rounds = (ns * base + kCU - 1) / kCU;
-    const double cost = rounds * ((sk / kBN) * t_tile + t_start) + (ns > 1 ? ns * base * t_part + t_merge : 0.0);
-    if (cost < best * 0.999) {                // ties go to fewer splits
-      best = cost;
-      best_sk = sk;
-    }
-  }
-  return best_sk;
-}
+// Rows per workgroup of a layout (1: four waves x 32 rows; 2: two row blocks,
+// each shared by a wave pair that splits the output columns).
+static int layout_rows(int layout) { return layout == 2 ? kBM / 2 : kBM; }
 
-// Column split of a workgroup's waves (see verify_split_kernel).
-static int col_split(int64_t M) { return M <= kBM / 2 ? 2 : 1; }
+// Modelled time (microseconds) of one launch, split kernel plus merge, for a
+// layout and split size.  Workgroups run one per compute unit, so G of them
+// take ceil(G / kCU) rounds; a round costs its key tiles plus a start-up (the
+// burst of query and first-tile loads), every partial costs its write and its
+// read in the merge, and splitting at all adds the merge launch.  The
+// constants are fitted to measurements at R = 512, P = 64 (a 128-row tile of
+// 32 keys about 2.05 us, a 128-row partial about 0.12 us) and scale with the
+// contraction work of one wave and with the rows a partial holds.
+static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R, int P, int layout) {
+  const int rows = layout_rows(layout);
+  const double t_tile = 2.05 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+  const double t_start = 6.0;
+  const double t_part = 0.12 * rows / kBM * R / 512.0;
+  const double t_merge = 5.0;
+  const int64_t ns = (n_max + sk - 1) / sk;
+  const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
+  return rounds * ((sk / kBN) * t_tile + t_start) + (ns > 1 ? ns * n_seq_tiles * t_part + t_merge : 0.0);
+}
 
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int rc = validate(d);
   if (rc != KDT_OK) return rc;
   const int M = d->q_len * d->H;
-  const int cs = col_split(M);
-  const int n_rt = (M + kBM / cs - 1) / (kBM / cs);
   const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
+  // candidate layouts: the requested one, or both; candidate split sizes:
+  // the requested one, or every distinct split count up to 4096
+  int best_layout = d->layout ? d->layout : 1;
   int64_t sk = d->split_keys;
-  if (sk == 0) sk = auto_split_keys((int64_t)d->B * n_rt, n_max, d->R, d->P, cs);
+  double best = 1e300;
+  for (int layout = 1; layout <= 2; ++layout) {
+    if (d->layout && layout != d->layout) continue;
+    const int64_t n_seq_tiles = (int64_t)d->B * ((M + layout_rows(layout) - 1) / layout_rows(layout));
+    const int64_t n_tiles = (n_max + kBN - 1) / kBN;
+    for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
+      int64_t k = d->split_keys ? d->split_keys : ((n_max + s - 1) / s + 63) / 64 * 64;
+      if (!d->split_keys && (n_max + k - 1) / k != s) continue;   // covered by a smaller s
+      const double c = launch_cost(n_seq_tiles, n_max, k, d->R, d->P, layout);
+      if (c < best * 0.999) {                 // ties go to fewer splits, then layout 1
+        best = c;
+        sk = k;
+        best_layout = layout;
+      }
+      if (d->split_keys) break;
+    }
+  }
+  p->layout = best_layout;
   const int64_t ns = (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
@@ -863,7 +871,8 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.seq_status = d->seq_status;
   a.scale_log2 = d->softmax_scale * kLog2e;
   a.B = d->B; a.q = d->q_len; a.H = d->H; a.M = d->q_len * d->H; a.W = (d->q_len + 63) / 64;
-  a.n_rt = (a.M + kBM / col_split(a.M) - 1) / (kBM / col_split(a.M));
+  a.layout = p.layout;
+  a.n_rt = (a.M + layout_rows(p.layout) - 1) / layout_rows(p.layout);
   a.n_blk = (a.M + 31) / 32;
   a.max_splits = p.max_splits;
   a.split_keys = p.split_keys;
@@ -875,7 +884,7 @@ template <typename T, int R, int P>
 static int launch_split(const VerifyArgs& a, bool direct, hipStream_t s) {
   const int64_t grid = (int64_t)a.B * a.n_rt * a.max_splits;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
-  const bool cs2 = col_split(a.M) == 2;
+  const bool cs2 = a.layout == 2;
   if (direct && cs2)
     hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else if (direct)

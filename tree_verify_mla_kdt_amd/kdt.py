@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdt.so")
 
 KDT_F32, KDT_BF16 = 0, 1
+ABI_VERSION = 2                       # the KDT_ABI_VERSION this binding was written for
 KDT_SEQ_BAD_TREE, KDT_SEQ_BAD_LEN, KDT_SEQ_BAD_INDEX = 1, 2, 4
 MAX_Q_LEN = 128
 
@@ -37,14 +38,14 @@ class VerifyDesc(ctypes.Structure):
         ("out", _c_p), ("out_sb", _c_i64), ("out_st", _c_i64), ("out_sh", _c_i64),
         ("lse", _c_p),
         ("seq_status", _c_p),
-        ("split_keys", _c_i32),
+        ("split_keys", _c_i32), ("layout", _c_i32),
     ]
 
 
 class VerifyPlan(ctypes.Structure):
     _fields_ = [
         ("split_keys", _c_i32), ("max_splits", _c_i32), ("rows", _c_i32), ("direct", _c_i32),
-        ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64), ("workspace_bytes", ctypes.c_size_t),
+        ("layout", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -78,7 +79,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_partials",
                    "kdt_merge_partials", "kdt_gather_accepted"):
             getattr(L, fn).restype = ctypes.c_int
-        if L.kdt_abi_version() != 1:
+        if L.kdt_abi_version() != ABI_VERSION:
             raise RuntimeError("libkdt.so ABI version mismatch")
         _lib = L
     return _lib
@@ -128,7 +129,7 @@ def build_visibility(parents: torch.Tensor, vis=None, depth=None, seq_status=Non
 
 
 def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                 seq_status, split_keys):
+                 seq_status, split_keys, layout=0):
     B, q, H, R = q_lat.shape
     P = q_pe.shape[-1]
     d = VerifyDesc()
@@ -147,11 +148,12 @@ def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_p
     d.lse = lse.data_ptr()
     d.seq_status = 0 if seq_status is None else seq_status.data_ptr()
     d.split_keys = int(split_keys)
+    d.layout = int(layout)
     return d
 
 
 def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                    seq_status, split_keys):
+                    seq_status, split_keys, layout=0):
     for t in (q_lat, q_pe, c_kv, k_pe):
         if t.stride(-1) != 1:
             raise ValueError("innermost dimension must be contiguous")
@@ -166,7 +168,7 @@ def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
     if lse is None:
         lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
     d = _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                     seq_status, split_keys)
+                     seq_status, split_keys, layout)
     return d, out, lse
 
 
@@ -177,11 +179,11 @@ def verify_plan(desc: VerifyDesc) -> VerifyPlan:
 
 
 def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
-                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None):
+                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0):
     """Tree-verify attention.  c_kv [B, S, R] and k_pe [B, S, P] may be views of
     one fused [B, S, R+P] cache.  Returns (out [B, q, H, R], lse [B, q, H])."""
     d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                                  out, lse, seq_status, split_keys)
+                                  out, lse, seq_status, split_keys, layout)
     p = verify_plan(d)
     if p.workspace_bytes and (workspace is None or workspace.numel() * workspace.element_size() < p.workspace_bytes):
         workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
@@ -219,12 +221,12 @@ def tile_partials(rows_major):
 
 
 def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None,
-                    workspace=None, seq_status=None, split_keys=0, stream=None):
+                    workspace=None, seq_status=None, split_keys=0, stream=None, layout=0):
     """Split stage only.  Returns (part_o, part_lse, plan): part_o float32
     [B, S, NBLK, 32*R] in the tiled layout (see untile_partials), part_lse
     float32 [B, S, q*H]."""
     d, _, _ = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                              None, None, seq_status, split_keys)
+                              None, None, seq_status, split_keys, layout)
     p = verify_plan(d)
     B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
     need = max(int(p.workspace_bytes), p.part_lse_offset + B * S * M * 4, 1)
