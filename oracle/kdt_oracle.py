@@ -36,6 +36,14 @@ What is computed, and where it comes from:
     gathered into the rows directly after the prefix ("after accept gather
     accepted-path latents", post-verify compaction) [Checkpoint, "The
     Message"].
+  * Greedy tree accept: the engine verifies the tree and accepts a prefix of
+    it greedily, which must reproduce autoregressive greedy decoding
+    [Final, "Input Knowledge Required"; Checkpoint, "The Message",
+    tree_accept and the greedy-exact invariant].  From the root, the walk
+    moves to a child whose draft token equals the target's greedy prediction
+    at the current node, while one exists; the prediction at the last
+    accepted node is the bonus token.  Walks are bounded by the tree size,
+    the safety bound of [Milestone, "Mistakes and Incorrect Assumptions"].
 
 Readings where the pages are silent (each also listed in the design notes):
   * Tree node t's latents sit in cache row L_b + t (node order); its position
@@ -44,6 +52,10 @@ Readings where the pages are silent (each also listed in the design notes):
     else is rejected here (the GPU side flags it per sequence instead).
   * Bits at or above q_len in the last word are zero.
   * The gather reads every source row before writing any destination row.
+  * Accept: when several children of a node carry the predicted token, the
+    lowest-index child (the earliest in best-first order) is taken; the
+    accepted list starts with the root (node 0), so it feeds the gather
+    directly.
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, brute force, library routines or invariants; none is "parity unpinned".
@@ -250,3 +262,52 @@ def gather_accepted(cache, prefix_lens, accepted, n_accepted):
         for k in range(int(n_accepted[b])):
             new[b, L + k] = old[b, L + int(accepted[b, k])]
     return new
+
+
+# ----------------------------------------------------------------------------
+# Greedy tree accept  [Checkpoint, "The Message": tree_accept, greedy-exact;
+# Milestone, "Mistakes and Incorrect Assumptions": walks bounded]
+# ----------------------------------------------------------------------------
+
+def tree_accept(parents, tokens, target_pred):
+    """Greedy acceptance of a verified draft tree, one sequence at a time.
+
+    parents     int [B, q], parent[0] = -1, 0 <= parent[i] < i
+    tokens      int [B, q], the draft token of each node (node 0: the
+                verified token)
+    target_pred int [B, q], the target model's greedy next token after each
+                node (argmax of its logits at that node)
+
+    Returns (accepted [B, q] int32 node indices, -1 past the end,
+    n_accepted [B] int32, bonus [B] int32): starting at the root, repeatedly
+    move to the lowest-index child c of the current node u whose token equals
+    target_pred[u]; stop when no child matches.  accepted lists the visited
+    nodes from the root; bonus = target_pred[last accepted node].
+    """
+    parents = np.asarray(parents)
+    tokens = np.asarray(tokens)
+    target_pred = np.asarray(target_pred)
+    B, q = parents.shape
+    for b in range(B):
+        check_parents(parents[b])
+    accepted = np.full((B, q), -1, dtype=np.int32)
+    n_acc = np.zeros(B, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        u = 0
+        path = [0]
+        for _ in range(q):                      # a path has at most q nodes
+            want = target_pred[b, u]
+            nxt = None
+            for c in range(1, q):               # children in index order
+                if parents[b, c] == u and tokens[b, c] == want:
+                    nxt = c
+                    break
+            if nxt is None:
+                break
+            u = nxt
+            path.append(u)
+        accepted[b, :len(path)] = path
+        n_acc[b] = len(path)
+        bonus[b] = target_pred[b, u]
+    return accepted, n_acc, bonus

@@ -309,3 +309,36 @@ def generate(cfg: Config, seed: int | None = None, *, prefix_override=None,
 def rng_for(tag: int) -> np.random.Generator:
     """A generator for ad-hoc test inputs, seeded off the same base."""
     return np.random.Generator(np.random.PCG64(SEED_BASE + 1000 + int(tag)))
+
+
+def accept_inputs(parents: np.ndarray, seed: int, vocab: int = 32, p_follow: float = 0.75):
+    """Draft tokens and target predictions for a batch of trees (random draws
+    only).  Siblings carry distinct tokens (as a top-k expansion gives); the
+    target's prediction at a node is, with probability p_follow, the token of
+    one of its children (chosen uniformly), and otherwise a token none of its
+    children carries.  Node 0's token is the verified token.
+
+    Returns (tokens [B, q], target_pred [B, q]) as int32."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 2000 + int(seed)))
+    parents = np.asarray(parents)
+    B, q = parents.shape
+    tokens = np.zeros((B, q), dtype=np.int32)
+    pred = np.zeros((B, q), dtype=np.int32)
+    for b in range(B):
+        children = [[] for _ in range(q)]
+        for i in range(1, q):
+            children[int(parents[b, i])].append(i)
+        tokens[b, 0] = rng.integers(vocab)
+        for u in range(q):
+            kids = children[u]
+            if kids:
+                tokens[b, kids] = rng.choice(vocab, size=len(kids), replace=False)
+        for u in range(q):
+            kids = children[u]
+            taken = set(int(tokens[b, c]) for c in kids)
+            if kids and rng.random() < p_follow:
+                pred[b, u] = tokens[b, kids[int(rng.integers(len(kids)))]]
+            else:
+                free = [v for v in range(vocab) if v not in taken]
+                pred[b, u] = free[int(rng.integers(len(free)))]
+    return tokens, pred
