@@ -105,9 +105,11 @@ def write_traffic(args):
 
 
 def source_hash() -> str:
+    """Hash of the sources the split-attention kernel is compiled from: stored
+    traffic counts are used only while this still matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_verify_mla_kdt_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("kdt_common.hpp", "kdt_verify.hip"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -257,6 +259,23 @@ def main():
     torch.cuda.synchronize()
     split_ms = e0.elapsed_time(e1) / (reps * n_copies)
 
+    # --- greedy tree accept on the same trees (timed on its own: the step
+    # above takes the accepted paths as input)
+    tok_np, pred_np = synth.accept_inputs(inp.parents, 0)
+    tok_d, pred_d = torch.from_numpy(tok_np).to(dev), torch.from_numpy(pred_np).to(dev)
+    acc_d = torch.empty((B, q), dtype=torch.int32, device=dev)
+    nacc_d = torch.empty((B,), dtype=torch.int32, device=dev)
+    bonus_d = torch.empty((B,), dtype=torch.int32, device=dev)
+    g_acc = capture(lambda i: kdt.tree_accept(parents, tok_d, pred_d, accepted=acc_d, n_accepted=nacc_d,
+                                              bonus=bonus_d), range(20))
+    g_acc.replay()
+    e0.record(cur)
+    for _ in range(10):
+        g_acc.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    accept_us = e0.elapsed_time(e1) * 1e3 / 200
+
     pairs = visible_pairs(inp.parents, inp.prefix_lens, H)
     flops = pairs * 2 * (R + P + R)                       # score over R+P, value over R
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -300,6 +319,7 @@ def main():
         "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg_bytes,
+        "tree_accept_us": accept_us,
     }
 
     if not args.no_cpu and not args.kernel_only:

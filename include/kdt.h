@@ -230,6 +230,33 @@ int kdt_gather_accepted(int32_t dtype, int32_t B, int32_t q_len, int32_t row_ele
                         const int32_t* n_accepted, int32_t max_acc,
                         int32_t* new_prefix_lens, int32_t* seq_status, void* stream);
 
+/* ------------------------------------------------------------------------
+ * kdt_tree_accept — greedy acceptance of a verified draft tree.
+ * [Checkpoint, "The Message"]: the decode loop runs tree build -> verify ->
+ * tree accept -> cache compaction, and greedy tree decoding reproduces greedy
+ * autoregressive decoding token for token; [Milestone, "Mistakes and
+ * Incorrect Assumptions"]: walks are bounded (cyclic inputs cannot hang).
+ *
+ * For each sequence b, starting at node 0 (the verified token), repeatedly
+ * move to the lowest-index child c of the current node u with
+ * tokens[b][c] == target_pred[b][u]; stop when no child matches.
+ *   parents      int32 [B, q_len]  (as for kdt_build_visibility)
+ *   tokens       int32 [B, q_len]  draft token of each node (node 0: the verified token)
+ *   target_pred  int32 [B, q_len]  the target model's greedy next token after each node
+ *   accepted     int32 [B, q_len]  out: visited nodes from the root, -1 after the last;
+ *                                  pass it with max_acc = q_len to kdt_gather_accepted
+ *   n_accepted   int32 [B]         out: path length (>= 1, the root is always accepted)
+ *   bonus        int32 [B]         out, nullable: target_pred at the last accepted node
+ *   seq_status   int32 [B]         nullable; a node whose parent is not an earlier
+ *                                  node (or node 0 with a parent) is unreachable and
+ *                                  KDT_SEQ_BAD_TREE is flagged
+ * Supported: 1 <= q_len <= KDT_MAX_Q_LEN, B >= 1.  The result is exact
+ * (integer comparisons only).
+ * ---------------------------------------------------------------------- */
+int kdt_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* target_pred,
+                    int32_t B, int32_t q_len, int32_t* accepted, int32_t* n_accepted,
+                    int32_t* bonus, int32_t* seq_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

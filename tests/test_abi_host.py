@@ -109,7 +109,7 @@ def test_verify_needs_workspace_when_split():
     assert rc == 3
 
 
-def test_visibility_and_gather_argument_checks():
+def test_visibility_gather_and_accept_argument_checks():
     L = kdt.lib()
     assert L.kdt_build_visibility(None, 1, 9, FAKE, None, None, None) == 1
     assert L.kdt_build_visibility(FAKE, 0, 9, FAKE, None, None, None) == 1
@@ -125,6 +125,13 @@ def test_visibility_and_gather_argument_checks():
     assert m(1, 1, 9, 4, 512, None, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 1
     assert m(1, 1, 9, 4, 512, FAKE, FAKE, 2, None, 64, FAKE, 0, 0, 0, FAKE, None) == 1           # needs prefix_lens
     assert m(1, 1, 9, 4, 36, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2             # R % 8
+    a = L.kdt_tree_accept
+    # parents, tokens, target_pred, B, q, accepted, n_accepted, bonus, seq_status, stream
+    assert a(None, FAKE, FAKE, 1, 9, FAKE, FAKE, None, None, None) == 1
+    assert a(FAKE, FAKE, FAKE, 1, 9, None, FAKE, None, None, None) == 1
+    assert a(FAKE, FAKE, FAKE, 0, 9, FAKE, FAKE, None, None, None) == 1
+    assert a(FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, None, None, None) == 1
+    assert a(FAKE, FAKE, FAKE, 1, 129, FAKE, FAKE, None, None, None) == 2
 
 
 def test_auto_split_counts_follow_the_launch_model():

@@ -76,8 +76,9 @@ def lib() -> ctypes.CDLL:
                                          _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]
         L.kdt_gather_accepted.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
                                           _c_i64, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p]
+        L.kdt_tree_accept.argtypes = [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p]
         for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_partials",
-                   "kdt_merge_partials", "kdt_gather_accepted"):
+                   "kdt_merge_partials", "kdt_gather_accepted", "kdt_tree_accept"):
             getattr(L, fn).restype = ctypes.c_int
         if L.kdt_abi_version() != ABI_VERSION:
             raise RuntimeError("libkdt.so ABI version mismatch")
@@ -276,6 +277,26 @@ def gather_accepted(cache, prefix_lens, accepted, n_accepted, q_len, row_elems=N
         int(layer_stride), _ptr(prefix_lens), _ptr(accepted), _ptr(n_accepted), accepted.shape[1],
         _ptr(new_prefix_lens), _ptr(seq_status), _stream(stream)))
     return cache
+
+
+def tree_accept(parents, tokens, target_pred, accepted=None, n_accepted=None, bonus=None, seq_status=None,
+                stream=None):
+    """Greedy tree acceptance: int32 [B, q] parents / tokens / target_pred ->
+    (accepted int32 [B, q] with -1 past the path, n_accepted int32 [B], bonus int32 [B])."""
+    for t in (parents, tokens, target_pred):
+        assert t.dtype == torch.int32 and t.is_contiguous() and t.dim() == 2 and t.shape == parents.shape
+    B, q = parents.shape
+    dev = parents.device
+    if accepted is None:
+        accepted = torch.empty((B, q), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("kdt_tree_accept", lib().kdt_tree_accept(
+        _ptr(parents), _ptr(tokens), _ptr(target_pred), B, q, _ptr(accepted), _ptr(n_accepted), _ptr(bonus),
+        _ptr(seq_status), _stream(stream)))
+    return accepted, n_accepted, bonus
 
 
 def softmax_scale_for(R: int, P: int) -> float:

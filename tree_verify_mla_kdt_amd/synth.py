@@ -332,13 +332,15 @@ def accept_inputs(parents: np.ndarray, seed: int, vocab: int = 32, p_follow: flo
         for u in range(q):
             kids = children[u]
             if kids:
-                tokens[b, kids] = rng.choice(vocab, size=len(kids), replace=False)
+                # a node with more children than the vocabulary has letters
+                # draws from a vocabulary just large enough
+                tokens[b, kids] = rng.choice(max(vocab, len(kids) + 1), size=len(kids), replace=False)
         for u in range(q):
             kids = children[u]
             taken = set(int(tokens[b, c]) for c in kids)
             if kids and rng.random() < p_follow:
                 pred[b, u] = tokens[b, kids[int(rng.integers(len(kids)))]]
             else:
-                free = [v for v in range(vocab) if v not in taken]
+                free = [v for v in range(max(vocab, len(kids) + 1)) if v not in taken]
                 pred[b, u] = free[int(rng.integers(len(free)))]
     return tokens, pred
