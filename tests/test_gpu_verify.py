@@ -99,6 +99,35 @@ def test_strided_fused_and_separate_caches():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("layout", [1, 2])
+def test_query_layouts_give_identical_results(layout):
+    """Queries with padded rows (one uniform row stride larger than R) and in a
+    head-major buffer (token stride smaller than the head stride) give the
+    same bits as contiguous queries: the 64-row layout copies uniformly
+    strided query rows through LDS and loads the others directly."""
+    cfg = small_cfg(q=9, H=16, prefix=("uniform", 40, 400), B=3, index=62)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    o1, l1 = run_gpu(g, layout=layout)
+    B, q, H, R, P = cfg.B, cfg.q_len, cfg.H, cfg.R, cfg.P
+    # padded rows: [B, q, H, R + 32] and [B, q, H, P + 16] buffers
+    ql_pad = torch.zeros((B, q, H, R + 32), dtype=g.q_lat.dtype, device=g.q_lat.device)
+    qp_pad = torch.zeros((B, q, H, P + 16), dtype=g.q_pe.dtype, device=g.q_pe.device)
+    ql_pad[..., :R] = g.q_lat
+    qp_pad[..., :P] = g.q_pe
+    q_lat0, q_pe0 = g.q_lat, g.q_pe
+    g.q_lat, g.q_pe = ql_pad[..., :R], qp_pad[..., :P]
+    o2, l2 = run_gpu(g, layout=layout)
+    # head-major buffers viewed as [B, q, H, *]
+    g.q_lat = q_lat0.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    g.q_pe = q_pe0.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    o3, l3 = run_gpu(g, layout=layout)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+    ro, rl = oracle_full(inp)
+    check_close("bf16", o1, ro, l1, rl, f"layout {layout}")
+
+
 # ---------------------------------------------------------------- full-size configurations
 
 def test_config_max_budget_full():

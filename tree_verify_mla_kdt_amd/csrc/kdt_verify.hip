@@ -120,6 +120,7 @@ struct VerifyArgs {
   int32_t* seq_status;
   float scale_log2;
   int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len, layout;
+  int q_rows_uniform;   // query rows m = t * H + h sit at one byte stride (q_lat and q_pe)
 };
 
 // The value of C-layout register v of a 32x32 MFMA result held by a lane in
@@ -335,31 +336,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int t = row_ok ? m / a.H : 0;
   const int h = row_ok ? m - t * a.H : 0;
 
-  // The prefix length is requested first; the query fragments, the
-  // visibility words and (below) the first two key tiles are requested while
-  // it is in flight, so their memory latencies overlap.
-  const int L = a.prefix_lens[b];
-  // The query fragments and visibility words do not depend on it.  Padding rows
-  // (m >= M) load token 0 / head 0: an output column of either contraction
-  // depends only on its own query column, and padding rows are never written,
-  // so no masking is needed.
-  frag qf[NCHUNK];
-  {
-    const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
-    const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
-#pragma unroll
-    for (int c = 0; c < NCHUNK; ++c) {
-      if (c < R / KMF) qf[c] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
-      else qf[c] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
-    }
-  }
-  uint64_t vw0 = ~0ull, vw1 = ~0ull;
-  if (row_ok) {
-    const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
-    vw0 = vr[0];
-    vw1 = a.W > 1 ? vr[1] : 0ull;
-  }
-
+  // Start-up order: the speculative copies of the first two key tiles, so
+  // the key stream starts at once, then the query fragments and visibility
+  // words, then the prefix length (a scalar load: the index is uniform, so
+  // waiting for it waits for no vector load).  All four latencies overlap.
   const int k_begin = split * a.split_keys;
   const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
   const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
@@ -383,6 +363,53 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     stage_rows(0, s_tiles[0], kBN);
     stage_rows(1, s_tiles[1], kBN);
   }
+
+  // The query fragments and visibility words do not depend on the prefix
+  // length.  Padding rows (m >= M) load token 0 / head 0: an output column of
+  // either contraction depends only on its own query column, and padding rows
+  // are never written, so no masking is needed.
+  //
+  // In the 64-row layout (bf16) the workgroup's query rows are copied like
+  // two key tiles, into the two ring buffers the first tiles leave free, and
+  // each wave then reads its fragments with the score operand's LDS pattern:
+  // 1 KB contiguous per copy instead of 32 scattered rows per load.
+  constexpr bool Q_VIA_LDS = (CS == 2) && (KW == 8) && (NBUF == 4);
+  static_assert(!Q_VIA_LDS || BM == 2 * kBN, "query staging: two 32-row blocks per workgroup");
+  const bool q_lds = Q_VIA_LDS && a.q_rows_uniform;
+  frag qf[NCHUNK];
+  if (q_lds) {
+    const uint32_t ql_ss = (uint32_t)(a.q_lat_sh * (int64_t)sizeof(T));
+    const uint32_t qp_ss = (uint32_t)(a.q_pe_sh * (int64_t)sizeof(T));
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int row0 = rt * BM + blk * kBN;
+      const int nr = min(kBN, a.M - row0);    // rows of this block that exist
+      const int base_row = nr > 0 ? row0 : rt * BM;
+      const int nrows = nr > 0 ? nr : 1;
+      const char* ql = reinterpret_cast<const char*>(a.q_lat) +
+                       (b * a.q_lat_sb + (int64_t)base_row * a.q_lat_sh) * (int64_t)sizeof(T);
+      const char* qp = reinterpret_cast<const char*>(a.q_pe) +
+                       (b * a.q_pe_sb + (int64_t)base_row * a.q_pe_sh) * (int64_t)sizeof(T);
+      stage_region<kBN, RC>(make_rsrc(ql, (uint32_t)nrows * ql_ss), ql_ss, nrows, s_tiles[2 + blk], wave, lane);
+      stage_region<kBN, PC>(make_rsrc(qp, (uint32_t)nrows * qp_ss), qp_ss, nrows, s_tiles[2 + blk] + LAT_BYTES,
+                            wave, lane);
+    }
+  } else {
+    const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
+    const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+      if (c < R / KMF) qf[c] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
+      else qf[c] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
+    }
+  }
+  uint64_t vw0 = ~0ull, vw1 = ~0ull;
+  if (row_ok) {
+    const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
+    vw0 = vr[0];
+    vw1 = a.W > 1 ? vr[1] : 0ull;
+  }
+  const int L = ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
 
   const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
   const int N = L + a.q;
@@ -449,6 +476,23 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4) pv_base[half][d4] = base + 64 * ((d4 ^ s2) - d4);
+    }
+  }
+
+  if constexpr (Q_VIA_LDS) {
+    if (q_lds) {
+      // the query copies (and the first tiles, issued before them) have landed
+      wait_vmem_lds<0>();
+      tile_barrier();
+      const char* qbuf = s_tiles[2 + rb];
+#pragma unroll
+      for (int c = 0; c < NCHUNK; ++c) {
+        const char* src = (c < R / KMF) ? qbuf + qk_lat[c % QB] + 16 * LSW * (c / QB) : qbuf + qk_pe[c - R / KMF];
+        qf[c] = *reinterpret_cast<const frag*>(src);
+      }
+      // every wave has its fragments before the buffers take key tiles again
+      wait_vmem_lds<0>();
+      tile_barrier();
     }
   }
 
@@ -877,6 +921,9 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.max_splits = p.max_splits;
   a.split_keys = p.split_keys;
   a.max_prefix_len = d->max_prefix_len;
+  const int64_t es = elem_size(d->dtype);
+  a.q_rows_uniform = d->q_lat_st == (int64_t)d->H * d->q_lat_sh && d->q_pe_st == (int64_t)d->H * d->q_pe_sh &&
+                     d->q_lat_sh * es < (1ll << 26) && d->q_pe_sh * es < (1ll << 26);
   return a;
 }
 
