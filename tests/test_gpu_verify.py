@@ -128,6 +128,37 @@ def test_query_layouts_give_identical_results(layout):
     check_close("bf16", o1, ro, l1, rl, f"layout {layout}")
 
 
+def _growing_scores_inputs(q, H, L, B=2, index=63):
+    """Scores that rise by far more than 2^32 in weight after the first key
+    tiles: q_lat is all ones, c_kv rows are a per-key level plus small noise,
+    with level 0 for the first keys and 3 from key L // 3 on, so the reference
+    a split takes from its first tile is exceeded later and the split is
+    redone against the exact maximum."""
+    cfg = small_cfg(q=q, H=H, prefix=("fixed", L), B=B, index=index)
+    inp = synth.generate(cfg)
+    rng = synth.rng_for(63)
+    R, P = cfg.R, cfg.P
+    S = inp.cache.shape[1]
+    level = np.where(np.arange(S) < L // 3, 0.0, 3.0).astype(np.float32)
+    c = level[None, :, None] + 0.02 * rng.standard_normal((B, S, R + P)).astype(np.float32)
+    c[..., R:] = 0.0
+    inp.cache = synth.f32_to_bf16_bits(c)
+    inp.q_lat = synth.f32_to_bf16_bits(np.ones(inp.q_lat.shape, np.float32))
+    inp.q_pe = synth.f32_to_bf16_bits(np.zeros(inp.q_pe.shape, np.float32))
+    return inp
+
+
+@pytest.mark.parametrize("layout,split_keys", [(1, 0), (2, 0), (1, 256), (2, 256), (2, 64)])
+def test_redo_when_scores_outgrow_the_reference(layout, split_keys):
+    inp = _growing_scores_inputs(q=9, H=16, L=900)
+    g = GpuInputs(inp)
+    o, l = run_gpu(g, split_keys=split_keys, layout=layout)
+    ro, rl = oracle_full(inp)
+    # the weight sits on the level-3 keys: every output is near 3
+    assert np.all(np.abs(ro - 3.0) < 0.1)
+    check_close("bf16", o, ro, l, rl, f"layout {layout} split {split_keys}")
+
+
 # ---------------------------------------------------------------- full-size configurations
 
 def test_config_max_budget_full():

@@ -250,16 +250,21 @@ constexpr int min_wave_loads(int slots) { return (slots / 64) / (kThreads / 64);
 // `wave` must be wave-uniform (an SGPR): the LDS destination and, for regions
 // of 64 chunks per row, the source row are then scalar and each load needs a
 // single per-lane offset register.
+// Wave-loads per wave for a region of ROWS x NCH 16-byte chunks (the maximum
+// over the waves; some waves may issue one fewer).
 template <int ROWS, int NCH>
-__device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, char* lds, int wave, int lane) {
+constexpr int region_wave_loads() { return (ROWS * NCH / 64 + kThreads / 64 - 1) / (kThreads / 64); }
+
+// The jj-th wave-load of this wave for one region (nothing if this wave has
+// fewer).  stage_region issues them all.
+template <int ROWS, int NCH>
+__device__ __forceinline__ void stage_one(i32x4 rs, uint32_t ss, int nrows, char* lds, int wave, int lane, int jj) {
   constexpr int SLOTS = ROWS * NCH;
   static_assert(SLOTS % 64 == 0, "tile region must be whole wave loads");
   constexpr int WAVES = kThreads / 64;
-  constexpr int PER_WAVE = (SLOTS / 64 + WAVES - 1) / WAVES;
-#pragma unroll
-  for (int jj = 0; jj < PER_WAVE; ++jj) {
+  {
     const int j = wave + jj * WAVES;
-    if ((SLOTS / 64) % WAVES != 0 && j >= SLOTS / 64) break;
+    if ((SLOTS / 64) % WAVES != 0 && j >= SLOTS / 64) return;
     uint32_t voff, soff;
     if constexpr (NCH == 64) {
       // one row per instruction: the row (and its swizzle) is wave-uniform
@@ -278,6 +283,12 @@ __device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, c
     dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds_addr(lds + j * 1024)), voff,
                  __builtin_amdgcn_readfirstlane(soff));
   }
+}
+
+template <int ROWS, int NCH>
+__device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, char* lds, int wave, int lane) {
+#pragma unroll
+  for (int jj = 0; jj < region_wave_loads<ROWS, NCH>(); ++jj) stage_one<ROWS, NCH>(rs, ss, nrows, lds, wave, lane, jj);
 }
 
 // CS (column split) = 1: the four waves own 32 rows each, all R output
@@ -435,6 +446,20 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const bool spec_ok = spec && k_begin + 2 * kBN <= k_end;
 
   auto stage = [&](int tile, char* buf) { stage_rows(tile, buf, min(kBN, k_end - (k_begin + tile * kBN))); };
+  // The same copy, one wave-load at a time (pieces 0 .. NPIECE - 1), so that
+  // the copies can be issued between value MFMAs: a wave waiting for the
+  // texture unit to accept a copy then still has MFMAs in flight.
+  constexpr int LAT_PIECES = region_wave_loads<kBN, RC>();
+  constexpr int NPIECE = LAT_PIECES + region_wave_loads<kBN, PC>();
+  auto stage_piece = [&](int tile, int nrows, char* buf, int piece) __attribute__((always_inline)) {
+    const int kt = k_begin + tile * kBN;
+    if (piece < LAT_PIECES)
+      stage_one<kBN, RC>(make_rsrc(kv_lat + (int64_t)kt * lat_ss, (uint32_t)nrows * lat_ss), lat_ss, nrows, buf,
+                         wave, lane, piece);
+    else
+      stage_one<kBN, PC>(make_rsrc(kv_pe + (int64_t)kt * pe_ss, (uint32_t)nrows * pe_ss), pe_ss, nrows,
+                         buf + LAT_BYTES, wave, lane, piece - LAT_PIECES);
+  };
 
 
 
@@ -505,16 +530,20 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // the weights are taken against: fixed at the first tile with a visible key,
   // it never moves while weights stay below 2^kRefSlack, so the accumulators
   // are never rescaled.  m_max is the true running max.  If some row's max
-  // outgrows its reference by more than that, the wave stops accumulating
-  // ("dead"), keeps tracking m_max, and redoes the split once with
-  // m_ref = m_max (the exact max), which cannot trigger again.
+  // outgrows its reference by more than that, the wave's accumulation is void
+  // ("dead"): it keeps running its tiles (the copy schedule is shared by all
+  // waves) and tracking m_max, then redoes the split once with m_ref = m_max
+  // (the exact max), which cannot trigger again, discarding what it summed.
   float m_ref = -INFINITY, m_max = -INFINITY;
   float l_run = 0.0f;           // this lane's share of sum_j exp2(s_j - m_ref)
   bool dead = false;            // wave-uniform
 
-  // One key tile: scores, softmax, value contraction.  `buf` is one of the
-  // two LDS buffers; the tile's first key is kt.
-  auto tile_body = [&](const int tile, const char* buf) __attribute__((always_inline)) {
+  // One key tile: scores, softmax, value contraction.  `buf` is the tile's
+  // ring buffer; the tile's first key is kt.  The copy of the first st_rows
+  // rows of tile st_tile into st_buf is issued piece by piece between the
+  // value MFMAs.
+  auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, char* st_buf)
+                       __attribute__((always_inline)) {
     const int kt = k_begin + tile * kBN;
     if constexpr (STASH) {
 #pragma unroll
@@ -614,7 +643,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         acc[NBL - 1][4 * g + 3] = v[3];
       }
     }
-    if (dead) return;                       // keep tracking m_max only
     const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
     float p[16];
 #pragma unroll
@@ -635,6 +663,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       if (i + VPF < STEPS) vq[(i + VPF) % (VPF + 1)] = value_frag((i + VPF) / NBL, (i + VPF) % NBL);
       acc[db] = MM::mma(vq[i % (VPF + 1)], pfr[c], acc[db]);
       fence_mem_mfma();
+      // copy pieces [i * NPIECE / STEPS, (i + 1) * NPIECE / STEPS) follow this MFMA
+#pragma unroll
+      for (int pc = i * NPIECE / STEPS; pc < (i + 1) * NPIECE / STEPS; ++pc)
+        stage_piece(st_tile, st_rows, st_buf, pc);
     }
   };
 
@@ -656,14 +688,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     const bool compute = (pass == 0) || dead;
     dead = false;
     // Tiles rotate through the NBUF buffers: the step for tile t waits for its
-    // copy (the copies of the following tiles may still run), starts the copy
-    // of tile t + NBUF - 1 into the buffer the previous step has finished
-    // reading, and computes.
-    auto wait_tile = [&](int newer) __attribute__((always_inline)) {
-      // copies of tiles t + 1 .. t + newer may stay in flight
-      if (newer >= 2 && NBUF > 3) wait_vmem_lds<STAGE_LOADS * (NBUF > 3 ? 2 : 1)>();
-      else if (newer >= 1) wait_vmem_lds<STAGE_LOADS>();
-      else wait_vmem_lds<0>();
+    // copy and computes, issuing between its value MFMAs the copy of tile
+    // t + NBUF - 1 into the buffer the previous step has finished reading.
+    // Every step issues exactly one copy: once no tile is left, a dummy copy
+    // (row 0 of tile t, re-read into every row) goes to that buffer, which no
+    // later tile uses.  So exactly NBUF - 2 copies are always younger than the
+    // one a step waits for, and one wait count serves every step.
+    auto wait_tile = [&]() __attribute__((always_inline)) {
+      wait_vmem_lds<STAGE_LOADS * (NBUF - 2)>();
       tile_barrier();
     };
     // The first tile, the query fragments and the visibility words are all
@@ -674,23 +706,30 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     } else {
       wait_vmem_lds<0>();                     // speculative copies land before their buffers are reused
       stage(0, s_tiles[0]);
-      wait_vmem_lds<0>();
       if (n_tiles > 1) stage(1, s_tiles[1]);
+      else stage_rows(0, s_tiles[1], 1);
     }
 #pragma unroll
-    for (int k = 2; k < NBUF - 1; ++k)
+    for (int k = 2; k < NBUF - 1; ++k) {
       if (k < n_tiles) stage(k, s_tiles[k]);
+      else stage_rows(0, s_tiles[k], 1);
+    }
 #pragma unroll 1
     for (int tile = 0; tile < n_tiles; tile += NBUF) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
         const int t = tile + k;
         if (t >= n_tiles) break;
-        wait_tile(min(NBUF - 2, n_tiles - 1 - t));
-        if (t + NBUF - 1 < n_tiles) stage(t + NBUF - 1, s_tiles[(k + NBUF - 1) % NBUF]);
-        if (compute) tile_body(t, s_tiles[k]);
+        wait_tile();
+        const bool real = t + NBUF - 1 < n_tiles;
+        const int st = real ? t + NBUF - 1 : t;
+        const int st_rows = real ? min(kBN, k_end - (k_begin + st * kBN)) : 1;
+        char* sb = s_tiles[(k + NBUF - 1) % NBUF];
+        if (compute) tile_body(t, s_tiles[k], st, st_rows, sb);
+        else stage_rows(st, sb, st_rows);
       }
     }
+    wait_vmem_lds<0>();                       // the last (dummy) copies land before anything else
   }
 
   // ---- epilogue: normalise and write (direct) or write the partial
@@ -735,8 +774,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 // Partials are in accumulator order (32-row blocks; column c of block row r at
 // 256 (c / 8) + 128 ((c / 4) % 2) + 4 r + c % 4), so one wave handles one
 // (sequence, block, 8-column group): every lane reads one float4 per split and
-// the wave's reads are one contiguous 1 KB run.  Splits are consumed eight at a
-// time with a running maximum, so eight loads per lane are in flight.  Splits
+// the wave's reads are one contiguous 1 KB run.  Splits are consumed sixteen
+// at a time with a running maximum, so sixteen loads per lane are in flight
+// (one memory round trip for up to sixteen splits).  Splits
 // with lse_k = -inf are skipped by selection, never by multiplication: their
 // partial output may never have been written.
 template <typename T>
@@ -744,7 +784,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
     int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys,
     T* __restrict__ out, int64_t out_sb, int64_t out_st, int64_t out_sh, float* __restrict__ lse) {
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int n_c8 = R >> 3;
   const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, hh = lane >> 5;
