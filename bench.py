@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="run a plain device copy of MB megabytes --steps times (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--layout", type=int, default=0, help="force a workgroup layout (0: the planner's choice)")
+    ap.add_argument("--split-keys", type=int, default=0, help="force a key split size (0: the planner's choice)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying HIP graphs (for counter runs)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB", "CAL_WRITE_DB"),
@@ -183,7 +185,8 @@ def main():
 
     c0 = copies[0]
     desc, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
-                                     prefix_lens, vis, cfg.softmax_scale, max_prefix, out, lse, None, 0)
+                                     prefix_lens, vis, cfg.softmax_scale, max_prefix, out, lse, None,
+                                     args.split_keys, args.layout)
     plan = kdt.verify_plan(desc)
     ws_bytes = max(int(plan.workspace_bytes), int(plan.part_lse_offset + B * plan.max_splits * plan.rows * 4))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -192,13 +195,15 @@ def main():
         c = copies[i % n_copies]
         kdt.build_visibility(parents, vis=vis, depth=depth)
         kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
-                        cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws)
+                        cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
+                        split_keys=args.split_keys, layout=args.layout)
         kdt.gather_accepted(c["cache"], prefix_lens, accepted, n_acc, q, new_prefix_lens=new_pl)
 
     def split_only(i):
         c = copies[i % n_copies]
         kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
-                            cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws)
+                            cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws,
+                            split_keys=args.split_keys, layout=args.layout)
 
     # Launches are replayed from HIP graphs: one graph runs the step once per
     # input copy, so host launch overhead stays out of the measured step time.
@@ -308,7 +313,7 @@ def main():
         "data": "synthetic (seeded N(0,1) tensors and random trees of the workload's shape)",
         "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": B, "heads": H, "kv_lora_rank": R,
                    "rope_dim": P, "q_len": q, "prefix_len_max": max_prefix,
-                   "split_keys": plan.split_keys, "splits": plan.max_splits,
+                   "split_keys": plan.split_keys, "splits": plan.max_splits, "layout": plan.layout,
                    "step": "build_visibility + verify (split + merge) + gather_accepted",
                    "input_copies": n_copies, "kernel_only": bool(args.kernel_only)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

@@ -40,10 +40,20 @@ __global__ __launch_bounds__(kGatherThreads) void gather_accepted_kernel(
   const int vec = slice * kSliceVecs + (tid % kSliceVecs);
   const int r0 = tid / kSliceVecs;
 
+  const int32_t* acc = accepted + (int64_t)b * max_acc;
+  const int n_max = max_acc < q ? max_acc : q;
+  // The accepted indices are requested together with the prefix length and
+  // the path length (every entry below max_acc is inside the caller's array),
+  // so the source rows are one memory round trip away instead of two.
+  int src_of[kMaxRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kMaxRowsPerThread; ++k) {
+    const int row = r0 + k * kRowsPerPass;
+    src_of[k] = row < n_max ? acc[row] : -1;
+  }
   const int L = prefix_lens[b];
   int n = n_accepted[b];
   const bool first = (layer == 0 && slice == 0 && tid == 0);
-  const int n_max = max_acc < q ? max_acc : q;
   if (L < 0 || (int64_t)L + q > capacity) {
     if (first) flag_seq(seq_status, b, KDT_SEQ_BAD_LEN);
     return;
@@ -55,7 +65,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_accepted_kernel(
   if (first && new_prefix_lens) new_prefix_lens[b] = L + n;
 
   char* base = cache + layer * layer_stride + b * cache_sb + (int64_t)L * cache_ss;
-  const int32_t* acc = accepted + (int64_t)b * max_acc;
 
   V buf[kMaxRowsPerThread];
   bool take[kMaxRowsPerThread];
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_accepted_kernel(
     const int row = r0 + k * kRowsPerPass;
     take[k] = false;
     if (row < n && vec < row_vecs) {
-      const int src = acc[row];
+      const int src = src_of[k];
       if (src >= 0 && src < q) {
         buf[k] = *reinterpret_cast<const V*>(base + (int64_t)src * cache_ss + (int64_t)vec * sizeof(V));
         take[k] = true;
