@@ -44,6 +44,13 @@ What is computed, and where it comes from:
     at the current node, while one exists; the prediction at the last
     accepted node is the bonus token.  Walks are bounded by the tree size,
     the safety bound of [Milestone, "Mistakes and Incorrect Assumptions"].
+  * Best-first tree build: the draft tree is built best-first from the
+    drafter's top-k candidates per draft position, with a heap, accumulating
+    log-probabilities in double precision; it yields the parent pointers
+    (which the visibility consumes) and a first-child / next-sibling encoding
+    whose sibling lists run in order of log-probability [Milestone, "The
+    Context: Why This Commit Exists", "The Reasoning Behind the Architecture";
+    Final, "Input Knowledge Required", best-first from top-k logits].
 
 Readings where the pages are silent (each also listed in the design notes):
   * Tree node t's latents sit in cache row L_b + t (node order); its position
@@ -56,6 +63,18 @@ Readings where the pages are silent (each also listed in the design notes):
     lowest-index child (the earliest in best-first order) is taken; the
     accepted list starts with the root (node 0), so it feeds the gather
     directly.
+  * Tree build: the drafter gives, for each draft position d = 1..D, its K
+    best tokens with log-probabilities sorted best first (one list per
+    position, shared by every node at depth d - 1: a block drafter predicts
+    positions, not paths).  The root (node 0, the verified token) has logw 0;
+    the child of rank j of a node at depth d - 1 has logw = logw(node) +
+    logprob[d][j].  Nodes are created in order of decreasing logw until the
+    budget of q nodes is reached or no candidate is left; a node's children
+    are offered lazily (a popped candidate offers its next sibling, then its
+    own first child), which creates the same nodes in the same order as
+    offering all K children at once.  Equal logw: the earlier offered
+    candidate wins.  Budget slots left over are padding: a child of the root
+    with token -1 (no prediction matches it), depth 1, logw -inf.
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, brute force, library routines or invariants; none is "parity unpinned".
@@ -311,3 +330,75 @@ def tree_accept(parents, tokens, target_pred):
         n_acc[b] = len(path)
         bonus[b] = target_pred[b, u]
     return accepted, n_acc, bonus
+
+
+# ----------------------------------------------------------------------------
+# Best-first tree build  [Milestone, "The Context: Why This Commit Exists",
+# "The Reasoning Behind the Architecture"; Final, "Input Knowledge Required"]
+# ----------------------------------------------------------------------------
+
+def build_tree(topk_tokens, topk_logprobs, root_tokens, q):
+    """Best-first draft tree from per-position top-k candidates.
+
+    topk_tokens   int [B, D, K]    K best draft tokens of each draft position
+    topk_logprobs float [B, D, K]  their log-probabilities, best first
+    root_tokens   int [B]          the verified token (node 0)
+    q             nodes per tree (budget), 1 <= q
+
+    Returns a dict of arrays (int32 unless noted):
+      parents [B, q], tokens [B, q], depth [B, q], logw float64 [B, q],
+      first_child [B, q], next_sibling [B, q] (-1: none), n_nodes [B]
+    Nodes past n_nodes are padding (parent 0, token -1, depth 1, logw -inf,
+    no links).
+    """
+    import heapq
+    topk_tokens = np.asarray(topk_tokens)
+    lp = np.asarray(topk_logprobs)
+    B, D, K = topk_tokens.shape
+    out = {
+        "parents": np.zeros((B, q), np.int32), "tokens": np.full((B, q), -1, np.int32),
+        "depth": np.ones((B, q), np.int32), "logw": np.full((B, q), -np.inf),
+        "first_child": np.full((B, q), -1, np.int32), "next_sibling": np.full((B, q), -1, np.int32),
+        "n_nodes": np.zeros(B, np.int32),
+    }
+    for b in range(B):
+        parents = [-1]
+        depth = [0]
+        logw = [0.0]
+        tokens = [int(root_tokens[b])]
+        last_child = {}
+        heap = []            # (-logw, order offered, depth, rank, parent node)
+        order = 0
+
+        def offer(w, d, j, par):
+            nonlocal order
+            heapq.heappush(heap, (-w, order, d, j, par))
+            order += 1
+
+        if D >= 1 and K >= 1:
+            offer(0.0 + float(lp[b, 0, 0]), 1, 0, 0)
+        while len(parents) < q and heap:
+            negw, _, d, j, par = heapq.heappop(heap)
+            node = len(parents)
+            parents.append(par)
+            depth.append(d)
+            logw.append(-negw)
+            tokens.append(int(topk_tokens[b, d - 1, j]))
+            if par in last_child:
+                out["next_sibling"][b, last_child[par]] = node
+            else:
+                out["first_child"][b, par] = node
+            last_child[par] = node
+            if j + 1 < K:                                  # next sibling of this candidate
+                offer(logw[par] + float(lp[b, d - 1, j + 1]), d, j + 1, par)
+            if d < D:                                      # first child of the new node
+                offer(logw[node] + float(lp[b, d, 0]), d + 1, 0, node)
+        n = len(parents)
+        out["n_nodes"][b] = n
+        out["parents"][b, :n] = parents
+        out["parents"][b, 0] = -1
+        out["tokens"][b, :n] = tokens
+        out["depth"][b, :n] = depth
+        out["depth"][b, 0] = 0
+        out["logw"][b, :n] = logw
+    return out

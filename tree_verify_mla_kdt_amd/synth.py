@@ -344,3 +344,22 @@ def accept_inputs(parents: np.ndarray, seed: int, vocab: int = 32, p_follow: flo
                 free = [v for v in range(max(vocab, len(kids) + 1)) if v not in taken]
                 pred[b, u] = free[int(rng.integers(len(free)))]
     return tokens, pred
+
+
+def tree_topk_inputs(B: int, D: int, K: int, seed: int, vocab: int = 1000, temp: float = 1.0):
+    """Drafter output for the best-first tree build (random draws only): for
+    each of B requests and D draft positions, the K most likely tokens of a
+    softmax over `vocab` random logits (N(0, 1) / temp), with their float32
+    log-probabilities sorted best first, plus a verified root token.
+
+    Returns (topk_tokens int32 [B, D, K], topk_logprobs float32 [B, D, K],
+    root_tokens int32 [B])."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 3000 + int(seed)))
+    logits = rng.standard_normal((B, D, vocab)) / temp
+    logits -= logits.max(axis=-1, keepdims=True)
+    logp = logits - np.log(np.exp(logits).sum(axis=-1, keepdims=True))
+    order = np.argsort(-logp, axis=-1, kind="stable")[..., :K]
+    tokens = order.astype(np.int32)
+    lps = np.take_along_axis(logp, order, axis=-1).astype(np.float32)
+    roots = rng.integers(0, vocab, size=B).astype(np.int32)
+    return tokens, lps, roots
