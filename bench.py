@@ -281,6 +281,19 @@ def main():
     torch.cuda.synchronize()
     accept_us = e0.elapsed_time(e1) * 1e3 / 200
 
+    # --- best-first tree build for the same batch and budget, from a drafter
+    # shape of 16 draft positions x 8 candidates (timed on its own)
+    tb_tok, tb_lp, tb_root = synth.tree_topk_inputs(B, 16, 8, 0)
+    tb_tok, tb_lp, tb_root = (torch.from_numpy(x).to(dev) for x in (tb_tok, tb_lp, tb_root))
+    g_tb = capture(lambda i: kdt.build_tree(tb_tok, tb_lp, tb_root, q), range(20))
+    g_tb.replay()
+    e0.record(cur)
+    for _ in range(10):
+        g_tb.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    tree_build_us = e0.elapsed_time(e1) * 1e3 / 200
+
     pairs = visible_pairs(inp.parents, inp.prefix_lens, H)
     flops = pairs * 2 * (R + P + R)                       # score over R+P, value over R
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -325,6 +338,7 @@ def main():
         "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg_bytes,
         "tree_accept_us": accept_us,
+        "tree_build_us": tree_build_us,
     }
 
     if not args.no_cpu and not args.kernel_only:

@@ -257,6 +257,43 @@ int kdt_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t
                     int32_t B, int32_t q_len, int32_t* accepted, int32_t* n_accepted,
                     int32_t* bonus, int32_t* seq_status, void* stream);
 
+/* ------------------------------------------------------------------------
+ * kdt_build_tree — best-first draft tree from the drafter's top-k lists.
+ * [Milestone, "The Context: Why This Commit Exists"]: the tree was built on
+ * the host with a heap (a device-host round trip per decode step); here it is
+ * built on the device.  [Milestone, "The Reasoning Behind the Architecture"]:
+ * one work unit per request, double-precision logw, first-child /
+ * next-sibling links sorted by log-probability.  [Final, "Input Knowledge
+ * Required"]: best-first from top-k logits.
+ *
+ * For draft position d = 1..D the drafter gives its K best tokens with
+ * log-probabilities, best first; every node at depth d - 1 has those K tokens
+ * as candidate children.  The root (node 0) is the verified token with logw
+ * 0; a child of rank j has logw = logw(parent) + logprob[d][j] (double).
+ * Nodes are created in order of decreasing logw (equal logw: the candidate
+ * offered first, candidates being offered lazily: a created node offers its
+ * parent's next-ranked child, then its own best child) until q_len nodes exist
+ * or no candidate remains.  Budget slots left over are padding: parent 0,
+ * token -1, depth 1, logw -inf, no links.
+ *   topk_tokens    int32 [B, D, K]   (read only)
+ *   topk_logprobs  float [B, D, K]   sorted best first per position (read only)
+ *   root_tokens    int32 [B]         the verified token of each request
+ *   parents        int32 [B, q_len]  out: -1 for the root, else an earlier node
+ *                                    (valid input for kdt_build_visibility)
+ *   tokens         int32 [B, q_len]  out: draft token of each node (root: root_tokens)
+ *   depth          int32 [B, q_len]  out
+ *   logw           double [B, q_len] out, nullable
+ *   first_child, next_sibling  int32 [B, q_len]  out, nullable (-1: none)
+ *   n_nodes        int32 [B]         out, nullable: created nodes (<= q_len)
+ * Supported: 1 <= q_len <= KDT_MAX_Q_LEN; D, K >= 1; K <= 64 unless q_len <= 64.
+ * The result is exact (the same double additions and comparisons in the same
+ * order as the definition).
+ * ---------------------------------------------------------------------- */
+int kdt_build_tree(const int32_t* topk_tokens, const float* topk_logprobs, const int32_t* root_tokens,
+                   int32_t B, int32_t D, int32_t K, int32_t q_len, int32_t* parents, int32_t* tokens,
+                   int32_t* depth, double* logw, int32_t* first_child, int32_t* next_sibling,
+                   int32_t* n_nodes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

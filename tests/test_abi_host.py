@@ -109,7 +109,7 @@ def test_verify_needs_workspace_when_split():
     assert rc == 3
 
 
-def test_visibility_gather_and_accept_argument_checks():
+def test_visibility_gather_accept_and_tree_argument_checks():
     L = kdt.lib()
     assert L.kdt_build_visibility(None, 1, 9, FAKE, None, None, None) == 1
     assert L.kdt_build_visibility(FAKE, 0, 9, FAKE, None, None, None) == 1
@@ -132,6 +132,14 @@ def test_visibility_gather_and_accept_argument_checks():
     assert a(FAKE, FAKE, FAKE, 0, 9, FAKE, FAKE, None, None, None) == 1
     assert a(FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, None, None, None) == 1
     assert a(FAKE, FAKE, FAKE, 1, 129, FAKE, FAKE, None, None, None) == 2
+    t = L.kdt_build_tree
+    # topk_tokens, topk_logprobs, roots, B, D, K, q, parents, tokens, depth, logw, first, next, n, stream
+    assert t(None, FAKE, FAKE, 1, 4, 4, 9, FAKE, FAKE, FAKE, None, None, None, None, None) == 1
+    assert t(FAKE, FAKE, FAKE, 1, 4, 4, 9, FAKE, None, FAKE, None, None, None, None, None) == 1
+    assert t(FAKE, FAKE, FAKE, 1, 0, 4, 9, FAKE, FAKE, FAKE, None, None, None, None, None) == 1
+    assert t(FAKE, FAKE, FAKE, 1, 4, 0, 9, FAKE, FAKE, FAKE, None, None, None, None, None) == 1
+    assert t(FAKE, FAKE, FAKE, 1, 4, 4, 129, FAKE, FAKE, FAKE, None, None, None, None, None) == 2
+    assert t(FAKE, FAKE, FAKE, 1, 4, 65, 65, FAKE, FAKE, FAKE, None, None, None, None, None) == 2
 
 
 def test_auto_split_counts_follow_the_launch_model():

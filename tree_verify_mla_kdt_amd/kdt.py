@@ -77,8 +77,10 @@ def lib() -> ctypes.CDLL:
         L.kdt_gather_accepted.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
                                           _c_i64, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p]
         L.kdt_tree_accept.argtypes = [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p]
+        L.kdt_build_tree.argtypes = [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p,
+                                     _c_p, _c_p, _c_p, _c_p]
         for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_partials",
-                   "kdt_merge_partials", "kdt_gather_accepted", "kdt_tree_accept"):
+                   "kdt_merge_partials", "kdt_gather_accepted", "kdt_tree_accept", "kdt_build_tree"):
             getattr(L, fn).restype = ctypes.c_int
         if L.kdt_abi_version() != ABI_VERSION:
             raise RuntimeError("libkdt.so ABI version mismatch")
@@ -297,6 +299,31 @@ def tree_accept(parents, tokens, target_pred, accepted=None, n_accepted=None, bo
         _ptr(parents), _ptr(tokens), _ptr(target_pred), B, q, _ptr(accepted), _ptr(n_accepted), _ptr(bonus),
         _ptr(seq_status), _stream(stream)))
     return accepted, n_accepted, bonus
+
+
+def build_tree(topk_tokens, topk_logprobs, root_tokens, q_len, with_links=True, stream=None):
+    """Best-first draft tree: int32 [B, D, K] tokens, float32 [B, D, K]
+    log-probabilities (best first), int32 [B] root tokens -> dict of device
+    tensors parents / tokens / depth (int32 [B, q]), logw (float64 [B, q]),
+    first_child / next_sibling (int32 [B, q], if with_links), n_nodes (int32 [B])."""
+    assert topk_tokens.dtype == torch.int32 and topk_logprobs.dtype == torch.float32
+    assert root_tokens.dtype == torch.int32
+    for t in (topk_tokens, topk_logprobs, root_tokens):
+        assert t.is_contiguous()
+    B, D, K = topk_tokens.shape
+    assert topk_logprobs.shape == (B, D, K) and root_tokens.shape == (B,)
+    dev = topk_tokens.device
+    out = {k: torch.empty((B, q_len), dtype=torch.int32, device=dev) for k in ("parents", "tokens", "depth")}
+    out["logw"] = torch.empty((B, q_len), dtype=torch.float64, device=dev)
+    if with_links:
+        out["first_child"] = torch.empty((B, q_len), dtype=torch.int32, device=dev)
+        out["next_sibling"] = torch.empty((B, q_len), dtype=torch.int32, device=dev)
+    out["n_nodes"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("kdt_build_tree", lib().kdt_build_tree(
+        _ptr(topk_tokens), _ptr(topk_logprobs), _ptr(root_tokens), B, D, K, int(q_len), _ptr(out["parents"]),
+        _ptr(out["tokens"]), _ptr(out["depth"]), _ptr(out["logw"]), _ptr(out.get("first_child")),
+        _ptr(out.get("next_sibling")), _ptr(out["n_nodes"]), _stream(stream)))
+    return out
 
 
 def softmax_scale_for(R: int, P: int) -> float:
