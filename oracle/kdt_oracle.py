@@ -52,6 +52,16 @@ What is computed, and where it comes from:
     Context: Why This Commit Exists", "The Reasoning Behind the Architecture";
     Final, "Input Knowledge Required", best-first from top-k logits].
 
+  * Around the verify: the query projection of a tree token is split into
+    its non-positional part and its rotary part (split_q); the first is
+    absorbed into the latent space with the per-head key up-projection w_kc
+    (absorb_qk), the second gets NeoX rotary embedding at position L + depth;
+    the tree tokens' latents and rotary keys are appended to the cache at
+    rows L + t (the key again rotated at L + depth); after the verify the
+    latent output is mapped back per head with w_vc (absorb_vc)
+    [Checkpoint, "The Message": split_q, absorb_qk/vc, rope, cache append,
+    positions L + depth; Final, "Input Knowledge Required", absorb form].
+
 Readings where the pages are silent (each also listed in the design notes):
   * Tree node t's latents sit in cache row L_b + t (node order); its position
     L_b + depth(t) only matters to RoPE, which happens upstream.
@@ -75,6 +85,12 @@ Readings where the pages are silent (each also listed in the design notes):
     offering all K children at once.  Equal logw: the earlier offered
     candidate wins.  Budget slots left over are padding: a child of the root
     with token -1 (no prediction matches it), depth 1, logw -inf.
+  * Rotary embedding (NeoX form): for i < P/2 the pair (x[i], x[i + P/2]) is
+    rotated by pos * theta^(-2i/P); theta is a parameter (the pages name
+    YaRN for the real model as a later swap, so plain NeoX is built here).
+  * Weight layouts: w_kc is given transposed per head, [H, R, dn] (row r
+    holds the dn weights of latent r), and w_vc as [H, dv, R]; then both
+    absorbs read each weight row contiguously along the contraction.
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, brute force, library routines or invariants; none is "parity unpinned".
@@ -402,3 +418,62 @@ def build_tree(topk_tokens, topk_logprobs, root_tokens, q):
         out["depth"][b, 0] = 0
         out["logw"][b, :n] = logw
     return out
+
+
+# ----------------------------------------------------------------------------
+# Around the verify: split_q + absorb_qk + RoPE, cache append, absorb_vc
+# [Checkpoint, "The Message"; Final, "Input Knowledge Required"]
+# ----------------------------------------------------------------------------
+
+def rope_neox(x, pos, theta):
+    """NeoX rotary embedding of x [..., P] at integer positions pos [...]:
+    the pair (x[i], x[i + P/2]) turns by pos * theta^(-2i/P)."""
+    x = np.asarray(x, dtype=np.float64)
+    P = x.shape[-1]
+    half = P // 2
+    inv = np.asarray(theta, dtype=np.float64) ** (-(2.0 * np.arange(half)) / P)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def tree_positions(prefix_lens, depth):
+    """Position of tree node t of sequence b: L_b + depth(t)."""
+    return np.asarray(prefix_lens, np.int64)[:, None] + np.asarray(depth, np.int64)
+
+
+def absorb_q(q, w_kc_t, prefix_lens, depth, dn, theta):
+    """q [B, T, H, dn + P] -> (q_lat [B, T, H, R], q_pe [B, T, H, P]):
+    q_lat[b, t, h, r] = sum_i q[b, t, h, i] * w_kc_t[h, r, i] (i < dn) and
+    q_pe = rope(q[..., dn:], L_b + depth[b, t])."""
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w_kc_t, dtype=np.float64)
+    q_nope, q_rope = q[..., :dn], q[..., dn:]
+    q_lat = np.einsum("bthi,hri->bthr", q_nope, w)
+    pos = tree_positions(prefix_lens, depth)
+    q_pe = rope_neox(q_rope, pos[:, :, None], theta)
+    return q_lat, q_pe
+
+
+def absorb_o(o_lat, w_vc):
+    """o_lat [B, T, H, R] -> o [B, T, H, dv]: o[b, t, h, j] = sum_r w_vc[h, j, r] o_lat[b, t, h, r]."""
+    return np.einsum("bthr,hjr->bthj", np.asarray(o_lat, np.float64), np.asarray(w_vc, np.float64))
+
+
+def append_tree_kv(cache, c_kv_new, k_rope_new, prefix_lens, depth, theta):
+    """Cache append of the tree tokens: row L_b + t of sequence b gets the
+    token's latent c_kv_new[b, t] and its rotary key rotated at L_b +
+    depth[b, t].  cache [B, S, R + P] (returned as a new float64 array)."""
+    new = np.array(cache, dtype=np.float64, copy=True)
+    c = np.asarray(c_kv_new, np.float64)
+    k = np.asarray(k_rope_new, np.float64)
+    R = c.shape[-1]
+    pos = tree_positions(prefix_lens, depth)
+    kr = rope_neox(k, pos, theta)
+    for b in range(new.shape[0]):
+        L = int(prefix_lens[b])
+        T = c.shape[1]
+        new[b, L:L + T, :R] = c[b]
+        new[b, L:L + T, R:] = kr[b]
+    return new

@@ -363,3 +363,22 @@ def tree_topk_inputs(B: int, D: int, K: int, seed: int, vocab: int = 1000, temp:
     lps = np.take_along_axis(logp, order, axis=-1).astype(np.float32)
     roots = rng.integers(0, vocab, size=B).astype(np.int32)
     return tokens, lps, roots
+
+
+def absorb_inputs(B: int, T: int, H: int, dn: int, P: int, R: int, dv: int, seed: int):
+    """Inputs of the steps around the verify (random draws only), all bf16 bit
+    patterns: the per-head query projection q [B, T, H, dn + P] (N(0, 1)),
+    the absorbed key weights w_kc_t [H, R, dn] (N(0, 1/dn)), the value
+    weights w_vc [H, dv, R] (N(0, 1/R)), a latent attention output
+    o_lat [B, T, H, R], and the tree tokens' new latents c_kv_new [B, T, R]
+    and rotary keys k_rope_new [B, T, P] (N(0, 1))."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 4000 + int(seed)))
+    f = lambda shape, sd: f32_to_bf16_bits((rng.standard_normal(shape) * sd).astype(np.float32))
+    return {
+        "q": f((B, T, H, dn + P), 1.0),
+        "w_kc_t": f((H, R, dn), dn ** -0.5),
+        "w_vc": f((H, dv, R), R ** -0.5),
+        "o_lat": f((B, T, H, R), 1.0),
+        "c_kv_new": f((B, T, R), 1.0),
+        "k_rope_new": f((B, T, P), 1.0),
+    }
