@@ -294,6 +294,48 @@ int kdt_build_tree(const int32_t* topk_tokens, const float* topk_logprobs, const
                    int32_t* depth, double* logw, int32_t* first_child, int32_t* next_sibling,
                    int32_t* n_nodes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The steps on either side of the verify [Checkpoint, "The Message": split_q,
+ * absorb_qk / absorb_vc, rope, cache append, positions L + depth; Final,
+ * "Input Knowledge Required": absorb form].  bf16 in and out, fp32 (rotary
+ * angles: fp64) inside.  Positions: node t of sequence b sits at
+ * prefix_lens[b] + depth[b, t] (depth int32 [B, T], e.g. from
+ * kdt_build_visibility or kdt_build_tree).  NeoX rotary embedding: for
+ * i < P/2 the pair (x[i], x[i + P/2]) turns by pos * rope_theta^(-2i/P).
+ *
+ * kdt_absorb_q: q [B, T, H, dn + P] (element strides q_sb, q_st, q_sh, each a
+ *   multiple of 8; innermost contiguous) is split per head into its first dn
+ *   values and its last P values;
+ *     q_lat[b, t, h, r] = sum_i w_kc_t[h, r, i] * q[b, t, h, i]   (i < dn)
+ *     q_pe[b, t, h, :]  = rope(q[b, t, h, dn:], pos(b, t))
+ *   w_kc_t [H, R, dn] contiguous (the key up-projection of each head,
+ *   transposed); q_lat [B, T, H, R] and q_pe [B, T, H, P] contiguous outputs
+ *   (the verify's query inputs).  Supported: dtype KDT_BF16, dn in {32, 64,
+ *   128, 256, 512}, R a multiple of 32 * (4, 4, 4, 2, 1) respectively, P even,
+ *   16-byte aligned q, w_kc_t, q_lat.
+ * kdt_absorb_o: o[b, t, h, j] = sum_r w_vc[h, j, r] * o_lat[b, t, h, r];
+ *   o_lat [B, T, H, R], w_vc [H, dv, R], o [B, T, H, dv], all contiguous and
+ *   16-byte aligned.  Supported: R in {32, 64, 128, 256, 512}, dv a multiple
+ *   of 32 * (4, 4, 4, 2, 1) respectively.
+ * kdt_append_tree_kv: cache row prefix_lens[b] + t of sequence b (cache
+ *   [B, capacity, >= R + P], element strides cache_sb, cache_ss) gets
+ *   [c_kv_new[b, t] (R) | rope(k_rope_new[b, t], pos(b, t)) (P)];
+ *   c_kv_new [B, T, R], k_rope_new [B, T, P] contiguous.  A sequence with
+ *   prefix_lens[b] + T > capacity (or < 0) is skipped and flagged
+ *   KDT_SEQ_BAD_LEN in seq_status (nullable).
+ * All three are asynchronous on `stream` and keep no pointer.
+ * ---------------------------------------------------------------------- */
+int kdt_absorb_q(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t dn, int32_t P, int32_t R,
+                 const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh, const void* w_kc_t,
+                 const int32_t* prefix_lens, const int32_t* depth, float rope_theta, void* q_lat,
+                 void* q_pe, void* stream);
+int kdt_absorb_o(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t R, int32_t dv,
+                 const void* o_lat, const void* w_vc, void* o, void* stream);
+int kdt_append_tree_kv(int32_t dtype, int32_t B, int32_t T, int32_t R, int32_t P, const void* c_kv_new,
+                       const void* k_rope_new, const int32_t* prefix_lens, const int32_t* depth,
+                       float rope_theta, void* cache, int64_t cache_sb, int64_t cache_ss,
+                       int64_t capacity, int32_t* seq_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

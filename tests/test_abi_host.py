@@ -140,6 +140,19 @@ def test_visibility_gather_accept_and_tree_argument_checks():
     assert t(FAKE, FAKE, FAKE, 1, 4, 0, 9, FAKE, FAKE, FAKE, None, None, None, None, None) == 1
     assert t(FAKE, FAKE, FAKE, 1, 4, 4, 129, FAKE, FAKE, FAKE, None, None, None, None, None) == 2
     assert t(FAKE, FAKE, FAKE, 1, 4, 65, 65, FAKE, FAKE, FAKE, None, None, None, None, None) == 2
+    aq = L.kdt_absorb_q
+    # dtype, B, T, H, dn, P, R, q, sb, st, sh, w, pl, depth, theta, q_lat, q_pe, stream
+    assert aq(1, 1, 9, 16, 128, 64, 512, None, 0, 0, 0, FAKE, FAKE, FAKE, 1e4, FAKE, FAKE, None) == 1
+    assert aq(1, 1, 9, 16, 128, 64, 512, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, 0.5, FAKE, FAKE, None) == 1
+    assert aq(0, 1, 9, 16, 128, 64, 512, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, 1e4, FAKE, FAKE, None) == 2  # fp32
+    assert aq(1, 1, 9, 16, 128, 63, 512, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, 1e4, FAKE, FAKE, None) == 2  # odd P
+    assert aq(1, 1, 9, 16, 128, 64, 512, FAKE, 3, 0, 0, FAKE, FAKE, FAKE, 1e4, FAKE, FAKE, None) == 2  # stride
+    ao = L.kdt_absorb_o
+    assert ao(1, 1, 9, 16, 512, 128, None, FAKE, FAKE, None) == 1
+    assert ao(1, 1, 9, 16, 512, 128, FAKE + 2, FAKE, FAKE, None) == 2                            # alignment
+    ap = L.kdt_append_tree_kv
+    assert ap(1, 1, 9, 512, 64, FAKE, FAKE, FAKE, FAKE, 1e4, None, 0, 576, 64, None, None) == 1
+    assert ap(1, 1, 9, 512, 64, FAKE, FAKE, FAKE, FAKE, 1e4, FAKE, 0, 500, 64, None, None) == 1   # row too short
 
 
 def test_auto_split_counts_follow_the_launch_model():

@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkdt.so")
-SOURCES = ["kdt_abi.hip", "kdt_visibility.hip", "kdt_verify.hip", "kdt_gather.hip", "kdt_accept.hip", "kdt_tree_build.hip"]
+SOURCES = ["kdt_abi.hip", "kdt_visibility.hip", "kdt_verify.hip", "kdt_gather.hip", "kdt_accept.hip", "kdt_tree_build.hip",
+           "kdt_absorb.hip"]
 ARCH = "gfx950"
 
 

@@ -79,8 +79,14 @@ def lib() -> ctypes.CDLL:
         L.kdt_tree_accept.argtypes = [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p]
         L.kdt_build_tree.argtypes = [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p,
                                      _c_p, _c_p, _c_p, _c_p]
+        L.kdt_absorb_q.argtypes = [_c_i32] * 7 + [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_float,
+                                                  _c_p, _c_p, _c_p]
+        L.kdt_absorb_o.argtypes = [_c_i32] * 6 + [_c_p, _c_p, _c_p, _c_p]
+        L.kdt_append_tree_kv.argtypes = [_c_i32] * 5 + [_c_p, _c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_i64, _c_i64,
+                                                        _c_i64, _c_p, _c_p]
         for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_partials",
-                   "kdt_merge_partials", "kdt_gather_accepted", "kdt_tree_accept", "kdt_build_tree"):
+                   "kdt_merge_partials", "kdt_gather_accepted", "kdt_tree_accept", "kdt_build_tree",
+                   "kdt_absorb_q", "kdt_absorb_o", "kdt_append_tree_kv"):
             getattr(L, fn).restype = ctypes.c_int
         if L.kdt_abi_version() != ABI_VERSION:
             raise RuntimeError("libkdt.so ABI version mismatch")
@@ -324,6 +330,50 @@ def build_tree(topk_tokens, topk_logprobs, root_tokens, q_len, with_links=True, 
         _ptr(out["tokens"]), _ptr(out["depth"]), _ptr(out["logw"]), _ptr(out.get("first_child")),
         _ptr(out.get("next_sibling")), _ptr(out["n_nodes"]), _stream(stream)))
     return out
+
+
+def absorb_q(q, w_kc_t, prefix_lens, depth, dn, rope_theta, q_lat=None, q_pe=None, stream=None):
+    """Query split + key absorb + rotary embedding at L + depth.
+    q bf16 [B, T, H, dn + P] (innermost contiguous), w_kc_t bf16 [H, R, dn],
+    prefix_lens int32 [B], depth int32 [B, T] -> (q_lat [B, T, H, R], q_pe [B, T, H, P])."""
+    assert q.dtype == torch.bfloat16 and w_kc_t.dtype == torch.bfloat16 and w_kc_t.is_contiguous()
+    assert q.stride(-1) == 1 and depth.dtype == torch.int32 and depth.is_contiguous()
+    B, T, H, E = q.shape
+    P = E - dn
+    R = w_kc_t.shape[1]
+    if q_lat is None:
+        q_lat = torch.empty((B, T, H, R), dtype=torch.bfloat16, device=q.device)
+    if q_pe is None:
+        q_pe = torch.empty((B, T, H, P), dtype=torch.bfloat16, device=q.device)
+    sb, st, sh = q.stride()[:3]
+    _check("kdt_absorb_q", lib().kdt_absorb_q(
+        KDT_BF16, B, T, H, int(dn), P, R, _ptr(q), sb, st, sh, _ptr(w_kc_t), _ptr(prefix_lens), _ptr(depth),
+        float(rope_theta), _ptr(q_lat), _ptr(q_pe), _stream(stream)))
+    return q_lat, q_pe
+
+
+def absorb_o(o_lat, w_vc, o=None, stream=None):
+    """Value absorb: o_lat bf16 [B, T, H, R], w_vc bf16 [H, dv, R] -> o [B, T, H, dv]."""
+    assert o_lat.dtype == torch.bfloat16 and o_lat.is_contiguous() and w_vc.is_contiguous()
+    B, T, H, R = o_lat.shape
+    dv = w_vc.shape[1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=o_lat.device)
+    _check("kdt_absorb_o", lib().kdt_absorb_o(KDT_BF16, B, T, H, R, dv, _ptr(o_lat), _ptr(w_vc), _ptr(o),
+                                              _stream(stream)))
+    return o
+
+
+def append_tree_kv(cache, c_kv_new, k_rope_new, prefix_lens, depth, rope_theta, seq_status=None, stream=None):
+    """Cache append of the tree tokens into cache [B, S, R + P] (in place)."""
+    assert cache.dtype == torch.bfloat16 and c_kv_new.is_contiguous() and k_rope_new.is_contiguous()
+    B, T, R = c_kv_new.shape
+    P = k_rope_new.shape[-1]
+    sb, ss = cache.stride()[:2]
+    _check("kdt_append_tree_kv", lib().kdt_append_tree_kv(
+        KDT_BF16, B, T, R, P, _ptr(c_kv_new), _ptr(k_rope_new), _ptr(prefix_lens), _ptr(depth),
+        float(rope_theta), _ptr(cache), sb, ss, cache.shape[1], _ptr(seq_status), _stream(stream)))
+    return cache
 
 
 def softmax_scale_for(R: int, P: int) -> float:
