@@ -294,6 +294,35 @@ def main():
     torch.cuda.synchronize()
     tree_build_us = e0.elapsed_time(e1) * 1e3 / 200
 
+    # --- the steps around the verify for the same batch (dn = dv = 128, the
+    # MLA head dims of the model family): absorb_q + RoPE, cache append,
+    # absorb_o, each timed on its own
+    ab = synth.absorb_inputs(B, q, H, 128, P, R, 128, 0)
+    ab = {k: torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16) for k, v in ab.items()}
+    ab_depth = depth.clone()
+    ab_qlat = torch.empty((B, q, H, R), dtype=torch.bfloat16, device=dev)
+    ab_qpe = torch.empty((B, q, H, P), dtype=torch.bfloat16, device=dev)
+    ab_o = torch.empty((B, q, H, 128), dtype=torch.bfloat16, device=dev)
+    ab_cache = copies[0]["cache"]
+
+    def time_graph(fn):
+        g = capture(lambda i: fn(), range(20))
+        g.replay()
+        e0.record(cur)
+        for _ in range(10):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / 200
+
+    around_us = {
+        "absorb_q": time_graph(lambda: kdt.absorb_q(ab["q"], ab["w_kc_t"], prefix_lens, ab_depth, 128, 50000.0,
+                                                    q_lat=ab_qlat, q_pe=ab_qpe)),
+        "append_tree_kv": time_graph(lambda: kdt.append_tree_kv(ab_cache, ab["c_kv_new"], ab["k_rope_new"],
+                                                                prefix_lens, ab_depth, 50000.0)),
+        "absorb_o": time_graph(lambda: kdt.absorb_o(ab["o_lat"], ab["w_vc"], o=ab_o)),
+    }
+
     pairs = visible_pairs(inp.parents, inp.prefix_lens, H)
     flops = pairs * 2 * (R + P + R)                       # score over R+P, value over R
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -339,6 +368,7 @@ def main():
         "algorithmic_bytes_per_step": alg_bytes,
         "tree_accept_us": accept_us,
         "tree_build_us": tree_build_us,
+        "around_verify_us": around_us,
     }
 
     if not args.no_cpu and not args.kernel_only:

@@ -20,8 +20,9 @@
 // along the contraction; they run on v_mfma_f32_32x32x16_bf16 as the
 // transposed product C^T = W . X^T, so that a lane ends up holding four
 // consecutive outputs of one row (8-byte stores).  A workgroup owns one head
-// and NCB 32-wide blocks of outputs and keeps their weight operands for the
-// whole contraction in registers; its four waves sweep the rows 32 at a time.
+// and NCB 32-wide blocks of outputs for a group of up to kAbsorbRowBlocks
+// 32-row blocks, and keeps its weight operands for the whole contraction in
+// registers; its four waves take the row blocks in turn.
 #include <math.h>
 
 #include "kdt_common.hpp"
@@ -31,6 +32,8 @@ namespace kdt {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kAbsorbRowBlocks = 8;             // 32-row blocks per workgroup (two per wave)
 
 // Row source of a contraction: element (row m, k) of head h.
 struct RowSrc {
@@ -63,9 +66,9 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(RowSrc x, const __bf16
 #pragma unroll
     for (int c = 0; c < KS; ++c) wf[cb][c] = *reinterpret_cast<const bf16x8_t*>(wr + 16 * c);
   }
-  const int n_rb = (M + 31) / 32;
+  const int n_rb = min((M + 31) / 32, (int)(blockIdx.z + 1) * kAbsorbRowBlocks);
 #pragma unroll 1
-  for (int rb = wave; rb < n_rb; rb += 4) {
+  for (int rb = blockIdx.z * kAbsorbRowBlocks + wave; rb < n_rb; rb += 4) {
     const int m = rb * 32 + r;
     const bool ok = m < M;
     const __bf16* xr = x.row(ok ? m : 0, h) + 8 * hh;
@@ -93,21 +96,26 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(RowSrc x, const __bf16
   }
 }
 
-// NeoX rotary embedding of one P-vector in place of its copy: the pair
-// (x[i], x[i + P/2]) turns by pos * theta^(-2i/P).  The angle is formed and
-// reduced in double precision (positions reach 10^5 and more).
-__device__ __forceinline__ void rope_pair(const __bf16* src, __bf16* dst, int P, int i, double pos,
-                                          double log2_theta) {
-  const int half = P / 2;
-  const double inv = exp2(-(2.0 * i / P) * log2_theta);
-  const double ang = pos * inv;
-  const double s = sin(ang), c = cos(ang);
-  const double x1 = (double)(float)src[i], x2 = (double)(float)src[i + half];
-  dst[i] = (__bf16)(float)(x1 * c - x2 * s);
-  dst[i + half] = (__bf16)(float)(x2 * c + x1 * s);
+// Rotation of pair i at position pos: the pair (x[i], x[i + P/2]) turns by
+// pos * theta^(-2i/P).  The angle is formed and reduced to [-pi, pi] in double
+// precision (positions reach 10^5 and more); the sine and cosine of the
+// reduced angle are taken in single precision.
+__device__ __forceinline__ void rope_angle(int P, int i, double pos, double log2_theta, float& c, float& s) {
+  const double ang = pos * exp2(-(2.0 * i / P) * log2_theta);
+  const double two_pi = 6.283185307179586476925286766559;
+  const float red = (float)(ang - two_pi * rint(ang / two_pi));
+  s = sinf(red);
+  c = cosf(red);
 }
 
-// q_pe[b, t, h, :] = rope(q[b, t, h, dn:], L_b + depth[b, t]); one thread per pair
+__device__ __forceinline__ void rope_apply(const __bf16* src, __bf16* dst, int half, int i, float c, float s) {
+  const float x1 = (float)src[i], x2 = (float)src[i + half];
+  dst[i] = (__bf16)(x1 * c - x2 * s);
+  dst[i + half] = (__bf16)(x2 * c + x1 * s);
+}
+
+// q_pe[b, t, h, :] = rope(q[b, t, h, dn:], L_b + depth[b, t]); one thread per
+// (row, head, pair)
 __global__ __launch_bounds__(256) void rope_q_kernel(RowSrc q, int dn, int P, int H, int M,
                                                      const int32_t* __restrict__ prefix_lens,
                                                      const int32_t* __restrict__ depth, double log2_theta,
@@ -119,8 +127,9 @@ __global__ __launch_bounds__(256) void rope_q_kernel(RowSrc q, int dn, int P, in
   const int64_t mh = gid / half;
   const int h = (int)(mh % H), m = (int)(mh / H);
   const int b = m / q.T;
-  const double pos = (double)prefix_lens[b] + (double)depth[m];
-  rope_pair(q.row(m, h) + dn, q_pe + ((int64_t)m * H + h) * P, P, i, pos, log2_theta);
+  float c, s;
+  rope_angle(P, i, (double)prefix_lens[b] + (double)depth[m], log2_theta, c, s);
+  rope_apply(q.row(m, h) + dn, q_pe + ((int64_t)m * H + h) * P, half, i, c, s);
 }
 
 // cache row L_b + t <- [c_kv_new[b, t] | rope(k_rope_new[b, t], L_b + depth[b, t])]
@@ -141,24 +150,32 @@ __global__ __launch_bounds__(256) void append_kernel(const __bf16* __restrict__ 
   const __bf16* cs = c_new + (int64_t)m * R;
   for (int i = threadIdx.x; i < R; i += blockDim.x) row[i] = cs[i];
   const double pos = (double)L + (double)depth[m];
-  for (int i = threadIdx.x; i < P / 2; i += blockDim.x) rope_pair(k_new + (int64_t)m * P, row + R, P, i, pos, log2_theta);
+  for (int i = threadIdx.x; i < P / 2; i += blockDim.x) {
+    float c, s;
+    rope_angle(P, i, pos, log2_theta, c, s);
+    rope_apply(k_new + (int64_t)m * P, row + R, P / 2, i, c, s);
+  }
 }
 
 template <int KS, int NCB>
 static int launch_gemm(const RowSrc& x, const __bf16* w, int M, int H, int N, __bf16* out, hipStream_t s) {
   if (N % (32 * NCB)) return KDT_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((absorb_gemm_kernel<KS, NCB>), dim3(H, N / (32 * NCB)), dim3(256), 0, s, x, w, M, H, N, out);
+  const int groups = ((M + 31) / 32 + kAbsorbRowBlocks - 1) / kAbsorbRowBlocks;
+  if (groups > 65535) return KDT_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((absorb_gemm_kernel<KS, NCB>), dim3(H, N / (32 * NCB), groups), dim3(256), 0, s, x, w, M, H,
+                     N, out);
   return launch_status();
 }
 
 // dispatch on the contraction length: the weight fragments of a workgroup
-// (NCB x KS x 4 registers) stay within 128 registers
+// (NCB x KS x 4 registers) stay within 64 registers where possible, so that
+// two waves fit on a SIMD
 static int gemm(const RowSrc& x, const __bf16* w, int K, int M, int H, int N, __bf16* out, hipStream_t s) {
   switch (K) {
-    case 32: return launch_gemm<2, 4>(x, w, M, H, N, out, s);
-    case 64: return launch_gemm<4, 4>(x, w, M, H, N, out, s);
-    case 128: return launch_gemm<8, 4>(x, w, M, H, N, out, s);
-    case 256: return launch_gemm<16, 2>(x, w, M, H, N, out, s);
+    case 32: return launch_gemm<2, 2>(x, w, M, H, N, out, s);
+    case 64: return launch_gemm<4, 2>(x, w, M, H, N, out, s);
+    case 128: return launch_gemm<8, 2>(x, w, M, H, N, out, s);
+    case 256: return launch_gemm<16, 1>(x, w, M, H, N, out, s);
     case 512: return launch_gemm<32, 1>(x, w, M, H, N, out, s);
     default: return KDT_ERR_UNSUPPORTED;
   }
