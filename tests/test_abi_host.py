@@ -187,8 +187,12 @@ def test_layout_forcing_and_validation():
         assert p.rows == 65 * 16 and rows in (64, 128)
     rc, p = _plan(_desc())
     assert rc == 0 and p.layout in (1, 2)
-    rc, p = _plan(_desc(layout=3))
-    assert rc == kdt.KDT_ERR_INVALID_ARG if hasattr(kdt, "KDT_ERR_INVALID_ARG") else rc == 1
+    rc, p = _plan(_desc(layout=3))            # depth-split pairs: bf16, R = 512, P = 64
+    assert rc == 0 and p.layout == 3
+    rc, p = _plan(_desc(layout=3, R=64, P=16))
+    assert rc == 2
+    rc, p = _plan(_desc(layout=4))
+    assert rc == 1
     rc, p = _plan(_desc(layout=-1))
     assert rc == 1
     # AR decoding (64 rows) plans the column-split layout

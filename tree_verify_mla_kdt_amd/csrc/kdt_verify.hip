@@ -238,6 +238,10 @@ __device__ __forceinline__ void wait_vmem_lds() {
 // across it; the wait above provides the ordering the tile ring needs.
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS accesses are done (tile copies
+// may stay in flight).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Loads one wave issues for a region of SLOTS 16-byte chunks when wave-loads
 // are dealt round-robin to the four waves: the minimum over the waves.
 constexpr int min_wave_loads(int slots) { return (slots / 64) / (kThreads / 64); }
@@ -306,9 +310,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int KW = MM::KW, KMF = MM::KMF;
   constexpr int NCHUNK = D / KMF;             // MFMA steps of the score contraction
   constexpr int NB = R / 32;                  // 32-wide output column blocks
-  static_assert(CS == 1 || CS == 2, "column split");
-  constexpr int NBL = NB / CS;                // output column blocks of one wave
-  constexpr int BM = kBM / CS;                // query rows per workgroup
+  static_assert(CS == 1 || CS == 2 || CS == 3, "layout");
+  // CS = 3: the 64-row layout with the score contraction split by depth: the
+  // two waves of a pair each contract half of the R + P columns, exchange
+  // their partial scores through LDS and add them, so no score MFMA is done
+  // twice; the softmax is duplicated as in CS = 2 and the values split by
+  // columns.
+  constexpr bool DS = (CS == 3);
+  constexpr int CSC = DS ? 2 : CS;            // column split of the output
+  static_assert(!DS || (NCHUNK % 2 == 0 && KW == 8), "depth split: bf16, even contraction steps");
+  constexpr int NQF = DS ? NCHUNK / 2 : NCHUNK;   // query fragments (score steps) of one wave
+  constexpr int NBL = NB / CSC;               // output column blocks of one wave
+  constexpr int BM = kBM / CSC;               // query rows per workgroup
   constexpr int PV_STEPS = kBN / KMF;         // MFMA steps of the value contraction per tile
   constexpr int RC = R * (int)sizeof(T) / 16; // 16-byte chunks of c_kv per key
   constexpr int PC = P * (int)sizeof(T) / 16; // 16-byte chunks of k_pe per key
@@ -321,13 +334,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // inline asm the compiler does not track, so one array indexed with
   // constants serves.
   constexpr bool STASH_LDS = (NBL == 16);
-  constexpr int NBUF = STASH_LDS ? 3 : 4;
+  constexpr int NBUF = (STASH_LDS || DS) ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) char s_tiles[NBUF][BUF_BYTES];
   // vmcnt per tile copy on every wave (a wave that issued more waits a
   // little longer, which is safe).
   constexpr int STAGE_LOADS = min_wave_loads(kBN * RC) + min_wave_loads(kBN * PC);
   static_assert(STAGE_LOADS * (NBUF - 2) < 64, "vmcnt range");
   __shared__ int s_dead;
+  // depth split: each wave's partial score tile, 16 floats per lane
+  __shared__ __attribute__((aligned(16))) f32x4 s_sx[DS ? 4 * kThreads : 1];
   // One accumulator block per lane parks here while the score tile is alive
   // (all 512 registers are otherwise taken: 256 accumulators, Q, scores).
   constexpr bool STASH = STASH_LDS;
@@ -341,7 +356,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int rb = wave / CS, chalf = wave % CS;   // row block, output column half
+  const int rb = wave / CSC, chalf = wave % CSC;   // row block, output column half (and depth half)
+  const int c0 = DS ? chalf * NQF : 0;          // first score step of this wave
   const int m = rt * BM + rb * 32 + r;        // this lane's query row
   const bool row_ok = m < a.M;
   const int t = row_ok ? m / a.H : 0;
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr bool Q_VIA_LDS = (CS == 2) && (KW == 8) && (NBUF == 4);
   static_assert(!Q_VIA_LDS || BM == 2 * kBN, "query staging: two 32-row blocks per workgroup");
   const bool q_lds = Q_VIA_LDS && a.q_rows_uniform;
-  frag qf[NCHUNK];
+  frag qf[NQF];
   if (q_lds) {
     const uint32_t ql_ss = (uint32_t)(a.q_lat_sh * (int64_t)sizeof(T));
     const uint32_t qp_ss = (uint32_t)(a.q_pe_sh * (int64_t)sizeof(T));
@@ -409,9 +425,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
     const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
 #pragma unroll
-    for (int c = 0; c < NCHUNK; ++c) {
-      if (c < R / KMF) qf[c] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
-      else qf[c] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
+    for (int j = 0; j < NQF; ++j) {
+      const int c = c0 + j;
+      if (c < R / KMF) qf[j] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
+      else qf[j] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
     }
   }
   uint64_t vw0 = ~0ull, vw1 = ~0ull;
@@ -564,19 +581,33 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         return buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
       }
     };
-    constexpr int QPF = NCHUNK < KDT_SCORE_PREFETCH ? NCHUNK : KDT_SCORE_PREFETCH;
+    constexpr int QPF = NQF < KDT_SCORE_PREFETCH ? NQF : KDT_SCORE_PREFETCH;
     frag kf[QPF];
 #pragma unroll
-    for (int c = 0; c < QPF; ++c) kf[c] = *reinterpret_cast<const frag*>(score_src(c));
+    for (int j = 0; j < QPF; ++j) kf[j] = *reinterpret_cast<const frag*>(score_src(c0 + j));
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NCHUNK; ++c) {
-      const frag cur = kf[c % QPF];
-      if (c + QPF < NCHUNK) kf[c % QPF] = *reinterpret_cast<const frag*>(score_src(c + QPF));
-      s = MM::mma(cur, qf[c], s);
+    for (int j = 0; j < NQF; ++j) {
+      const frag cur = kf[j % QPF];
+      if (j + QPF < NQF) kf[j % QPF] = *reinterpret_cast<const frag*>(score_src(c0 + j + QPF));
+      s = MM::mma(cur, qf[j], s);
       fence_mem_mfma();
+    }
+    if constexpr (DS) {
+      // add the partner's half of the contraction (the pair's waves hold the
+      // same rows and keys; a + b is the same on both)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) s_sx[(wave * 4 + g) * 64 + lane] = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
+      wait_lds();
+      tile_barrier();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o = s_sx[((wave ^ 1) * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * g + e] += o[e];
+      }
     }
     // Value operand of contraction step c (16 keys), output block db.
     auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
@@ -676,16 +707,19 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     if (pass == 1) {
       __syncthreads();
       if (s_dead == 0) break;                 // common case: no redo
-      if (dead) {
+      // Depth split: every wave takes part in the score exchange (a
+      // workgroup barrier), so all waves redo the split; rows that did not
+      // outgrow their reference recompute the same sums.
+      if (dead || DS) {
 #pragma unroll
         for (int i = 0; i < NBL; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
         l_run = 0.0f;
-        m_ref = m_max;
+        if (dead) m_ref = m_max;
       }
     }
-    const bool compute = (pass == 0) || dead;
+    const bool compute = (pass == 0) || dead || DS;
     dead = false;
     // Tiles rotate through the NBUF buffers: the step for tile t waits for its
     // copy and computes, issuing between its value MFMAs the copy of tile
@@ -850,6 +884,9 @@ static bool shape_supported(int dtype, int R, int P) {
   return false;
 }
 
+// Layout 3 (depth-split score pairs) is built for the bf16 rank-512 shape.
+static bool depth_split_supported(int dtype, int R, int P) { return dtype == KDT_BF16 && R == 512 && P == 64; }
+
 static int validate(const kdt_verify_desc* d) {
   if (!d) return KDT_ERR_INVALID_ARG;
   if (d->B <= 0 || d->q_len <= 0 || d->H <= 0 || d->R <= 0 || d->P <= 0) return KDT_ERR_INVALID_ARG;
@@ -858,7 +895,7 @@ static int validate(const kdt_verify_desc* d) {
   if (d->max_prefix_len < 0 || d->capacity < (int64_t)d->max_prefix_len + d->q_len)
     return KDT_ERR_INVALID_ARG;
   if (d->split_keys < 0 || (d->split_keys % 64) != 0) return KDT_ERR_INVALID_ARG;
-  if (d->layout < 0 || d->layout > 2) return KDT_ERR_INVALID_ARG;
+  if (d->layout < 0 || d->layout > 3) return KDT_ERR_INVALID_ARG;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
   if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
   if (!shape_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
@@ -872,12 +909,13 @@ static int validate(const kdt_verify_desc* d) {
   for (int64_t s : strides)
     if (s < 0 || s % vec) return KDT_ERR_UNSUPPORTED;
   if ((int64_t)d->B * d->q_len * d->H > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
+  if (d->layout == 3 && !depth_split_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
   return KDT_OK;
 }
 
 // Rows per workgroup of a layout (1: four waves x 32 rows; 2: two row blocks,
 // each shared by a wave pair that splits the output columns).
-static int layout_rows(int layout) { return layout == 2 ? kBM / 2 : kBM; }
+static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 
 // Modelled time (microseconds) of one launch, split kernel plus merge, for a
 // layout and split size.  Workgroups run one per compute unit, so G of them
@@ -908,8 +946,8 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   int best_layout = d->layout ? d->layout : 1;
   int64_t sk = d->split_keys;
   double best = 1e300;
-  for (int layout = 1; layout <= 2; ++layout) {
-    if (d->layout && layout != d->layout) continue;
+  for (int layout = 1; layout <= 3; ++layout) {
+    if (d->layout ? layout != d->layout : layout == 3) continue;
     const int64_t n_seq_tiles = (int64_t)d->B * ((M + layout_rows(layout) - 1) / layout_rows(layout));
     const int64_t n_tiles = (n_max + kBN - 1) / kBN;
     for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
@@ -925,6 +963,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
     }
   }
   p->layout = best_layout;
+  if (sk <= 0) return KDT_ERR_INVALID_ARG;   // (no candidate: cannot happen for a validated descriptor)
   const int64_t ns = (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
@@ -972,6 +1011,15 @@ static int launch_split(const VerifyArgs& a, bool direct, hipStream_t s) {
   const int64_t grid = (int64_t)a.B * a.n_rt * a.max_splits;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
   const bool cs2 = a.layout == 2;
+  if constexpr (R == 512 && P == 64 && sizeof(T) == 2) {
+    if (a.layout == 3) {
+      if (direct)
+        hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 3>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 3>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+      return launch_status();
+    }
+  }
   if (direct && cs2)
     hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else if (direct)
