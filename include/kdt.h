@@ -130,8 +130,12 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  * one sequence), each of its four waves 32 rows and all R output columns;
  * 2 = a workgroup owns 64 rows, each pair of waves shares 32 rows and splits
  * the output columns (half the value work per wave, the score work done by
- * both).  0 lets the library choose (and the split size) by modelling the
- * launch; results agree between layouts to rounding.
+ * both); 3 = as 2, but the two waves of a pair each contract half of the score
+ * depth (R + P) and add each other's partial scores through LDS (no score work
+ * repeated, one more workgroup barrier per key tile; bf16 with R = 512 and
+ * P = 64 only, KDT_ERR_UNSUPPORTED otherwise).  0 lets the library choose
+ * between 1 and 2 (and the split size) by modelling the launch; results agree
+ * between layouts to rounding.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t dtype;                       /* kdt_dtype */
@@ -149,7 +153,7 @@ typedef struct {
   float* lse;                          /* device float32 [B, q_len, H] */
   int32_t* seq_status;                 /* device int32 [B], nullable */
   int32_t split_keys;                  /* 0 = auto, else a multiple of 64 */
-  int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split */
+  int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split */
 } kdt_verify_desc;
 
 /* Host-only planning: no device access.  The partial buffers live in the
@@ -168,7 +172,7 @@ typedef struct {
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
   int32_t rows;                /* q_len * H */
   int32_t direct;              /* 1: max_splits == 1, no partials, no merge */
-  int32_t layout;              /* workgroup layout used: 1 or 2 */
+  int32_t layout;              /* workgroup layout used: 1, 2 or 3 */
   int64_t part_o_offset;       /* bytes into the workspace */
   int64_t part_lse_offset;
   size_t workspace_bytes;      /* 0 when direct */
