@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layout", type=int, default=0, help="force a workgroup layout (0: the planner's choice)")
     ap.add_argument("--split-keys", type=int, default=0, help="force a key split size (0: the planner's choice)")
+    ap.add_argument("--partials-f32", action="store_true",
+                    help="keep the split partials in float32 (default: the input dtype)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying HIP graphs (for counter runs)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB", "CAL_WRITE_DB"),
@@ -186,7 +188,7 @@ def main():
     c0 = copies[0]
     desc, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
                                      prefix_lens, vis, cfg.softmax_scale, max_prefix, out, lse, None,
-                                     args.split_keys, args.layout)
+                                     args.split_keys, args.layout, args.partials_f32)
     plan = kdt.verify_plan(desc)
     ws_bytes = max(int(plan.workspace_bytes), int(plan.part_lse_offset + B * plan.max_splits * plan.rows * 4))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -196,14 +198,14 @@ def main():
         kdt.build_visibility(parents, vis=vis, depth=depth)
         kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
                         cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
-                        split_keys=args.split_keys, layout=args.layout)
+                        split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32)
         kdt.gather_accepted(c["cache"], prefix_lens, accepted, n_acc, q, new_prefix_lens=new_pl)
 
     def split_only(i):
         c = copies[i % n_copies]
         kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
                             cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws,
-                            split_keys=args.split_keys, layout=args.layout)
+                            split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32)
 
     # Launches are replayed from HIP graphs: one graph runs the step once per
     # input copy, so host launch overhead stays out of the measured step time.
@@ -356,6 +358,7 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": B, "heads": H, "kv_lora_rank": R,
                    "rope_dim": P, "q_len": q, "prefix_len_max": max_prefix,
                    "split_keys": plan.split_keys, "splits": plan.max_splits, "layout": plan.layout,
+                   "partials": "bf16" if plan.part_dtype == kdt.KDT_BF16 else "f32",
                    "step": "build_visibility + verify (split + merge) + gather_accepted",
                    "input_copies": n_copies, "kernel_only": bool(args.kernel_only)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

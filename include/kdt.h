@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDT_ABI_VERSION 2
+#define KDT_ABI_VERSION 3
 #define KDT_MAX_Q_LEN 128           /* tree tokens per sequence (two 64-bit mask words) */
 
 typedef enum {
@@ -154,25 +154,31 @@ typedef struct {
   int32_t* seq_status;                 /* device int32 [B], nullable */
   int32_t split_keys;                  /* 0 = auto, else a multiple of 64 */
   int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split */
+  int32_t partials_f32;                /* 1 = keep split partial outputs in float32; 0 = in the input dtype */
 } kdt_verify_desc;
 
 /* Host-only planning: no device access.  The partial buffers live in the
  * workspace at the given byte offsets:
- *   part_o   float32 [B, max_splits, NBLK, 32*R]   normalised partial outputs, tiled
- *   part_lse float32 [B, max_splits, q_len*H]      natural-log partial LSE (-inf: empty split)
+ *   part_o   part_dtype [B, max_splits, NBLK, 32*R]  normalised partial outputs, tiled
+ *   part_lse float32 [B, max_splits, q_len*H]        natural-log partial LSE (-inf: empty split)
  * Row index within a sequence is m = t*H + h.  NBLK = ceil(q_len*H / 32): rows
  * are grouped in blocks of 32, and inside block m / 32 element (m, c) sits at
- *   256*(c/8) + 128*((c/4)%2) + 4*(m%32) + c%4
- * which is the register order of a 32x32 matrix-core accumulator, so the split
- * kernel writes whole cache lines.  Padding rows of the last block hold
- * unspecified values.  Sequence b uses splits
- * 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1. */
+ *   float32:  256*(c/8) + 128*((c/4)%2) + 4*(m%32) + c%4
+ *   bf16:     512*(c/16) + 8*(m%32 + 32*((c/4)%2)) + 4*((c/8)%2) + c%4
+ * (elements), the register order of a 32x32 matrix-core accumulator, so the
+ * split kernel writes whole cache lines (each lane 16 bytes, each store
+ * instruction one contiguous 1 KB run).  Padding rows of the last block hold
+ * unspecified values.  part_dtype is KDT_F32 for float32 inputs or when
+ * partials_f32 is set, else KDT_BF16 (rounded to nearest even: one more
+ * rounding of the output's own precision, which halves the partial traffic).
+ * Sequence b uses splits 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1. */
 typedef struct {
   int32_t split_keys;          /* keys per split (multiple of 64) */
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
   int32_t rows;                /* q_len * H */
   int32_t direct;              /* 1: max_splits == 1, no partials, no merge */
   int32_t layout;              /* workgroup layout used: 1, 2 or 3 */
+  int32_t part_dtype;          /* kdt_dtype of part_o */
   int64_t part_o_offset;       /* bytes into the workspace */
   int64_t part_lse_offset;
   size_t workspace_bytes;      /* 0 when direct */
@@ -196,13 +202,14 @@ int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_byt
  * ceil((prefix_lens[b] + q_len) / split_keys) clamped to [1, max_splits].
  * Splits with part_lse = -inf carry no weight; a row with no finite split gets
  * out = 0 and lse = -inf.  out is written in `dtype` (bf16: round to nearest
- * even).  part_o / part_lse are contiguous with the layout given above (tiled
- * part_o); out has strides out_sb, out_st, out_sh (elements) over
- * [B, q_len, H, R].  R must be a multiple of 8.
+ * even).  part_o (elements of `part_dtype`, KDT_F32 or KDT_BF16) and part_lse
+ * are contiguous with the layout given above (tiled part_o); out has strides
+ * out_sb, out_st, out_sh (elements) over [B, q_len, H, R].  R must be a
+ * multiple of 8 (of 16 for bf16 partials).
  * prefix_lens may be NULL when split_keys == 0.
  * ---------------------------------------------------------------------- */
-int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32_t R,
-                       const float* part_o, const float* part_lse, int32_t max_splits,
+int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32_t R, int32_t part_dtype,
+                       const void* part_o, const float* part_lse, int32_t max_splits,
                        const int32_t* prefix_lens, int32_t split_keys,
                        void* out, int64_t out_sb, int64_t out_st, int64_t out_sh,
                        float* lse, void* stream);

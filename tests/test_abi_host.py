@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
 
 
 def test_version_and_status_strings():
-    assert kdt.lib().kdt_abi_version() == 2
+    assert kdt.lib().kdt_abi_version() == 3
     for code in range(5):
         assert kdt.status_str(code)
     assert kdt.status_str(99) == "unknown status"
@@ -66,8 +66,13 @@ def test_plan_sizes_and_layout():
     assert p.max_splits == -(-(4096 + 65) // p.split_keys)
     assert p.direct == (1 if p.max_splits == 1 else 0)
     nblk = -(-M // 32)
-    assert p.part_lse_offset >= 1 * p.max_splits * nblk * 32 * 512 * 4 and p.part_lse_offset % 256 == 0
+    assert p.part_dtype == kdt.KDT_BF16            # bf16 inputs: bf16 partials unless asked otherwise
+    assert p.part_lse_offset >= 1 * p.max_splits * nblk * 32 * 512 * 2 and p.part_lse_offset % 256 == 0
     assert p.workspace_bytes == p.part_lse_offset + p.max_splits * M * 4
+    rc, p32 = _plan(_desc(partials_f32=1, split_keys=p.split_keys))
+    assert rc == 0 and p32.part_dtype == kdt.KDT_F32 and p32.max_splits == p.max_splits
+    assert p32.part_lse_offset >= p.max_splits * nblk * 32 * 512 * 4
+    assert _plan(_desc(partials_f32=2))[0] == 1
     rc, p = _plan(_desc(split_keys=128))
     assert rc == 0 and p.split_keys == 128 and p.max_splits == 33
     # a single split: no workspace
@@ -122,9 +127,11 @@ def test_visibility_gather_accept_and_tree_argument_checks():
     assert g(5, 1, 9, 576, FAKE, 0, 576, 64, 1, 0, FAKE, FAKE, FAKE, 9, None, None, None) == 2    # dtype
     assert g(1, 1, 200, 576, FAKE, 0, 576, 256, 1, 0, FAKE, FAKE, FAKE, 9, None, None, None) == 2
     m = L.kdt_merge_partials
-    assert m(1, 1, 9, 4, 512, None, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 1
-    assert m(1, 1, 9, 4, 512, FAKE, FAKE, 2, None, 64, FAKE, 0, 0, 0, FAKE, None) == 1           # needs prefix_lens
-    assert m(1, 1, 9, 4, 36, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2             # R % 8
+    assert m(1, 1, 9, 4, 512, 0, None, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 1
+    assert m(1, 1, 9, 4, 512, 0, FAKE, FAKE, 2, None, 64, FAKE, 0, 0, 0, FAKE, None) == 1        # needs prefix_lens
+    assert m(1, 1, 9, 4, 36, 0, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2          # R % 8
+    assert m(1, 1, 9, 4, 40, 1, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2          # bf16 partials: R % 16
+    assert m(1, 1, 9, 4, 512, 2, FAKE, FAKE, 2, None, 0, FAKE, 0, 0, 0, FAKE, None) == 2         # partial dtype
     a = L.kdt_tree_accept
     # parents, tokens, target_pred, B, q, accepted, n_accepted, bonus, seq_status, stream
     assert a(None, FAKE, FAKE, 1, 9, FAKE, FAKE, None, None, None) == 1

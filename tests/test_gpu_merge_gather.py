@@ -11,19 +11,23 @@ from gpu_util import GpuInputs, check_close, dev, require_gpu, to_f64
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_merge_matches_oracle_with_empty_splits(out_dtype):
+@pytest.mark.parametrize("S", [5, 37])
+def test_merge_matches_oracle_with_empty_splits(out_dtype, part_dtype, S):
     require_gpu()
-    rng = synth.rng_for(5)
-    B, S, q, H, R = 3, 5, 9, 4, 512
+    rng = synth.rng_for(5 + S)
+    B, q, H, R = 3, 9, 4, 512
     M = q * H
     po = rng.standard_normal((B, S, M, R)).astype(np.float32)
+    if part_dtype == torch.bfloat16:        # the partials the merge reads are exactly these values
+        po = torch.from_numpy(po).to(torch.bfloat16).float().numpy()
     pl = (rng.standard_normal((B, S, M)) * 4).astype(np.float32)
     pl[rng.random((B, S, M)) < 0.3] = -np.inf
     pl[0, :, 3] = -np.inf                      # a row with no finite split
     po[pl == -np.inf] = np.nan                 # never read
-    po_tiled = kdt.tile_partials(torch.from_numpy(po).to(dev()))
-    assert np.array_equal(kdt.untile_partials(po_tiled, M).cpu().numpy(), po, equal_nan=True)
+    po_tiled = kdt.tile_partials(torch.from_numpy(po).to(part_dtype).to(dev()))
+    assert np.array_equal(kdt.untile_partials(po_tiled, M).float().cpu().numpy(), po, equal_nan=True)
     out, lse = kdt.merge_partials(po_tiled, torch.from_numpy(pl).to(dev()), q, H, out_dtype)
     torch.cuda.synchronize()
     ro, rl = oracle.merge_partials(np.moveaxis(np.nan_to_num(po, nan=0.0), 1, 0).astype(np.float64),
@@ -37,7 +41,8 @@ def test_merge_matches_oracle_with_empty_splits(out_dtype):
     assert np.max(np.abs(got_l[fin] - rl[fin])) < 1e-5
 
 
-def test_partials_merge_to_full_result():
+@pytest.mark.parametrize("partials_f32", [False, True])
+def test_partials_merge_to_full_result(partials_f32):
     cfg = synth.Config("merge_cfg", 12, "bf16", B=2, H=16, R=512, P=64, q_len=17, prefix=("uniform", 100, 900),
                        tree="uniform")
     inp = synth.generate(cfg)
@@ -45,13 +50,14 @@ def test_partials_merge_to_full_result():
     vis, _ = kdt.build_visibility(g.parents)
     part_o, part_lse, plan = kdt.verify_partials(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis,
                                                  cfg.softmax_scale, max_prefix_len=g.max_prefix_len,
-                                                 split_keys=128)
+                                                 split_keys=128, partials_f32=partials_f32)
     torch.cuda.synchronize()
+    assert part_o.dtype == (torch.float32 if partials_f32 else torch.bfloat16)
     # each split's partial equals the oracle on that chunk of keys
     vis_np, _ = oracle.build_visibility(inp.parents)
     cache = inp.f64("cache")
     ql, qp = inp.f64("q_lat"), inp.f64("q_pe")
-    po = kdt.untile_partials(part_o, cfg.q_len * cfg.H).cpu().numpy()
+    po = kdt.untile_partials(part_o, cfg.q_len * cfg.H).float().cpu().numpy()
     pl = part_lse.cpu().numpy()
     for b in range(cfg.B):
         L = int(inp.prefix_lens[b])
@@ -72,7 +78,7 @@ def test_partials_merge_to_full_result():
                                   split_keys=plan.split_keys)
     torch.cuda.synchronize()
     o_full, l_full = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis, cfg.softmax_scale,
-                                     max_prefix_len=g.max_prefix_len, split_keys=128)
+                                     max_prefix_len=g.max_prefix_len, split_keys=128, partials_f32=partials_f32)
     torch.cuda.synchronize()
     assert torch.equal(out, o_full) and torch.equal(lse, l_full)
 

@@ -18,13 +18,15 @@ from gpu_util import (GpuInputs, check_close, oracle_full, oracle_rows, require_
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(g: GpuInputs, split_keys=0, vis=None, max_prefix_len=None, seq_status=None, layout=0):
+def run_gpu(g: GpuInputs, split_keys=0, vis=None, max_prefix_len=None, seq_status=None, layout=0,
+            partials_f32=False):
     require_gpu()
     if vis is None:
         vis, _ = kdt.build_visibility(g.parents)
     out, lse = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis, g.cfg.softmax_scale,
                                max_prefix_len=g.max_prefix_len if max_prefix_len is None else max_prefix_len,
-                               split_keys=split_keys, seq_status=seq_status, layout=layout)
+                               split_keys=split_keys, seq_status=seq_status, layout=layout,
+                               partials_f32=partials_f32)
     torch.cuda.synchronize()
     return to_f64(out), lse.cpu().numpy().astype(np.float64)
 
@@ -56,14 +58,15 @@ def test_bf16_full_parity_tree_shapes(q, tree):
     check_close("bf16", o, ro, l, rl, f"q={q} {tree}")
 
 
+@pytest.mark.parametrize("partials_f32", [False, True])
 @pytest.mark.parametrize("split_keys", [0, 64, 128, 192, 1024])
-def test_bf16_split_counts_agree(split_keys):
+def test_bf16_split_counts_agree(split_keys, partials_f32):
     cfg = small_cfg(q=33, tree="deep_chain", prefix=("uniform", 40, 700), B=3, H=16, index=31)
     inp = synth.generate(cfg)
     g = GpuInputs(inp)
-    o, l = run_gpu(g, split_keys=split_keys)
+    o, l = run_gpu(g, split_keys=split_keys, partials_f32=partials_f32)
     ro, rl = oracle_full(inp)
-    check_close("bf16", o, ro, l, rl, f"split_keys={split_keys}")
+    check_close("bf16", o, ro, l, rl, f"split_keys={split_keys} partials_f32={partials_f32}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -152,11 +155,13 @@ def _growing_scores_inputs(q, H, L, B=2, index=63):
 def test_redo_when_scores_outgrow_the_reference(layout, split_keys):
     inp = _growing_scores_inputs(q=9, H=16, L=900)
     g = GpuInputs(inp)
-    o, l = run_gpu(g, split_keys=split_keys, layout=layout)
     ro, rl = oracle_full(inp)
-    # the weight sits on the level-3 keys: every output is near 3
+    # the weight sits on the level-3 keys: every output is near 3 (the largest
+    # outputs of the suite, so the bf16 partials' rounding is largest here)
     assert np.all(np.abs(ro - 3.0) < 0.1)
-    check_close("bf16", o, ro, l, rl, f"layout {layout} split {split_keys}")
+    for pf in (False, True):
+        o, l = run_gpu(g, split_keys=split_keys, layout=layout, partials_f32=pf)
+        check_close("bf16", o, ro, l, rl, f"layout {layout} split {split_keys} partials_f32={pf}")
 
 
 # ---------------------------------------------------------------- full-size configurations

@@ -115,12 +115,13 @@ struct VerifyArgs {
   const uint64_t* vis;
   void* out; int64_t out_sb, out_st, out_sh;
   float* lse;
-  float* part_o;
+  void* part_o;         // float32 or bf16 (part_bf16), tiled
   float* part_lse;
   int32_t* seq_status;
   float scale_log2;
   int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len, layout;
   int q_rows_uniform;   // query rows m = t * H + h sit at one byte stride (q_lat and q_pe)
+  int part_bf16;        // partial outputs in bf16 (else float32)
 };
 
 // The value of C-layout register v of a 32x32 MFMA result held by a lane in
@@ -786,45 +787,78 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     if (hh == 0 && chalf == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
   } else {
     // Partials stay in accumulator order: the wave's 32 rows form one block
-    // of 32 x R floats in which register group (db, g) of every lane is one
-    // contiguous 1 KB run, so each store instruction writes whole lines.
+    // of 32 x R values in which every store instruction writes one contiguous
+    // 1 KB run (float32: register group (db, g) of every lane; bf16: groups
+    // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).
     const int blk = rt * (BM / 32) + rb;
-    float* o = a.part_o + (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R) + 4 * lane;
+    const int64_t base = (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R);
+    if (a.part_bf16) {
+      __bf16* o = static_cast<__bf16*>(a.part_o) + base + 8 * lane;
 #pragma unroll
-    for (int db = 0; db < NBL; ++db)
+      for (int db = 0; db < NBL; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v4[4];
+        for (int gp = 0; gp < 2; ++gp) {
+          bf16x8 v8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
-        store4<float>(o + 256 * (4 * (chalf * NBL + db) + g), v4);
-      }
+          for (int e = 0; e < 8; ++e) v8[e] = (__bf16)(acc[db][8 * gp + e] * inv);
+          *reinterpret_cast<bf16x8*>(o + 512 * (2 * (chalf * NBL + db) + gp)) = v8;
+        }
+    } else {
+      float* o = static_cast<float*>(a.part_o) + base + 4 * lane;
+#pragma unroll
+      for (int db = 0; db < NBL; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
+          store4<float>(o + 256 * (4 * (chalf * NBL + db) + g), v4);
+        }
+    }
     if (hh == 0 && chalf == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Cross-split merge: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
-// Partials are in accumulator order (32-row blocks; column c of block row r at
-// 256 (c / 8) + 128 ((c / 4) % 2) + 4 r + c % 4), so one wave handles one
-// (sequence, block, 8-column group): every lane reads one float4 per split and
-// the wave's reads are one contiguous 1 KB run.  Splits are consumed sixteen
-// at a time with a running maximum, so sixteen loads per lane are in flight
-// (one memory round trip for up to sixteen splits).  Splits
-// with lse_k = -inf are skipped by selection, never by multiplication: their
-// partial output may never have been written.
-template <typename T>
+// Partials are in accumulator order (32-row blocks, see the split kernel's
+// epilogue), so one wave handles one (sequence, block, column group) of 8
+// float32 or 16 bf16 columns: every lane reads 16 bytes per split and the
+// wave's reads are one contiguous 1 KB run.  Splits are consumed sixteen at a
+// time with a running maximum, so sixteen loads per lane are in flight (one
+// memory round trip for up to sixteen splits).  Splits with lse_k = -inf are
+// skipped by selection, never by multiplication: their partial output may
+// never have been written.
+template <typename PT>
+struct PartLoad;
+template <>
+struct PartLoad<float> {
+  static constexpr int NV = 4;                  // values per lane per split
+  typedef f32x4 raw;
+  __device__ static __forceinline__ float get(const raw& r, int i) { return r[i]; }
+};
+template <>
+struct PartLoad<__bf16> {
+  static constexpr int NV = 8;
+  typedef bf16x8 raw;
+  __device__ static __forceinline__ float get(const raw& r, int i) { return (float)r[i]; }
+};
+
+template <typename T, typename PT>
 __global__ __launch_bounds__(256) void merge_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
+    const PT* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
     int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys,
     T* __restrict__ out, int64_t out_sb, int64_t out_st, int64_t out_sh, float* __restrict__ lse) {
   constexpr int U = 16;
-  const int n_c8 = R >> 3;
+  constexpr int NV = PartLoad<PT>::NV;
+  constexpr int CW = 2 * NV;                    // columns per wave
+  typedef typename PartLoad<PT>::raw raw;
+  const int n_cg = R / CW;
   const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, hh = lane >> 5;
-  if (wid >= (int64_t)B * n_blk * n_c8) return;
-  const int c8 = (int)(wid % n_c8);
-  const int64_t bblk = wid / n_c8;
+  if (wid >= (int64_t)B * n_blk * n_cg) return;
+  const int cg = (int)(wid % n_cg);
+  const int64_t bblk = wid / n_cg;
   const int blk = (int)(bblk % n_blk), b = (int)(bblk / n_blk);
   const int M = q * H;
   const int m = blk * 32 + (lane & 31);
@@ -837,17 +871,19 @@ __global__ __launch_bounds__(256) void merge_kernel(
   }
   const float* pl = part_lse + (int64_t)b * max_splits * M + m;
   const int64_t split_stride = (int64_t)n_blk * 32 * R;
-  const float* po = part_o + ((int64_t)b * max_splits * n_blk + blk) * (32 * R) + 256 * c8 + 4 * lane;
+  const PT* po = part_o + ((int64_t)b * max_splits * n_blk + blk) * (32 * R) + 32 * CW * cg + NV * lane;
   float mx = -INFINITY, z = 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
   for (int k0 = 0; k0 < ns; k0 += U) {
     float lk[U];
-    f32x4 ok[U];
+    raw ok[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int k = k0 + j;
       lk[j] = k < ns ? pl[(int64_t)k * M] : -INFINITY;
-      ok[j] = k < ns ? *reinterpret_cast<const f32x4*>(po + k * split_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < ns) ok[j] = *reinterpret_cast<const raw*>(po + k * split_stride);
     }
     float cm = lk[0];
 #pragma unroll
@@ -855,7 +891,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
     if (cm > mx) {
       const float sc = __expf(mx - cm);   // 0 while mx is still -inf
       z *= sc;
-      acc *= sc;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] *= sc;
       mx = cm;
     }
 #pragma unroll
@@ -863,14 +900,19 @@ __global__ __launch_bounds__(256) void merge_kernel(
       const bool live = lk[j] != -INFINITY;
       const float w = live ? __expf(lk[j] - mx) : 0.0f;
       z += w;
-      acc = live ? acc + w * ok[j] : acc;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = live ? acc[i] + w * PartLoad<PT>::get(ok[j], i) : acc[i];
     }
   }
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-  const float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
   const int t = m / H, h = m - t * H;
-  store4<T>(out + b * out_sb + t * out_st + h * out_sh + 8 * c8 + 4 * hh, v4);
-  if (c8 == 0 && hh == 0) lse[(int64_t)b * M + m] = z > 0.0f ? mx + logf(z) : -INFINITY;
+  T* o = out + b * out_sb + t * out_st + h * out_sh + CW * cg + 4 * hh;
+#pragma unroll
+  for (int q4 = 0; q4 < NV / 4; ++q4) {       // value i of the lane is column CW*cg + 8*(i/4) + 4*hh + i%4
+    const float v4[4] = {acc[4 * q4] * inv, acc[4 * q4 + 1] * inv, acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv};
+    store4<T>(o + 8 * q4, v4);
+  }
+  if (cg == 0 && hh == 0) lse[(int64_t)b * M + m] = z > 0.0f ? mx + logf(z) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -896,6 +938,7 @@ static int validate(const kdt_verify_desc* d) {
     return KDT_ERR_INVALID_ARG;
   if (d->split_keys < 0 || (d->split_keys % 64) != 0) return KDT_ERR_INVALID_ARG;
   if (d->layout < 0 || d->layout > 3) return KDT_ERR_INVALID_ARG;
+  if (d->partials_f32 != 0 && d->partials_f32 != 1) return KDT_ERR_INVALID_ARG;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
   if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
   if (!shape_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
@@ -923,13 +966,14 @@ static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 // burst of query and first-tile loads), every partial costs its write and its
 // read in the merge, and splitting at all adds the merge launch.  The
 // constants are fitted to measurements at R = 512, P = 64 (a 128-row tile of
-// 32 keys about 2.05 us, a 128-row partial about 0.12 us) and scale with the
-// contraction work of one wave and with the rows a partial holds.
-static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R, int P, int layout) {
+// 32 keys about 2.05 us, a 128-row float32 partial about 0.12 us) and scale
+// with the contraction work of one wave and with the bytes a partial holds.
+static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R, int P, int layout,
+                          int part_bytes) {
   const int rows = layout_rows(layout);
   const double t_tile = 2.05 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
   const double t_start = 6.0;
-  const double t_part = 0.12 * rows / kBM * R / 512.0;
+  const double t_part = 0.12 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 5.0;
   const int64_t ns = (n_max + sk - 1) / sk;
   const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
@@ -941,6 +985,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   if (rc != KDT_OK) return rc;
   const int M = d->q_len * d->H;
   const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
+  const int part_dtype = (d->dtype == KDT_BF16 && !d->partials_f32) ? KDT_BF16 : KDT_F32;
   // candidate layouts: the requested one, or both; candidate split sizes:
   // the requested one, or every distinct split count up to 4096
   int best_layout = d->layout ? d->layout : 1;
@@ -953,7 +998,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
     for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
       int64_t k = d->split_keys ? d->split_keys : ((n_max + s - 1) / s + 63) / 64 * 64;
       if (!d->split_keys && (n_max + k - 1) / k != s) continue;   // covered by a smaller s
-      const double c = launch_cost(n_seq_tiles, n_max, k, d->R, d->P, layout);
+      const double c = launch_cost(n_seq_tiles, n_max, k, d->R, d->P, layout, elem_size(part_dtype));
       if (c < best * 0.999) {                 // ties go to fewer splits, then layout 1
         best = c;
         sk = k;
@@ -963,6 +1008,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
     }
   }
   p->layout = best_layout;
+  p->part_dtype = part_dtype;
   if (sk <= 0) return KDT_ERR_INVALID_ARG;   // (no candidate: cannot happen for a validated descriptor)
   const int64_t ns = (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
@@ -971,7 +1017,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   p->rows = M;
   p->direct = ns == 1 ? 1 : 0;
   const int64_t n_part_rows = (int64_t)d->B * ns * M;
-  const int64_t o_bytes = (int64_t)d->B * ns * ((M + 31) / 32) * 32 * d->R * 4;
+  const int64_t o_bytes = (int64_t)d->B * ns * ((M + 31) / 32) * 32 * d->R * elem_size(part_dtype);
   p->part_o_offset = 0;
   p->part_lse_offset = (o_bytes + 255) / 256 * 256;
   p->workspace_bytes = (size_t)(p->part_lse_offset + n_part_rows * 4);
@@ -989,7 +1035,8 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.vis = d->vis;
   a.out = d->out; a.out_sb = d->out_sb; a.out_st = d->out_st; a.out_sh = d->out_sh;
   a.lse = d->lse;
-  a.part_o = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_offset) : nullptr;
+  a.part_o = ws ? static_cast<void*>(static_cast<char*>(ws) + p.part_o_offset) : nullptr;
+  a.part_bf16 = p.part_dtype == KDT_BF16;
   a.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_lse_offset) : nullptr;
   a.seq_status = d->seq_status;
   a.scale_log2 = d->softmax_scale * kLog2e;
@@ -1038,20 +1085,31 @@ static int dispatch_split(int dtype, int R, int P, const VerifyArgs& a, bool dir
   return KDT_ERR_UNSUPPORTED;
 }
 
-static int launch_merge(int dtype, int B, int q, int H, int R, const float* po, const float* pl,
-                        int max_splits, const int32_t* prefix_lens, int split_keys, void* out,
-                        int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
+template <typename PT>
+static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, const float* pl, int max_splits,
+                          const int32_t* prefix_lens, int split_keys, void* out, int64_t osb, int64_t ost,
+                          int64_t osh, float* lse, hipStream_t s) {
   const int n_blk = (q * H + 31) / 32;
-  const int64_t waves = (int64_t)B * n_blk * (R / 8);
+  const int64_t waves = (int64_t)B * n_blk * (R / (2 * PartLoad<PT>::NV));
   const int64_t grid = (waves + 3) / 4;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
   if (dtype == KDT_BF16)
-    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, H,
-                       R, n_blk, prefix_lens, split_keys, static_cast<__bf16*>(out), osb, ost, osh, lse);
+    hipLaunchKernelGGL((merge_kernel<__bf16, PT>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q,
+                       H, R, n_blk, prefix_lens, split_keys, static_cast<__bf16*>(out), osb, ost, osh, lse);
   else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, H,
-                       R, n_blk, prefix_lens, split_keys, static_cast<float*>(out), osb, ost, osh, lse);
+    hipLaunchKernelGGL((merge_kernel<float, PT>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q,
+                       H, R, n_blk, prefix_lens, split_keys, static_cast<float*>(out), osb, ost, osh, lse);
   return launch_status();
+}
+
+static int launch_merge(int dtype, int B, int q, int H, int R, int part_dtype, const void* po, const float* pl,
+                        int max_splits, const int32_t* prefix_lens, int split_keys, void* out,
+                        int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
+  if (part_dtype == KDT_BF16)
+    return launch_merge_t(dtype, B, q, H, R, static_cast<const __bf16*>(po), pl, max_splits, prefix_lens,
+                          split_keys, out, osb, ost, osh, lse, s);
+  return launch_merge_t(dtype, B, q, H, R, static_cast<const float*>(po), pl, max_splits, prefix_lens, split_keys,
+                        out, osb, ost, osh, lse, s);
 }
 
 }  // namespace kdt
@@ -1071,7 +1129,7 @@ extern "C" int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t
   const kdt::VerifyArgs a = kdt::make_args(d, p, p.direct ? nullptr : workspace);
   int r = kdt::dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
   if (r != KDT_OK || p.direct) return r;
-  return kdt::launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, a.part_o, a.part_lse, p.max_splits,
+  return kdt::launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, p.part_dtype, a.part_o, a.part_lse, p.max_splits,
                            d->prefix_lens, p.split_keys, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
 }
 
@@ -1086,7 +1144,7 @@ extern "C" int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, si
 }
 
 extern "C" int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32_t R,
-                                  const float* part_o, const float* part_lse, int32_t max_splits,
+                                  int32_t part_dtype, const void* part_o, const float* part_lse, int32_t max_splits,
                                   const int32_t* prefix_lens, int32_t split_keys, void* out,
                                   int64_t out_sb, int64_t out_st, int64_t out_sh, float* lse,
                                   void* stream) {
@@ -1095,11 +1153,12 @@ extern "C" int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32
     return KDT_ERR_INVALID_ARG;
   if (split_keys > 0 && !prefix_lens) return KDT_ERR_INVALID_ARG;
   if (dtype != KDT_F32 && dtype != KDT_BF16) return KDT_ERR_UNSUPPORTED;
-  if (R % 8) return KDT_ERR_UNSUPPORTED;
+  if (part_dtype != KDT_F32 && part_dtype != KDT_BF16) return KDT_ERR_UNSUPPORTED;
+  if (R % (part_dtype == KDT_BF16 ? 16 : 8)) return KDT_ERR_UNSUPPORTED;
   const int64_t vec = dtype == KDT_F32 ? 4 : 8;    // output elements per 16 bytes
   if (!kdt::aligned16(part_o) || !kdt::aligned16(out) || (R % vec) || out_sb % vec || out_st % vec ||
       out_sh % vec || out_sb < 0 || out_st < 0 || out_sh < 0)
     return KDT_ERR_UNSUPPORTED;
-  return kdt::launch_merge(dtype, B, q_len, H, R, part_o, part_lse, max_splits, prefix_lens, split_keys,
+  return kdt::launch_merge(dtype, B, q_len, H, R, part_dtype, part_o, part_lse, max_splits, prefix_lens, split_keys,
                            out, out_sb, out_st, out_sh, lse, static_cast<hipStream_t>(stream));
 }

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdt.so")
 
 KDT_F32, KDT_BF16 = 0, 1
-ABI_VERSION = 2                       # the KDT_ABI_VERSION this binding was written for
+ABI_VERSION = 3                       # the KDT_ABI_VERSION this binding was written for
 KDT_SEQ_BAD_TREE, KDT_SEQ_BAD_LEN, KDT_SEQ_BAD_INDEX = 1, 2, 4
 MAX_Q_LEN = 128
 
@@ -38,14 +38,14 @@ class VerifyDesc(ctypes.Structure):
         ("out", _c_p), ("out_sb", _c_i64), ("out_st", _c_i64), ("out_sh", _c_i64),
         ("lse", _c_p),
         ("seq_status", _c_p),
-        ("split_keys", _c_i32), ("layout", _c_i32),
+        ("split_keys", _c_i32), ("layout", _c_i32), ("partials_f32", _c_i32),
     ]
 
 
 class VerifyPlan(ctypes.Structure):
     _fields_ = [
         ("split_keys", _c_i32), ("max_splits", _c_i32), ("rows", _c_i32), ("direct", _c_i32),
-        ("layout", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64), ("workspace_bytes", ctypes.c_size_t),
+        ("layout", _c_i32), ("part_dtype", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.kdt_verify_get_plan.argtypes = [ctypes.POINTER(VerifyDesc), ctypes.POINTER(VerifyPlan)]
         L.kdt_verify_attn.argtypes = [ctypes.POINTER(VerifyDesc), _c_p, ctypes.c_size_t, _c_p]
         L.kdt_verify_partials.argtypes = [ctypes.POINTER(VerifyDesc), _c_p, ctypes.c_size_t, _c_p]
-        L.kdt_merge_partials.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p,
+        L.kdt_merge_partials.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p,
                                          _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]
         L.kdt_gather_accepted.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
                                           _c_i64, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p]
@@ -138,7 +138,7 @@ def build_visibility(parents: torch.Tensor, vis=None, depth=None, seq_status=Non
 
 
 def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                 seq_status, split_keys, layout=0):
+                 seq_status, split_keys, layout=0, partials_f32=False):
     B, q, H, R = q_lat.shape
     P = q_pe.shape[-1]
     d = VerifyDesc()
@@ -158,11 +158,12 @@ def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_p
     d.seq_status = 0 if seq_status is None else seq_status.data_ptr()
     d.split_keys = int(split_keys)
     d.layout = int(layout)
+    d.partials_f32 = 1 if partials_f32 else 0
     return d
 
 
 def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                    seq_status, split_keys, layout=0):
+                    seq_status, split_keys, layout=0, partials_f32=False):
     for t in (q_lat, q_pe, c_kv, k_pe):
         if t.stride(-1) != 1:
             raise ValueError("innermost dimension must be contiguous")
@@ -177,7 +178,7 @@ def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
     if lse is None:
         lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
     d = _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                     seq_status, split_keys, layout)
+                     seq_status, split_keys, layout, partials_f32)
     return d, out, lse
 
 
@@ -188,11 +189,11 @@ def verify_plan(desc: VerifyDesc) -> VerifyPlan:
 
 
 def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
-                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0):
+                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False):
     """Tree-verify attention.  c_kv [B, S, R] and k_pe [B, S, P] may be views of
     one fused [B, S, R+P] cache.  Returns (out [B, q, H, R], lse [B, q, H])."""
     d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                                  out, lse, seq_status, split_keys, layout)
+                                  out, lse, seq_status, split_keys, layout, partials_f32)
     p = verify_plan(d)
     if p.workspace_bytes and (workspace is None or workspace.numel() * workspace.element_size() < p.workspace_bytes):
         workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
@@ -210,32 +211,39 @@ def untile_partials(part_o, rows: int):
     """Row-major view of tiled partials: [B, S, NBLK, 32*R] -> [B, S, rows, R].
 
     In the tiled layout, column c of row r of a 32-row block sits at
-    256*(c//8) + 128*((c//4)%2) + 4*r + c%4 (the order of a 32x32 matrix-core
-    accumulator)."""
+    256*(c//8) + 128*((c//4)%2) + 4*r + c%4 (float32) or at
+    512*(c//16) + 8*(r + 32*((c//4)%2)) + 4*((c//8)%2) + c%4 (bf16): the
+    order of a 32x32 matrix-core accumulator."""
     B, S, nblk, w = part_o.shape
     R = w // 32
-    t = part_o.reshape(B, S, nblk, R // 8, 2, 32, 4).permute(0, 1, 2, 5, 3, 4, 6)
+    if part_o.dtype == torch.bfloat16:
+        t = part_o.reshape(B, S, nblk, R // 16, 2, 32, 2, 4).permute(0, 1, 2, 5, 3, 6, 4, 7)
+    else:
+        t = part_o.reshape(B, S, nblk, R // 8, 2, 32, 4).permute(0, 1, 2, 5, 3, 4, 6)
     return t.reshape(B, S, nblk * 32, R)[:, :, :rows]
 
 
 def tile_partials(rows_major):
     """Inverse of untile_partials: [B, S, rows, R] -> contiguous [B, S, NBLK, 32*R]
-    (padding rows zero)."""
+    in the encoding of rows_major's dtype (padding rows zero)."""
     B, S, M, R = rows_major.shape
     nblk = partial_blocks(M)
     pad = rows_major.new_zeros((B, S, nblk * 32, R))
     pad[:, :, :M] = rows_major
-    t = pad.reshape(B, S, nblk, 32, R // 8, 2, 4).permute(0, 1, 2, 4, 5, 3, 6)
+    if rows_major.dtype == torch.bfloat16:
+        t = pad.reshape(B, S, nblk, 32, R // 16, 2, 2, 4).permute(0, 1, 2, 4, 6, 3, 5, 7)
+    else:
+        t = pad.reshape(B, S, nblk, 32, R // 8, 2, 4).permute(0, 1, 2, 4, 5, 3, 6)
     return t.contiguous().reshape(B, S, nblk, 32 * R)
 
 
 def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None,
-                    workspace=None, seq_status=None, split_keys=0, stream=None, layout=0):
-    """Split stage only.  Returns (part_o, part_lse, plan): part_o float32
-    [B, S, NBLK, 32*R] in the tiled layout (see untile_partials), part_lse
-    float32 [B, S, q*H]."""
+                    workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False):
+    """Split stage only.  Returns (part_o, part_lse, plan): part_o
+    [B, S, NBLK, 32*R] in the tiled layout (see untile_partials), bf16 for
+    bf16 inputs unless partials_f32, else float32; part_lse float32 [B, S, q*H]."""
     d, _, _ = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                              None, None, seq_status, split_keys, layout)
+                              None, None, seq_status, split_keys, layout, partials_f32)
     p = verify_plan(d)
     B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
     need = max(int(p.workspace_bytes), p.part_lse_offset + B * S * M * 4, 1)
@@ -246,15 +254,17 @@ def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
                                                            _stream(stream)))
     nblk = partial_blocks(M)
     n_o = B * S * nblk * 32 * R
-    part_o = workspace[p.part_o_offset:p.part_o_offset + n_o * 4].view(torch.float32).view(B, S, nblk, 32 * R)
+    pdt = torch.bfloat16 if p.part_dtype == KDT_BF16 else torch.float32
+    es = 2 if p.part_dtype == KDT_BF16 else 4
+    part_o = workspace[p.part_o_offset:p.part_o_offset + n_o * es].view(pdt).view(B, S, nblk, 32 * R)
     part_lse = workspace[p.part_lse_offset:p.part_lse_offset + B * S * M * 4].view(torch.float32).view(B, S, M)
     return part_o, part_lse, p
 
 
 def merge_partials(part_o, part_lse, q_len, H, out_dtype, prefix_lens=None, split_keys=0, out=None, lse=None,
                    stream=None):
-    """part_o float32 [B, S, NBLK, 32*R] (tiled), part_lse float32 [B, S, q*H]
-    -> (out [B, q, H, R], lse [B, q, H])."""
+    """part_o float32 or bf16 [B, S, NBLK, 32*R] (tiled), part_lse float32
+    [B, S, q*H] -> (out [B, q, H, R], lse [B, q, H])."""
     B, S, nblk, w = part_o.shape
     R = w // 32
     assert nblk == partial_blocks(q_len * H) and part_lse.shape == (B, S, q_len * H)
@@ -266,7 +276,7 @@ def merge_partials(part_o, part_lse, q_len, H, out_dtype, prefix_lens=None, spli
     code = KDT_BF16 if out.dtype == torch.bfloat16 else KDT_F32
     sb, st, sh = out.stride()[:3]
     _check("kdt_merge_partials", lib().kdt_merge_partials(
-        code, B, q_len, H, R, _ptr(part_o), _ptr(part_lse), S, _ptr(prefix_lens), int(split_keys), _ptr(out),
+        code, B, q_len, H, R, KDT_BF16 if part_o.dtype == torch.bfloat16 else KDT_F32, _ptr(part_o), _ptr(part_lse), S, _ptr(prefix_lens), int(split_keys), _ptr(out),
         sb, st, sh, _ptr(lse), _stream(stream)))
     return out, lse
 
