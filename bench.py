@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload max_budget]
 
 One step = the whole hot path over one batch: visibility masks from parent
-pointers, split-prefix verify attention + log-sum-exp merge, and the
-accepted-path gather.  Inputs are seeded synthetic tensors of the workload's
+pointers (derived inside the split kernel; --separate-visibility runs the
+visibility kernel first instead), split-prefix verify attention + log-sum-exp
+merge, and the accepted-path gather.  Inputs are seeded synthetic tensors of the workload's
 shape, resident in HBM before timing starts; the step rotates over enough input
 copies (> 256 MB) that the Infinity Cache cannot hold them all.
 
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layout", type=int, default=0, help="force a workgroup layout (0: the planner's choice)")
     ap.add_argument("--split-keys", type=int, default=0, help="force a key split size (0: the planner's choice)")
+    ap.add_argument("--separate-visibility", action="store_true",
+                    help="build the masks with kdt_build_visibility in the step (default: the split kernel derives "
+                         "them from the parents)")
     ap.add_argument("--partials-f32", action="store_true",
                     help="keep the split partials in float32 (default: the input dtype)")
     ap.add_argument("--eager", action="store_true",
@@ -180,6 +184,9 @@ def main():
     max_prefix = int(inp.prefix_lens.max())
     W = (q + 63) // 64
     vis = torch.empty((B, q, W), dtype=torch.int64, device=dev)
+    # masks: from kdt_build_visibility in the step, or derived by the split
+    # kernel from the parents
+    vis_arg, par_arg = (vis, None) if args.separate_visibility else (None, parents)
     depth = torch.empty((B, q), dtype=torch.int32, device=dev)
     out = torch.empty((B, q, H, R), dtype=base["q_lat"].dtype, device=dev)
     lse = torch.empty((B, q, H), dtype=torch.float32, device=dev)
@@ -187,25 +194,28 @@ def main():
 
     c0 = copies[0]
     desc, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
-                                     prefix_lens, vis, cfg.softmax_scale, max_prefix, out, lse, None,
-                                     args.split_keys, args.layout, args.partials_f32)
+                                     prefix_lens, vis_arg, cfg.softmax_scale, max_prefix, out, lse, None,
+                                     args.split_keys, args.layout, args.partials_f32, par_arg)
     plan = kdt.verify_plan(desc)
     ws_bytes = max(int(plan.workspace_bytes), int(plan.part_lse_offset + B * plan.max_splits * plan.rows * 4))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step(i):
         c = copies[i % n_copies]
-        kdt.build_visibility(parents, vis=vis, depth=depth)
-        kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
+        if args.separate_visibility:
+            kdt.build_visibility(parents, vis=vis, depth=depth)
+        kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                         cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
-                        split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32)
+                        split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
+                        parents=par_arg)
         kdt.gather_accepted(c["cache"], prefix_lens, accepted, n_acc, q, new_prefix_lens=new_pl)
 
     def split_only(i):
         c = copies[i % n_copies]
-        kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis,
+        kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                             cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws,
-                            split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32)
+                            split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
+                            parents=par_arg)
 
     # Launches are replayed from HIP graphs: one graph runs the step once per
     # input copy, so host launch overhead stays out of the measured step time.
@@ -265,6 +275,17 @@ def main():
     e1.record(cur)
     torch.cuda.synchronize()
     split_ms = e0.elapsed_time(e1) / (reps * n_copies)
+
+    # --- the visibility kernel on its own (the step derives the masks inside
+    # the split kernel unless --separate-visibility)
+    g_vis = capture(lambda i: kdt.build_visibility(parents, vis=vis, depth=depth), range(20))
+    g_vis.replay()
+    e0.record(cur)
+    for _ in range(10):
+        g_vis.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    vis_us = e0.elapsed_time(e1) * 1e3 / 200
 
     # --- greedy tree accept on the same trees (timed on its own: the step
     # above takes the accepted paths as input)
@@ -359,7 +380,8 @@ def main():
                    "rope_dim": P, "q_len": q, "prefix_len_max": max_prefix,
                    "split_keys": plan.split_keys, "splits": plan.max_splits, "layout": plan.layout,
                    "partials": "bf16" if plan.part_dtype == kdt.KDT_BF16 else "f32",
-                   "step": "build_visibility + verify (split + merge) + gather_accepted",
+                   "step": ("build_visibility + verify (split + merge) + gather_accepted" if args.separate_visibility
+                            else "verify (split kernel deriving the masks from the parents + merge) + gather_accepted"),
                    "input_copies": n_copies, "kernel_only": bool(args.kernel_only)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
@@ -369,7 +391,7 @@ def main():
         "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": alg_bytes,
-        "tree_accept_us": accept_us,
+        "build_visibility_us": vis_us, "tree_accept_us": accept_us,
         "tree_build_us": tree_build_us,
         "around_verify_us": around_us,
     }

@@ -104,7 +104,12 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  *   q_pe  [B, q_len, H, P]   strides q_pe_sb,  q_pe_st,  q_pe_sh
  *   c_kv  [B, capacity, R]   strides c_kv_sb, c_kv_ss (row stride may be R+P for a fused [c_kv | k_pe] cache)
  *   k_pe  [B, capacity, P]   strides k_pe_sb, k_pe_ss
- *   vis   uint64 [B, q_len, W] contiguous (as written by kdt_build_visibility)
+ *   vis   uint64 [B, q_len, W] contiguous (as written by kdt_build_visibility),
+ *         or NULL: then `parents` (int32 [B, q_len] contiguous, as for
+ *         kdt_build_visibility) is required and the split kernel derives the
+ *         same masks itself, with the same treatment of invalid parents
+ *         (flagged KDT_SEQ_BAD_TREE in seq_status); this saves the separate
+ *         visibility launch.  When vis is given, parents is ignored.
  *   out   [B, q_len, H, R]   in `dtype`, strides out_sb, out_st, out_sh
  *   lse   float32 [B, q_len, H] contiguous
  * `dtype` is the element type of q_lat, q_pe, c_kv, k_pe and out.  Arithmetic:
@@ -155,6 +160,7 @@ typedef struct {
   int32_t split_keys;                  /* 0 = auto, else a multiple of 64 */
   int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split */
   int32_t partials_f32;                /* 1 = keep split partial outputs in float32; 0 = in the input dtype */
+  const int32_t* parents;              /* device int32 [B, q_len]; used when vis is NULL */
 } kdt_verify_desc;
 
 /* Host-only planning: no device access.  The partial buffers live in the

@@ -98,6 +98,12 @@ def test_plan_rejects_bad_descriptors(field, value, code):
     assert rc == code
 
 
+def test_masks_or_parents_required():
+    assert _plan(_desc(vis=0))[0] == 1                 # neither masks nor parents
+    rc, _ = _plan(_desc(vis=0, parents=FAKE))          # masks derived from parents
+    assert rc == 0
+
+
 def test_fp32_large_rank_is_unsupported():
     rc, _ = _plan(_desc(dtype=0))
     assert rc == 2

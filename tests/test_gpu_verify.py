@@ -327,3 +327,52 @@ def test_config_max_budget_all_layouts_agree():
     for layout in (1, 2, 3):
         o, l = run_gpu(g, layout=layout)
         check_close("bf16", o, ro, l, rl, f"max_budget layout {layout}")
+
+
+# ---------------------------------------------------------------- masks derived from parents
+
+@pytest.mark.parametrize("layout", [0, 1, 2, 3])
+@pytest.mark.parametrize("q,H,tree,split_keys", [(1, 16, "chain", 0), (17, 16, "uniform", 0),
+                                                 (65, 16, "best_first", 64), (100, 4, "uniform", 0),
+                                                 (128, 2, "deep_chain", 128), (33, 3, "deep_chain", 0)])
+def test_masks_from_parents_match_given_masks(layout, q, H, tree, split_keys):
+    """vis = None with parents: the split kernel derives the masks itself and
+    the result is bit-identical to the one with kdt_build_visibility's masks
+    (only splits that reach the tree derive them)."""
+    cfg = small_cfg(q=q, H=H, tree=tree, prefix=("uniform", 30, 700), B=3, index=300 + q + H)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    vis, _ = kdt.build_visibility(g.parents)
+    args = (g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens)
+    o1, l1 = kdt.verify_attn(*args, vis, cfg.softmax_scale, max_prefix_len=g.max_prefix_len,
+                             split_keys=split_keys, layout=layout)
+    st = torch.zeros(cfg.B, dtype=torch.int32, device=g.parents.device)
+    o2, l2 = kdt.verify_attn(*args, None, cfg.softmax_scale, max_prefix_len=g.max_prefix_len,
+                             split_keys=split_keys, layout=layout, parents=g.parents, seq_status=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert st.cpu().tolist() == [0] * cfg.B
+    ro, rl = oracle_full(inp)
+    check_close("bf16", to_f64(o2), ro, l2.cpu().numpy().astype(np.float64), rl, f"parents layout={layout} q={q}")
+
+
+def test_bad_trees_from_parents_are_flagged_like_the_mask_kernel():
+    cfg = small_cfg(q=9, H=4, tree="uniform", prefix=("fixed", 100), B=4, index=77)
+    inp = synth.generate(cfg)
+    par = inp.parents.copy()
+    par[1, 0] = 3                      # root with a parent
+    par[2, 4], par[2, 6] = 6, 4        # a cycle through forward parents
+    par[3, 2] = -7                     # out of range
+    g = GpuInputs(inp)
+    g.parents = torch.from_numpy(par).to(g.parents.device)
+    st1 = torch.zeros(cfg.B, dtype=torch.int32, device=g.parents.device)
+    vis, _ = kdt.build_visibility(g.parents, seq_status=st1)
+    args = (g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens)
+    o1, l1 = kdt.verify_attn(*args, vis, cfg.softmax_scale, max_prefix_len=g.max_prefix_len)
+    st2 = torch.zeros_like(st1)
+    o2, l2 = kdt.verify_attn(*args, None, cfg.softmax_scale, max_prefix_len=g.max_prefix_len,
+                             parents=g.parents, seq_status=st2)
+    torch.cuda.synchronize()
+    bad = kdt.KDT_SEQ_BAD_TREE
+    assert st1.cpu().tolist() == [0, bad, bad, bad] and st2.cpu().tolist() == st1.cpu().tolist()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

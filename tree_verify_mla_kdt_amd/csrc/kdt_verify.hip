@@ -113,6 +113,7 @@ struct VerifyArgs {
   int64_t capacity;
   const int32_t* prefix_lens;
   const uint64_t* vis;
+  const int32_t* parents;   // masks derived in the kernel from these when vis is null
   void* out; int64_t out_sb, out_st, out_sh;
   float* lse;
   void* part_o;         // float32 or bf16 (part_bf16), tiled
@@ -342,6 +343,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int STAGE_LOADS = min_wave_loads(kBN * RC) + min_wave_loads(kBN * PC);
   static_assert(STAGE_LOADS * (NBUF - 2) < 64, "vmcnt range");
   __shared__ int s_dead;
+  // per-wave pointer-doubling area when the masks are derived from parents
+  __shared__ uint64_t s_vm[kThreads / kWave][2 * KDT_MAX_Q_LEN];
+  __shared__ int s_vj[kThreads / kWave][KDT_MAX_Q_LEN];
   // depth split: each wave's partial score tile, 16 floats per lane
   __shared__ __attribute__((aligned(16))) f32x4 s_sx[DS ? 4 * kThreads : 1];
   // One accumulator block per lane parks here while the score tile is alive
@@ -387,6 +391,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // this is safe before the prefix length is known; it is right whenever the
   // split really covers both tiles (every split but a sequence's last).
   const bool spec = (int64_t)k_begin + 2 * kBN <= a.capacity;
+  // Parents (when the masks are derived here) are loaded first, so that by
+  // the time any later copy has been waited for they have landed too.
+  int par_v[2] = {-1, -1};
+  if (a.parents) {
+    const int32_t* pp = a.parents + (int64_t)b * a.q;
+    par_v[0] = lane < a.q ? pp[lane] : -1;
+    par_v[1] = lane + 64 < a.q ? pp[lane + 64] : -1;
+  }
   if (spec) {
     stage_rows(0, s_tiles[0], kBN);
     stage_rows(1, s_tiles[1], kBN);
@@ -433,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     }
   }
   uint64_t vw0 = ~0ull, vw1 = ~0ull;
-  if (row_ok) {
+  if (row_ok && a.vis) {
     const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
     vw0 = vr[0];
     vw1 = a.W > 1 ? vr[1] : 0ull;
@@ -522,11 +534,26 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     }
   }
 
+  // Visibility words from parent pointers, only where this split reaches the
+  // tree (keys L .. N - 1): every wave runs the pointer doubling for the
+  // sequence in its own LDS area and reads its tokens' rows.
+  auto derive_vis = [&]() {
+    if (!a.parents || k_end <= L) return;
+    uint64_t m0[2], m1[2];
+    const bool bad_tree = wave_ancestor_masks(par_v, a.q, s_vm[wave], s_vj[wave], lane, m0, m1);
+    if (__any(bad_tree) && lane == 0 && wave == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_TREE);
+    if (row_ok) {
+      vw0 = s_vm[wave][2 * t];
+      vw1 = s_vm[wave][2 * t + 1];
+    }
+  };
+
   if constexpr (Q_VIA_LDS) {
     if (q_lds) {
       // the query copies (and the first tiles, issued before them) have landed
       wait_vmem_lds<0>();
       tile_barrier();
+      derive_vis();
       const char* qbuf = s_tiles[2 + rb];
 #pragma unroll
       for (int c = 0; c < NCHUNK; ++c) {
@@ -538,6 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       tile_barrier();
     }
   }
+  if (!q_lds) derive_vis();
 
   f32x16 acc[NBL];
 #pragma unroll
@@ -932,7 +960,8 @@ static bool depth_split_supported(int dtype, int R, int P) { return dtype == KDT
 static int validate(const kdt_verify_desc* d) {
   if (!d) return KDT_ERR_INVALID_ARG;
   if (d->B <= 0 || d->q_len <= 0 || d->H <= 0 || d->R <= 0 || d->P <= 0) return KDT_ERR_INVALID_ARG;
-  if (!d->q_lat || !d->q_pe || !d->c_kv || !d->k_pe || !d->prefix_lens || !d->vis || !d->out || !d->lse)
+  if (!d->q_lat || !d->q_pe || !d->c_kv || !d->k_pe || !d->prefix_lens || (!d->vis && !d->parents) || !d->out ||
+      !d->lse)
     return KDT_ERR_INVALID_ARG;
   if (d->max_prefix_len < 0 || d->capacity < (int64_t)d->max_prefix_len + d->q_len)
     return KDT_ERR_INVALID_ARG;
@@ -1033,6 +1062,7 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.capacity = d->capacity;
   a.prefix_lens = d->prefix_lens;
   a.vis = d->vis;
+  a.parents = d->vis ? nullptr : d->parents;
   a.out = d->out; a.out_sb = d->out_sb; a.out_st = d->out_st; a.out_sh = d->out_sh;
   a.lse = d->lse;
   a.part_o = ws ? static_cast<void*>(static_cast<char*>(ws) + p.part_o_offset) : nullptr;

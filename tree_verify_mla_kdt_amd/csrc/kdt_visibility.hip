@@ -6,12 +6,11 @@
 // the sequential O(n) build is followed by a parallel O(n^2) expansion.
 //
 // On gfx950 the sequential chain is replaced by pointer doubling inside one
-// wavefront: the wave owns one sequence, lane i owns tree nodes i and i + 64.
-// After round k every node holds the union of itself and its ancestors less
-// than 2^k levels up, plus a pointer 2^k levels up; seven rounds cover any
-// tree of at most 128 nodes.  Each round is one LDS exchange, so the whole
-// build is ~7 LDS round trips regardless of tree depth, and the packed rows
-// are written directly (they are the rows of the full q x q matrix).
+// wavefront (wave_ancestor_masks): the wave owns one sequence, lane i owns tree
+// nodes i and i + 64, and seven rounds of one LDS exchange each cover any tree
+// of at most 128 nodes regardless of its depth.  The packed rows are written
+// directly (they are the rows of the full q x q matrix).  The verify kernel
+// runs the same function when it is handed parents instead of masks.
 //
 // Safety bound ("The Milestone Commit", section "Mistakes and Incorrect
 // Assumptions", the tree_accept crash on cyclic random trees): a parent that is
@@ -24,59 +23,18 @@ namespace kdt {
 __global__ __launch_bounds__(64) void build_visibility_kernel(
     const int32_t* __restrict__ parents, int q, uint64_t* __restrict__ vis,
     int32_t* __restrict__ depth, int32_t* __restrict__ seq_status) {
-  __shared__ uint64_t s_mask[2][128][2];
-  __shared__ int s_jump[2][128];
+  __shared__ uint64_t s_m[2 * KDT_MAX_Q_LEN];
+  __shared__ int s_j[KDT_MAX_Q_LEN];
 
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int W = (q + 63) >> 6;
   const int32_t* par = parents + (int64_t)b * q;
-
-  bool bad = false;
+  int p[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) p[k] = lane + 64 * k < q ? par[lane + 64 * k] : -1;
   uint64_t m0[2], m1[2];      // masks of node lane (index 0) and lane + 64 (index 1)
-  int jmp[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = lane + 64 * k;
-    int p = -1;
-    m0[k] = 0;
-    m1[k] = 0;
-    if (i < q) {
-      p = par[i];
-      const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
-      if (!ok) {
-        bad = true;
-        p = -1;
-      }
-      if (i < 64) m0[k] = 1ull << i; else m1[k] = 1ull << (i - 64);
-    }
-    jmp[k] = p;
-    s_mask[0][i][0] = m0[k];
-    s_mask[0][i][1] = m1[k];
-    s_jump[0][i] = p;
-  }
-  __syncthreads();
-
-  int cur = 0;
-#pragma unroll 1
-  for (int round = 0; round < 7; ++round) {
-    const int nxt = cur ^ 1;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = lane + 64 * k;
-      const int j = jmp[k];
-      if (j >= 0) {
-        m0[k] |= s_mask[cur][j][0];
-        m1[k] |= s_mask[cur][j][1];
-        jmp[k] = s_jump[cur][j];
-      }
-      s_mask[nxt][i][0] = m0[k];
-      s_mask[nxt][i][1] = m1[k];
-      s_jump[nxt][i] = jmp[k];
-    }
-    __syncthreads();
-    cur = nxt;
-  }
+  const bool bad = wave_ancestor_masks(p, q, s_m, s_j, lane, m0, m1);
 
 #pragma unroll
   for (int k = 0; k < 2; ++k) {

@@ -39,6 +39,7 @@ class VerifyDesc(ctypes.Structure):
         ("lse", _c_p),
         ("seq_status", _c_p),
         ("split_keys", _c_i32), ("layout", _c_i32), ("partials_f32", _c_i32),
+        ("parents", _c_p),
     ]
 
 
@@ -138,7 +139,7 @@ def build_visibility(parents: torch.Tensor, vis=None, depth=None, seq_status=Non
 
 
 def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                 seq_status, split_keys, layout=0, partials_f32=False):
+                 seq_status, split_keys, layout=0, partials_f32=False, parents=None):
     B, q, H, R = q_lat.shape
     P = q_pe.shape[-1]
     d = VerifyDesc()
@@ -151,7 +152,8 @@ def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_p
     d.capacity = c_kv.shape[1]
     d.prefix_lens = prefix_lens.data_ptr()
     d.max_prefix_len = int(max_prefix_len)
-    d.vis = vis.data_ptr()
+    d.vis = 0 if vis is None else vis.data_ptr()
+    d.parents = 0 if parents is None else parents.data_ptr()
     d.softmax_scale = float(softmax_scale)
     d.out = out.data_ptr(); d.out_sb, d.out_st, d.out_sh = out.stride()[:3]
     d.lse = lse.data_ptr()
@@ -163,13 +165,19 @@ def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_p
 
 
 def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                    seq_status, split_keys, layout=0, partials_f32=False):
+                    seq_status, split_keys, layout=0, partials_f32=False, parents=None):
     for t in (q_lat, q_pe, c_kv, k_pe):
         if t.stride(-1) != 1:
             raise ValueError("innermost dimension must be contiguous")
     if not (q_lat.dtype == q_pe.dtype == c_kv.dtype == k_pe.dtype):
         raise TypeError("q_lat, q_pe, c_kv and k_pe must share one dtype")
-    assert prefix_lens.dtype == torch.int32 and vis.dtype == torch.int64
+    assert prefix_lens.dtype == torch.int32
+    if vis is None:
+        if parents is None:
+            raise ValueError("give vis or parents")
+        assert parents.dtype == torch.int32 and parents.is_contiguous() and parents.shape == q_lat.shape[:2]
+    else:
+        assert vis.dtype == torch.int64
     B, q, H, R = q_lat.shape
     if max_prefix_len is None:
         max_prefix_len = c_kv.shape[1] - q        # always an upper bound on a valid prefix
@@ -178,7 +186,7 @@ def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
     if lse is None:
         lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
     d = _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                     seq_status, split_keys, layout, partials_f32)
+                     seq_status, split_keys, layout, partials_f32, parents)
     return d, out, lse
 
 
@@ -189,11 +197,14 @@ def verify_plan(desc: VerifyDesc) -> VerifyPlan:
 
 
 def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
-                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False):
+                lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
+                parents=None):
     """Tree-verify attention.  c_kv [B, S, R] and k_pe [B, S, P] may be views of
-    one fused [B, S, R+P] cache.  Returns (out [B, q, H, R], lse [B, q, H])."""
+    one fused [B, S, R+P] cache.  vis may be None when parents [B, q] int32 is
+    given (the split kernel then derives the masks).  Returns
+    (out [B, q, H, R], lse [B, q, H])."""
     d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                                  out, lse, seq_status, split_keys, layout, partials_f32)
+                                  out, lse, seq_status, split_keys, layout, partials_f32, parents)
     p = verify_plan(d)
     if p.workspace_bytes and (workspace is None or workspace.numel() * workspace.element_size() < p.workspace_bytes):
         workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
@@ -238,12 +249,13 @@ def tile_partials(rows_major):
 
 
 def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None,
-                    workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False):
+                    workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
+                    parents=None):
     """Split stage only.  Returns (part_o, part_lse, plan): part_o
     [B, S, NBLK, 32*R] in the tiled layout (see untile_partials), bf16 for
     bf16 inputs unless partials_f32, else float32; part_lse float32 [B, S, q*H]."""
     d, _, _ = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                              None, None, seq_status, split_keys, layout, partials_f32)
+                              None, None, seq_status, split_keys, layout, partials_f32, parents)
     p = verify_plan(d)
     B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
     need = max(int(p.workspace_bytes), p.part_lse_offset + B * S * M * 4, 1)
