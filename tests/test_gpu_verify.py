@@ -19,14 +19,17 @@ pytestmark = pytest.mark.gpu
 
 
 def run_gpu(g: GpuInputs, split_keys=0, vis=None, max_prefix_len=None, seq_status=None, layout=0,
-            partials_f32=False):
+            partials_f32=False, from_parents=False):
+    """from_parents: hand the verify the parent pointers (the split kernel
+    derives the masks, as in the bench step) instead of kdt_build_visibility's
+    masks."""
     require_gpu()
-    if vis is None:
+    if vis is None and not from_parents:
         vis, _ = kdt.build_visibility(g.parents)
     out, lse = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis, g.cfg.softmax_scale,
                                max_prefix_len=g.max_prefix_len if max_prefix_len is None else max_prefix_len,
                                split_keys=split_keys, seq_status=seq_status, layout=layout,
-                               partials_f32=partials_f32)
+                               partials_f32=partials_f32, parents=g.parents if from_parents else None)
     torch.cuda.synchronize()
     return to_f64(out), lse.cpu().numpy().astype(np.float64)
 
@@ -165,11 +168,22 @@ def test_redo_when_scores_outgrow_the_reference(layout, split_keys):
 
 
 # ---------------------------------------------------------------- full-size configurations
+#
+# Each runs both routes to the masks: kdt_build_visibility's, and the split
+# kernel deriving them from the parents (the bench step's launch
+# configuration); the two must agree bit for bit.
+
+def _both_routes(g, **kw):
+    o, l = run_gpu(g, **kw)
+    o2, l2 = run_gpu(g, from_parents=True, **kw)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2), "mask routes disagree"
+    return o, l
+
 
 def test_config_max_budget_full():
     inp = synth.generate(synth.CONFIGS["max_budget"])
     g = GpuInputs(inp)
-    o, l = run_gpu(g)
+    o, l = _both_routes(g)
     ro, rl = oracle_full(inp)
     check_close("bf16", o, ro, l, rl, "max_budget")
 
@@ -177,7 +191,7 @@ def test_config_max_budget_full():
 def test_config_batched_full():
     inp = synth.generate(synth.CONFIGS["batched"])
     g = GpuInputs(inp)
-    o, l = run_gpu(g)
+    o, l = _both_routes(g)
     ro, rl = oracle_full(inp)
     check_close("bf16", o, ro, l, rl, "batched")
 
@@ -186,7 +200,7 @@ def test_config_batched_full():
 def test_config_large_sampled_rows(name):
     inp = synth.generate(synth.CONFIGS[name])
     g = GpuInputs(inp)
-    o, l = run_gpu(g)
+    o, l = _both_routes(g)
     rows = sample_rows(inp, 48)
     ro, rl = oracle_rows(inp, rows)
     go = np.stack([o[b, t, h] for (b, t, h) in rows])
@@ -200,7 +214,7 @@ def test_ar_degenerate_q1(name):
     cfg = synth.config_variant(synth.CONFIGS[name], q_len=1)
     inp = synth.generate(cfg)
     g = GpuInputs(inp)
-    o, l = run_gpu(g)
+    o, l = _both_routes(g)
     if name == "max_budget":
         ro, rl = oracle_full(inp)
         check_close("bf16", o, ro, l, rl, f"{name} q=1")
