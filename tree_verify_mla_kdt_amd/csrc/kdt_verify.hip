@@ -156,6 +156,13 @@ template <>
 __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const float* v) {
   *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
 }
+// Streaming float32 store of four values, for partials the merge reads from
+// memory: written through whole lines instead of left dirty in L2 for the
+// end-of-kernel write-back.  (Not for the direct output, whose 8-byte
+// per-row pieces only form whole lines in L2.)
+__device__ __forceinline__ void store4_f32_nt(float* dst, const float* v) {
+  __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
+}
 
 // LDS image of one key tile.  Two regions: kBN rows of the c_kv part (RC
 // 16-byte chunks per row) followed by kBN rows of the k_pe part (PC chunks).
@@ -817,7 +824,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     // Partials stay in accumulator order: the wave's 32 rows form one block
     // of 32 x R values in which every store instruction writes one contiguous
     // 1 KB run (float32: register group (db, g) of every lane; bf16: groups
-    // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).
+    // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).  Streaming
+    // stores: the merge reads them from memory anyway.
     const int blk = rt * (BM / 32) + rb;
     const int64_t base = (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R);
     if (a.part_bf16) {
@@ -829,7 +837,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           bf16x8 v8;
 #pragma unroll
           for (int e = 0; e < 8; ++e) v8[e] = (__bf16)(acc[db][8 * gp + e] * inv);
-          *reinterpret_cast<bf16x8*>(o + 512 * (2 * (chalf * NBL + db) + gp)) = v8;
+          __builtin_nontemporal_store(v8, reinterpret_cast<bf16x8*>(o + 512 * (2 * (chalf * NBL + db) + gp)));
         }
     } else {
       float* o = static_cast<float*>(a.part_o) + base + 4 * lane;
@@ -840,7 +848,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           float v4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
-          store4<float>(o + 256 * (4 * (chalf * NBL + db) + g), v4);
+          store4_f32_nt(o + 256 * (4 * (chalf * NBL + db) + g), v4);
         }
     }
     if (hh == 0 && chalf == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
