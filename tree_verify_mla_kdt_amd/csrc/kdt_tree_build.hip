@@ -58,28 +58,30 @@ __device__ __forceinline__ bool better(double wa, int oa, double wb, int ob) {
 }
 
 // Whole-wave lane shifts (DPP): lane i receives lane i + 1's value (UP) or
-// lane i - 1's (DOWN); the lane with no source receives `fill`.
+// lane i - 1's (DOWN).  The lane with no source (63 for UP, 0 for DOWN)
+// receives zero; the rebuild below never selects that value (lane i takes
+// the UP value only while i < p1 <= 63, and lane 0 never takes DOWN).
 constexpr int kDppWaveShl1 = 0x130;
 constexpr int kDppWaveShr1 = 0x138;
 template <int CTRL>
-__device__ __forceinline__ int shift_i(int x, int fill) {
-  return __builtin_amdgcn_update_dpp(fill, x, CTRL, 0xf, 0xf, false);
+__device__ __forceinline__ int shift_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);
 }
 template <int CTRL>
-__device__ __forceinline__ float shift_f(float x, float fill) {
-  return __int_as_float(shift_i<CTRL>(__float_as_int(x), __float_as_int(fill)));
+__device__ __forceinline__ float shift_f(float x) {
+  return __int_as_float(shift_i<CTRL>(__float_as_int(x)));
 }
 template <int CTRL>
-__device__ __forceinline__ double shift_d(double x, double fill) {
-  const unsigned long long u = __double_as_longlong(x), f = __double_as_longlong(fill);
-  const int lo = shift_i<CTRL>((int)(u & 0xffffffffull), (int)(f & 0xffffffffull));
-  const int hi = shift_i<CTRL>((int)(u >> 32), (int)(f >> 32));
+__device__ __forceinline__ double shift_d(double x) {
+  const unsigned long long u = __double_as_longlong(x);
+  const int lo = shift_i<CTRL>((int)(u & 0xffffffffull));
+  const int hi = shift_i<CTRL>((int)(u >> 32));
   return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 template <int CTRL>
 __device__ __forceinline__ Cand shift_c(const Cand& c) {
-  return Cand{shift_d<CTRL>(c.w, -INFINITY), shift_d<CTRL>(c.base, 0.0), shift_i<CTRL>(c.order, INT_MAX),
-              shift_i<CTRL>(c.pk, 0), shift_f<CTRL>(c.lsib, 0.0f), shift_f<CTRL>(c.lch, 0.0f)};
+  return Cand{shift_d<CTRL>(c.w), shift_d<CTRL>(c.base), shift_i<CTRL>(c.order), shift_i<CTRL>(c.pk),
+              shift_f<CTRL>(c.lsib), shift_f<CTRL>(c.lch)};
 }
 
 __device__ __forceinline__ double lane0_d(double x) {
