@@ -16,33 +16,44 @@
 //   S^T = K * Q^T over D = R + P, and O^T = V^T * P^T over keys (V = c_kv).
 //   Both run on v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32
 //   (fp32).
-// * A workgroup is 4 waves (one per SIMD) and owns a tile of 128 rows of one
-//   sequence and one split of its key range.  Each wave owns 32 rows: their Q
-//   fragments stay in registers for the whole key loop and their 32 x R fp32
-//   output accumulators live in the accumulation registers.
+// * A workgroup is 4 waves (one per SIMD) and owns a tile of rows of one
+//   sequence and one split of its key range, in one of three layouts:
+//   1: 128 rows, each wave 32 rows and all R output columns (its Q fragments
+//      in registers for the whole key loop, its 32 x R fp32 accumulators in
+//      the accumulation registers, one block parked in LDS while the score
+//      tile is alive);
+//   2: 64 rows, each pair of waves shares 32 rows, computes the same scores
+//      and splits the output columns (half the value work per wave, no
+//      parking, a deeper tile ring);
+//   3: as 2, but the pair splits the score contraction by depth and adds the
+//      partner's partial scores through LDS.
 // * Keys stream through LDS in tiles of 32 rows x (R + P); all four waves read
-//   the same tile, so each K/V byte crosses L2 -> LDS once per 128 query rows.
+//   the same tile, so each K/V byte crosses L2 -> LDS once per workgroup.
 // * Computing S^T (keys along the MFMA rows) leaves every lane holding 16
 //   scores of ONE query row.  The row max needs one cross-half exchange, the
 //   running sum needs none until the end, and the softmax weights are already
 //   laid out as the B operand of the value contraction: no shuffles.
 // * Online softmax in the log2 domain against a per-row reference max fixed at
 //   the first visible key.  Weights stay below 2^32 for any realistic score
-//   range, so the 32 x R accumulators are never rescaled (a rescale would need
-//   a read-modify-write of all 256 accumulation registers every tile).  A row
-//   whose max outgrows its reference by more than that makes its wave redo the
+//   range, so the accumulators are never rescaled (a rescale would need a
+//   read-modify-write of every accumulation register every tile).  A row whose
+//   max outgrows its reference by more than that makes its wave redo the
 //   split once against the exact max, which it has tracked meanwhile.
-// * K/V tiles rotate through three LDS buffers and are copied straight from
-//   HBM into LDS with buffer_load_dwordx4 ... lds, so staging costs no
-//   registers and two tile copies are in flight while one tile is computed.  The value operand is read with the gfx950
-//   transposing LDS load (ds_read_b64_tr_b16) from the same key-major tile the
-//   score operand uses.
+// * K/V tiles rotate through three (layouts 1, 3) or four (layout 2) LDS
+//   buffers and are copied straight from HBM into LDS with
+//   buffer_load_dwordx4 ... lds, so staging costs no registers and all but one
+//   buffer are in flight while one tile is computed.  The value operand is
+//   read with the gfx950 transposing LDS load (ds_read_b64_tr_b16) from the
+//   same key-major tile the score operand uses.
 // * Masking costs nothing on prefix tiles; only tiles that reach the tree
-//   segment or the end of the split test bits.
+//   segment or the end of the split test bits.  The visibility words come from
+//   the caller, or, given parent pointers, from a pointer doubling that the
+//   workgroups whose split reaches the tree run before their key loop.
 // * Split-prefix: a sequence's keys are cut into splits of split_keys keys;
-//   each split writes a normalised partial and its log-sum-exp, and the merge
-//   kernel recombines them.  With a single split the verify kernel writes the
-//   final output directly.
+//   each split writes a normalised partial (bf16 for bf16 inputs, float32 on
+//   request, with streaming stores) and its log-sum-exp, and the merge kernel
+//   recombines them.  With a single split the verify kernel writes the final
+//   output directly.
 // * Workgroup indices are remapped so the workgroups on one XCD take
 //   consecutive work units (all row tiles of one key split), which keeps
 //   their shared K/V stream in that XCD's L2.
@@ -52,13 +63,13 @@
 
 namespace kdt {
 
-constexpr int kBM = 128;          // query rows per workgroup
+constexpr int kBM = 128;          // query rows per workgroup in layout 1 (half in layouts 2, 3)
 constexpr int kBN = 32;           // keys per LDS tile
 constexpr int kThreads = 256;     // 4 waves
 constexpr int kCU = 256;          // MI355X compute units (split heuristic)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRefSlack = 32.0f;
+constexpr float kRefSlack = 32.0f;   // max weight 2^32 against the reference (log2 units)
 // LDS operand fragments kept in flight ahead of the MFMA that consumes them
 // (LDS latency under load is a few hundred cycles, one MFMA about forty).
 #ifndef KDT_SCORE_PREFETCH
@@ -66,7 +77,7 @@ constexpr float kRefSlack = 32.0f;
 #endif
 #ifndef KDT_VALUE_PREFETCH
 #define KDT_VALUE_PREFETCH 2
-#endif    // max weight 2^32 against the reference (log2 units)
+#endif
 
 template <typename T>
 struct Mfma;
