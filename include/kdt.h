@@ -125,7 +125,8 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  * KDT_SEQ_BAD_LEN.
  *
  * Split-prefix execution.  The key range of each sequence is cut into splits of
- * `split_keys` keys (0 = the library's choice; otherwise a multiple of 64).
+ * `split_keys` keys (0 = the library's choice; otherwise a multiple of 32, the
+ * key tile).
  * Each split produces a normalised partial output and its log-sum-exp in the
  * workspace; a second kernel merges the splits by the log-sum-exp identity.
  * When every sequence fits in one split the merge is skipped and the first
@@ -157,7 +158,7 @@ typedef struct {
   void* out; int64_t out_sb, out_st, out_sh;
   float* lse;                          /* device float32 [B, q_len, H] */
   int32_t* seq_status;                 /* device int32 [B], nullable */
-  int32_t split_keys;                  /* 0 = auto, else a multiple of 64 */
+  int32_t split_keys;                  /* 0 = auto, else a multiple of 32 */
   int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split */
   int32_t partials_f32;                /* 1 = keep split partial outputs in float32; 0 = in the input dtype */
   const int32_t* parents;              /* device int32 [B, q_len]; used when vis is NULL */
@@ -179,7 +180,7 @@ typedef struct {
  * rounding of the output's own precision, which halves the partial traffic).
  * Sequence b uses splits 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1. */
 typedef struct {
-  int32_t split_keys;          /* keys per split (multiple of 64) */
+  int32_t split_keys;          /* keys per split (multiple of 32) */
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
   int32_t rows;                /* q_len * H */
   int32_t direct;              /* 1: max_splits == 1, no partials, no merge */

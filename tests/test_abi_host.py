@@ -62,7 +62,7 @@ def test_plan_sizes_and_layout():
     assert rc == 0
     M = 65 * 16
     assert p.rows == M
-    assert p.split_keys % 64 == 0 and p.split_keys >= 64
+    assert p.split_keys % 32 == 0 and p.split_keys >= 32
     assert p.max_splits == -(-(4096 + 65) // p.split_keys)
     assert p.direct == (1 if p.max_splits == 1 else 0)
     nblk = -(-M // 32)
@@ -83,7 +83,8 @@ def test_plan_sizes_and_layout():
 @pytest.mark.parametrize("field,value,code", [
     ("q_lat", 0, 1), ("lse", 0, 1), ("B", 0, 1), ("H", -1, 1),
     ("capacity", 4100, 1),                 # below max_prefix_len + q_len
-    ("split_keys", 100, 1),                # not a multiple of 64
+    ("split_keys", 100, 1),                # not a multiple of 32 (the key tile)
+    ("split_keys", 48, 1),
     ("softmax_scale", 0.0, 1),
     ("q_len", 129, 2),                     # beyond two mask words
     ("R", 256, 2), ("dtype", 7, 2),

@@ -62,7 +62,7 @@ def test_bf16_full_parity_tree_shapes(q, tree):
 
 
 @pytest.mark.parametrize("partials_f32", [False, True])
-@pytest.mark.parametrize("split_keys", [0, 64, 128, 192, 1024])
+@pytest.mark.parametrize("split_keys", [0, 32, 64, 96, 128, 192, 288, 1024])
 def test_bf16_split_counts_agree(split_keys, partials_f32):
     cfg = small_cfg(q=33, tree="deep_chain", prefix=("uniform", 40, 700), B=3, H=16, index=31)
     inp = synth.generate(cfg)
@@ -154,7 +154,8 @@ def _growing_scores_inputs(q, H, L, B=2, index=63):
     return inp
 
 
-@pytest.mark.parametrize("layout,split_keys", [(1, 0), (2, 0), (3, 0), (1, 256), (2, 256), (3, 256), (2, 64), (3, 64)])
+@pytest.mark.parametrize("layout,split_keys", [(1, 0), (2, 0), (3, 0), (1, 256), (2, 256), (3, 256), (2, 64), (3, 64),
+                                               (1, 32), (2, 96)])
 def test_redo_when_scores_outgrow_the_reference(layout, split_keys):
     inp = _growing_scores_inputs(q=9, H=16, L=900)
     g = GpuInputs(inp)
@@ -308,7 +309,7 @@ def test_bad_prefix_lengths_are_skipped_and_flagged():
 
 
 @pytest.mark.parametrize("q,H", [(3, 16), (4, 16), (65, 1)])
-@pytest.mark.parametrize("split_keys", [0, 64, 4096])
+@pytest.mark.parametrize("split_keys", [0, 32, 64, 4096])
 def test_short_row_counts_all_split_modes(q, H, split_keys):
     # q*H = 48 (second 32-row block half filled), 64 (exactly two blocks: the
     # column-split layout of a workgroup) and 65 (just past it, the full

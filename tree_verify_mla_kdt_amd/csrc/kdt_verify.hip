@@ -984,7 +984,7 @@ static int validate(const kdt_verify_desc* d) {
     return KDT_ERR_INVALID_ARG;
   if (d->max_prefix_len < 0 || d->capacity < (int64_t)d->max_prefix_len + d->q_len)
     return KDT_ERR_INVALID_ARG;
-  if (d->split_keys < 0 || (d->split_keys % 64) != 0) return KDT_ERR_INVALID_ARG;
+  if (d->split_keys < 0 || (d->split_keys % kBN) != 0) return KDT_ERR_INVALID_ARG;
   if (d->layout < 0 || d->layout > 3) return KDT_ERR_INVALID_ARG;
   if (d->partials_f32 != 0 && d->partials_f32 != 1) return KDT_ERR_INVALID_ARG;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
@@ -1012,20 +1012,24 @@ static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 // layout and split size.  Workgroups run one per compute unit, so G of them
 // take ceil(G / kCU) rounds; a round costs its key tiles plus a start-up (the
 // burst of query and first-tile loads), every partial costs its write and its
-// read in the merge, and splitting at all adds the merge launch.  The
-// constants are fitted to measurements at R = 512, P = 64 (a 128-row tile of
-// 32 keys about 2.05 us, a 128-row float32 partial about 0.12 us) and scale
-// with the contraction work of one wave and with the bytes a partial holds.
+// read in the merge, and splitting at all adds the merge launch plus one
+// memory round trip per sixteen splits (the merge consumes them sixteen at a
+// time).  The constants are fitted to a measured grid of split sizes and
+// layouts over six workloads at R = 512, P = 64 (a 128-row tile of 32 keys
+// about 1.7 us, a start-up about 4 us, a 128-row float32 partial about 0.2 us)
+// and scale with the contraction work of one wave and with the bytes a
+// partial holds.
 static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R, int P, int layout,
                           int part_bytes) {
   const int rows = layout_rows(layout);
-  const double t_tile = 2.05 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
-  const double t_start = 6.0;
-  const double t_part = 0.12 * rows / kBM * R / 512.0 * part_bytes / 4.0;
-  const double t_merge = 5.0;
+  const double t_tile = 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+  const double t_start = 4.0;
+  const double t_part = 0.2 * rows / kBM * R / 512.0 * part_bytes / 4.0;
+  const double t_merge = 3.0, t_merge_batch = 2.0;
   const int64_t ns = (n_max + sk - 1) / sk;
   const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
-  return rounds * ((sk / kBN) * t_tile + t_start) + (ns > 1 ? ns * n_seq_tiles * t_part + t_merge : 0.0);
+  const double merge = ns > 1 ? ns * n_seq_tiles * t_part + t_merge + t_merge_batch * (double)((ns + 15) / 16) : 0.0;
+  return rounds * ((sk / kBN) * t_tile + t_start) + merge;
 }
 
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
@@ -1044,7 +1048,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
     const int64_t n_seq_tiles = (int64_t)d->B * ((M + layout_rows(layout) - 1) / layout_rows(layout));
     const int64_t n_tiles = (n_max + kBN - 1) / kBN;
     for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
-      int64_t k = d->split_keys ? d->split_keys : ((n_max + s - 1) / s + 63) / 64 * 64;
+      int64_t k = d->split_keys ? d->split_keys : ((n_max + s - 1) / s + kBN - 1) / kBN * kBN;
       if (!d->split_keys && (n_max + k - 1) / k != s) continue;   // covered by a smaller s
       const double c = launch_cost(n_seq_tiles, n_max, k, d->R, d->P, layout, elem_size(part_dtype));
       if (c < best * 0.999) {                 // ties go to fewer splits, then layout 1
