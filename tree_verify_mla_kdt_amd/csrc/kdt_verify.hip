@@ -891,7 +891,12 @@ struct PartLoad<__bf16> {
   __device__ static __forceinline__ float get(const raw& r, int i) { return (float)r[i]; }
 };
 
-template <typename T, typename PT>
+// WIDE: one (sequence, block, column group) per workgroup, its splits cut
+// into four contiguous ranges, one per wave, which all load at once; the four
+// partial states (max, sum, weighted columns) are then combined through LDS
+// by wave 0.  Used when there are more splits than one wave loads in one
+// round trip.  Otherwise one item per wave.
+template <typename T, typename PT, bool WIDE>
 __global__ __launch_bounds__(256) void merge_kernel(
     const PT* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
     int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys,
@@ -900,37 +905,43 @@ __global__ __launch_bounds__(256) void merge_kernel(
   constexpr int NV = PartLoad<PT>::NV;
   constexpr int CW = 2 * NV;                    // columns per wave
   typedef typename PartLoad<PT>::raw raw;
+  __shared__ float s_st[WIDE ? 4 * (NV + 2) * 64 : 1];   // per wave: max, sum, NV columns per lane
   const int n_cg = R / CW;
-  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t wid = WIDE ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
   const int lane = threadIdx.x & 63, hh = lane >> 5;
-  if (wid >= (int64_t)B * n_blk * n_cg) return;
+  if (wid >= (int64_t)B * n_blk * n_cg) return;  // (uniform over the workgroup when WIDE)
   const int cg = (int)(wid % n_cg);
   const int64_t bblk = wid / n_cg;
   const int blk = (int)(bblk % n_blk), b = (int)(bblk / n_blk);
   const int M = q * H;
   const int m = blk * 32 + (lane & 31);
-  if (m >= M) return;
+  const bool row_ok = m < M;
+  if (!WIDE && !row_ok) return;
   int ns = max_splits;
   if (split_keys > 0) {
     const int64_t n = (int64_t)prefix_lens[b] + q;
     ns = (int)((n + split_keys - 1) / split_keys);
     ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
   }
-  const float* pl = part_lse + (int64_t)b * max_splits * M + m;
+  const int per = WIDE ? (ns + 3) / 4 : ns;
+  const int kb = WIDE ? wave * per : 0;
+  const int ke = row_ok ? min(ns, kb + per) : kb;   // padding rows of a wide block load nothing
+  const float* pl = part_lse + (int64_t)b * max_splits * M + (row_ok ? m : 0);
   const int64_t split_stride = (int64_t)n_blk * 32 * R;
   const PT* po = part_o + ((int64_t)b * max_splits * n_blk + blk) * (32 * R) + 32 * CW * cg + NV * lane;
   float mx = -INFINITY, z = 0.0f;
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-  for (int k0 = 0; k0 < ns; k0 += U) {
+  for (int k0 = kb; k0 < ke; k0 += U) {
     float lk[U];
     raw ok[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int k = k0 + j;
-      lk[j] = k < ns ? pl[(int64_t)k * M] : -INFINITY;
-      if (k < ns) ok[j] = *reinterpret_cast<const raw*>(po + k * split_stride);
+      lk[j] = k < ke ? pl[(int64_t)k * M] : -INFINITY;
+      if (k < ke) ok[j] = *reinterpret_cast<const raw*>(po + k * split_stride);
     }
     float cm = lk[0];
 #pragma unroll
@@ -949,6 +960,33 @@ __global__ __launch_bounds__(256) void merge_kernel(
       z += w;
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = live ? acc[i] + w * PartLoad<PT>::get(ok[j], i) : acc[i];
+    }
+  }
+  if constexpr (WIDE) {
+    float* st = s_st + wave * (NV + 2) * 64 + lane;
+    st[0] = mx;
+    st[64] = z;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) st[64 * (2 + i)] = acc[i];
+    __syncthreads();
+    if (wave != 0 || !row_ok) return;
+    // combine the four states against their common max (a wave without a
+    // finite split has max -inf and no weight)
+    float mw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mw[w] = s_st[w * (NV + 2) * 64 + lane];
+    const float mt = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    mx = mt;
+    z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* sw = s_st + w * (NV + 2) * 64 + lane;
+      const float f = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - mt);
+      z += f * sw[64];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] += f * sw[64 * (2 + i)];
     }
   }
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
@@ -1013,8 +1051,9 @@ static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 // take ceil(G / kCU) rounds; a round costs its key tiles plus a start-up (the
 // burst of query and first-tile loads), every partial costs its write and its
 // read in the merge, and splitting at all adds the merge launch plus one
-// memory round trip per sixteen splits (the merge consumes them sixteen at a
-// time).  The constants are fitted to a measured grid of split sizes and
+// memory round trip per batch of splits the merge loads at once (sixteen per
+// wave; up to sixty-four when a workgroup's four waves share the splits of
+// one item).  The constants are fitted to a measured grid of split sizes and
 // layouts over six workloads at R = 512, P = 64 (a 128-row tile of 32 keys
 // about 1.7 us, a start-up about 4 us, a 128-row float32 partial about 0.2 us)
 // and scale with the contraction work of one wave and with the bytes a
@@ -1028,7 +1067,8 @@ static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R,
   const double t_merge = 3.0, t_merge_batch = 2.0;
   const int64_t ns = (n_max + sk - 1) / sk;
   const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
-  const double merge = ns > 1 ? ns * n_seq_tiles * t_part + t_merge + t_merge_batch * (double)((ns + 15) / 16) : 0.0;
+  const int64_t batches = ns > 16 ? (ns + 63) / 64 : 1;
+  const double merge = ns > 1 ? ns * n_seq_tiles * t_part + t_merge + t_merge_batch * (double)batches : 0.0;
   return rounds * ((sk / kBN) * t_tile + t_start) + merge;
 }
 
@@ -1143,15 +1183,22 @@ static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, c
                           const int32_t* prefix_lens, int split_keys, void* out, int64_t osb, int64_t ost,
                           int64_t osh, float* lse, hipStream_t s) {
   const int n_blk = (q * H + 31) / 32;
-  const int64_t waves = (int64_t)B * n_blk * (R / (2 * PartLoad<PT>::NV));
-  const int64_t grid = (waves + 3) / 4;
+  const int64_t items = (int64_t)B * n_blk * (R / (2 * PartLoad<PT>::NV));
+  // more splits than one wave loads in one round trip: a workgroup per item
+  const bool wide = max_splits > 16;
+  const int64_t grid = wide ? items : (items + 3) / 4;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
-  if (dtype == KDT_BF16)
-    hipLaunchKernelGGL((merge_kernel<__bf16, PT>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q,
-                       H, R, n_blk, prefix_lens, split_keys, static_cast<__bf16*>(out), osb, ost, osh, lse);
-  else
-    hipLaunchKernelGGL((merge_kernel<float, PT>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q,
-                       H, R, n_blk, prefix_lens, split_keys, static_cast<float*>(out), osb, ost, osh, lse);
+#define KDT_MERGE_LAUNCH(TO, W)                                                                              \
+  hipLaunchKernelGGL((merge_kernel<TO, PT, W>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, \
+                     H, R, n_blk, prefix_lens, split_keys, static_cast<TO*>(out), osb, ost, osh, lse)
+  if (dtype == KDT_BF16) {
+    if (wide) KDT_MERGE_LAUNCH(__bf16, true);
+    else KDT_MERGE_LAUNCH(__bf16, false);
+  } else {
+    if (wide) KDT_MERGE_LAUNCH(float, true);
+    else KDT_MERGE_LAUNCH(float, false);
+  }
+#undef KDT_MERGE_LAUNCH
   return launch_status();
 }
 
