@@ -276,6 +276,30 @@ def main():
     torch.cuda.synchronize()
     split_ms = e0.elapsed_time(e1) / (reps * n_copies)
 
+    # --- one verify call (split + merge) on its own: per-call mean over one
+    # replay of a graph of n_copies calls, median and p90 over replays
+    verify_us = None
+    if not args.kernel_only:
+        def verify_only(i):
+            c = copies[i % n_copies]
+            kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
+                            cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
+                            split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
+                            parents=par_arg)
+        if args.separate_visibility:
+            kdt.build_visibility(parents, vis=vis, depth=depth)
+        g_ver = capture(verify_only, range(n_copies))
+        g_ver.replay()
+        samples = []
+        for _ in range(max(20, reps)):
+            e0.record(cur)
+            g_ver.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            samples.append(e0.elapsed_time(e1) * 1e3 / n_copies)
+        verify_us = {"median": float(np.median(samples)), "p90": float(np.percentile(samples, 90)),
+                     "samples": len(samples), "calls_per_sample": n_copies}
+
     # --- the visibility kernel on its own (the step derives the masks inside
     # the split kernel unless --separate-visibility)
     g_vis = capture(lambda i: kdt.build_visibility(parents, vis=vis, depth=depth), range(20))
@@ -387,6 +411,8 @@ def main():
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "verify_split_kernel", "kernel_ms": split_ms,
                      "flops_per_launch": flops, "visible_pairs": pairs},
+        "verify_attn_us": verify_us,
+        "verify_tree_tokens_per_s": (B * q / (verify_us["median"] * 1e-6)) if verify_us else None,
         "mfma_util": flops / (ms_per_step * 1e-3) / 1e12 / peak,
         "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
