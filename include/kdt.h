@@ -108,8 +108,9 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  *         or NULL: then `parents` (int32 [B, q_len] contiguous, as for
  *         kdt_build_visibility) is required and the split kernel derives the
  *         same masks itself, with the same treatment of invalid parents
- *         (flagged KDT_SEQ_BAD_TREE in seq_status); this saves the separate
- *         visibility launch.  When vis is given, parents is ignored.
+ *         (flagged KDT_SEQ_BAD_TREE in seq_status; a sequence skipped for its
+ *         prefix length is not examined); this saves the separate visibility
+ *         launch.  When vis is given, parents is ignored.
  *   out   [B, q_len, H, R]   in `dtype`, strides out_sb, out_st, out_sh
  *   lse   float32 [B, q_len, H] contiguous
  * `dtype` is the element type of q_lat, q_pe, c_kv, k_pe and out.  Arithmetic:
