@@ -200,15 +200,23 @@ def test_layout_forcing_and_validation():
         rows = 128 if layout == 1 else 64
         assert p.rows == 65 * 16 and rows in (64, 128)
     rc, p = _plan(_desc())
-    assert rc == 0 and p.layout in (1, 2)
+    assert rc == 0 and p.layout in (1, 2, 4)           # the planner never picks layout 3
+    rc, p = _plan(_desc(R=64, P=16, q_lat_sh=64, q_lat_st=16 * 64, q_lat_sb=65 * 16 * 64,
+                        q_pe_sh=16, q_pe_st=16 * 16, q_pe_sb=65 * 16 * 16, c_kv_ss=80, k_pe_ss=80,
+                        c_kv_sb=4224 * 80, k_pe_sb=4224 * 80, out_sh=64, out_st=16 * 64, out_sb=65 * 16 * 64))
+    assert rc == 0 and p.layout in (1, 2)              # layout 4 only for the rank-512 shape
     rc, p = _plan(_desc(layout=3))            # depth-split pairs: bf16, R = 512, P = 64
     assert rc == 0 and p.layout == 3
     rc, p = _plan(_desc(layout=3, R=64, P=16))
     assert rc == 2
-    rc, p = _plan(_desc(layout=4))
+    rc, p = _plan(_desc(layout=4))            # two key streams: bf16, R = 512, P = 64
+    assert rc == 0 and p.layout == 4
+    rc, p = _plan(_desc(layout=4, R=64, P=16))
+    assert rc == 2
+    rc, p = _plan(_desc(layout=5))
     assert rc == 1
     rc, p = _plan(_desc(layout=-1))
     assert rc == 1
-    # AR decoding (64 rows) plans the column-split layout
+    # AR decoding (64 rows) plans a 64-row layout (two key streams at rank 512)
     rc, p = _plan(_desc(q_len=1, H=64, max_prefix_len=32768, capacity=32769))
-    assert rc == 0 and p.layout == 2
+    assert rc == 0 and p.layout == 4

@@ -105,7 +105,7 @@ def test_strided_fused_and_separate_caches():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("layout", [1, 2, 3])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4])
 def test_query_layouts_give_identical_results(layout):
     """Queries with padded rows (one uniform row stride larger than R) and in a
     head-major buffer (token stride smaller than the head stride) give the
@@ -154,8 +154,8 @@ def _growing_scores_inputs(q, H, L, B=2, index=63):
     return inp
 
 
-@pytest.mark.parametrize("layout,split_keys", [(1, 0), (2, 0), (3, 0), (1, 256), (2, 256), (3, 256), (2, 64), (3, 64),
-                                               (1, 32), (2, 96)])
+@pytest.mark.parametrize("layout,split_keys", [(1, 0), (2, 0), (3, 0), (4, 0), (1, 256), (2, 256), (3, 256), (4, 256),
+                                               (2, 64), (3, 64), (4, 64), (1, 32), (2, 96), (4, 32), (4, 96)])
 def test_redo_when_scores_outgrow_the_reference(layout, split_keys):
     inp = _growing_scores_inputs(q=9, H=16, L=900)
     g = GpuInputs(inp)
@@ -322,7 +322,7 @@ def test_short_row_counts_all_split_modes(q, H, split_keys):
     check_close("bf16", o, ro, l, rl, f"q={q} H={H} split_keys={split_keys}")
 
 
-@pytest.mark.parametrize("layout", [1, 2, 3])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4])
 @pytest.mark.parametrize("q,H,tree", [(1, 16, "chain"), (17, 16, "uniform"), (65, 16, "best_first"),
                                       (33, 3, "deep_chain")])
 def test_forced_layouts_match_oracle(layout, q, H, tree):
@@ -339,14 +339,14 @@ def test_config_max_budget_all_layouts_agree():
     inp = synth.generate(synth.CONFIGS["max_budget"])
     g = GpuInputs(inp)
     ro, rl = oracle_full(inp)
-    for layout in (1, 2, 3):
+    for layout in (1, 2, 3, 4):
         o, l = run_gpu(g, layout=layout)
         check_close("bf16", o, ro, l, rl, f"max_budget layout {layout}")
 
 
 # ---------------------------------------------------------------- masks derived from parents
 
-@pytest.mark.parametrize("layout", [0, 1, 2, 3])
+@pytest.mark.parametrize("layout", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("q,H,tree,split_keys", [(1, 16, "chain", 0), (17, 16, "uniform", 0),
                                                  (65, 16, "best_first", 64), (100, 4, "uniform", 0),
                                                  (128, 2, "deep_chain", 128), (33, 3, "deep_chain", 0)])

@@ -330,18 +330,29 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int KW = MM::KW, KMF = MM::KMF;
   constexpr int NCHUNK = D / KMF;             // MFMA steps of the score contraction
   constexpr int NB = R / 32;                  // 32-wide output column blocks
-  static_assert(CS == 1 || CS == 2 || CS == 3, "layout");
+  static_assert(CS >= 1 && CS <= 4, "layout");
   // CS = 3: the 64-row layout with the score contraction split by depth: the
   // two waves of a pair each contract half of the R + P columns, exchange
   // their partial scores through LDS and add them, so no score MFMA is done
   // twice; the softmax is duplicated as in CS = 2 and the values split by
   // columns.
   constexpr bool DS = (CS == 3);
-  constexpr int CSC = DS ? 2 : CS;            // column split of the output
+  // CS = 4: 64 rows, two key streams.  Wave w owns row block w / 2 and all R
+  // output columns, and takes every other key tile (stream w % 2), so no
+  // contraction step is done twice and each tile is read by two waves; the
+  // two streams' softmax states and accumulators are combined once, after
+  // the last tile.  The query's rope part is read from LDS every tile, which
+  // frees the registers layout 1 gets by parking an accumulator block.
+  constexpr bool KS = (CS == 4);
+  constexpr int CSC = DS ? 2 : (KS ? 1 : CS); // column split of the output
   static_assert(!DS || (NCHUNK % 2 == 0 && KW == 8), "depth split: bf16, even contraction steps");
-  constexpr int NQF = DS ? NCHUNK / 2 : NCHUNK;   // query fragments (score steps) of one wave
+  static_assert(!KS || (KW == 8 && R % KMF == 0), "key streams: bf16");
+  // query fragments held in registers by one wave (score steps)
+  constexpr int NQF = DS ? NCHUNK / 2 : (KS ? R / KMF : NCHUNK);
+  constexpr int NQR = NCHUNK - R / KMF;       // rope steps (read from LDS when KS)
+  constexpr int NSTEP = KS ? NCHUNK : NQF;    // score steps of one wave
   constexpr int NBL = NB / CSC;               // output column blocks of one wave
-  constexpr int BM = kBM / CSC;               // query rows per workgroup
+  constexpr int BM = KS ? kBM / 2 : kBM / CSC;    // query rows per workgroup
   constexpr int PV_STEPS = kBN / KMF;         // MFMA steps of the value contraction per tile
   constexpr int RC = R * (int)sizeof(T) / 16; // 16-byte chunks of c_kv per key
   constexpr int PC = P * (int)sizeof(T) / 16; // 16-byte chunks of k_pe per key
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // the accumulator stash also needs LDS, four otherwise.  The copies are
   // inline asm the compiler does not track, so one array indexed with
   // constants serves.
-  constexpr bool STASH_LDS = (NBL == 16);
+  constexpr bool STASH_LDS = (NBL == 16) && !KS;
   constexpr int NBUF = (STASH_LDS || DS) ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) char s_tiles[NBUF][BUF_BYTES];
   // vmcnt per tile copy on every wave (a wave that issued more waits a
@@ -362,8 +373,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   static_assert(STAGE_LOADS * (NBUF - 2) < 64, "vmcnt range");
   __shared__ int s_dead;
   // per-wave pointer-doubling area when the masks are derived from parents
-  __shared__ uint64_t s_vm[kThreads / kWave][2 * KDT_MAX_Q_LEN];
-  __shared__ int s_vj[kThreads / kWave][KDT_MAX_Q_LEN];
+  // (one area, run by wave 0, in the key-stream layout, whose LDS is full)
+  constexpr int NVA = KS ? 1 : kThreads / kWave;
+  __shared__ uint64_t s_vm[NVA][2 * KDT_MAX_Q_LEN];
+  __shared__ int s_vj[NVA][KDT_MAX_Q_LEN];
+  // key streams: the rope part of each row block's query fragments, one
+  // 16-byte fragment per (row block, step, lane)
+  __shared__ __attribute__((aligned(16))) char s_qpe[KS ? 2 * NQR * 64 * 16 : 16];
   // depth split: each wave's partial score tile, 16 floats per lane
   __shared__ __attribute__((aligned(16))) f32x4 s_sx[DS ? 4 * kThreads : 1];
   // One accumulator block per lane parks here while the score tile is alive
@@ -379,7 +395,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int rb = wave / CSC, chalf = wave % CSC;   // row block, output column half (and depth half)
+  // row block, output column half (and depth half), key stream
+  const int rb = KS ? (wave >> 1) : wave / CSC, chalf = KS ? 0 : wave % CSC, kp = KS ? (wave & 1) : 0;
   const int c0 = DS ? chalf * NQF : 0;          // first score step of this wave
   const int m = rt * BM + rb * 32 + r;        // this lane's query row
   const bool row_ok = m < a.M;
@@ -431,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // two key tiles, into the two ring buffers the first tiles leave free, and
   // each wave then reads its fragments with the score operand's LDS pattern:
   // 1 KB contiguous per copy instead of 32 scattered rows per load.
-  constexpr bool Q_VIA_LDS = (CS == 2) && (KW == 8) && (NBUF == 4);
+  constexpr bool Q_VIA_LDS = (CS == 2 || KS) && (KW == 8) && (NBUF == 4);
   static_assert(!Q_VIA_LDS || BM == 2 * kBN, "query staging: two 32-row blocks per workgroup");
   const bool q_lds = Q_VIA_LDS && a.q_rows_uniform;
   frag qf[NQF];
@@ -460,6 +477,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       const int c = c0 + j;
       if (c < R / KMF) qf[j] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
       else qf[j] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
+    }
+    if constexpr (KS) {
+      // the rope fragments go to LDS (one wave of each row block writes them)
+      if (kp == 0) {
+#pragma unroll
+        for (int i = 0; i < NQR; ++i)
+          *reinterpret_cast<frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16) =
+              *reinterpret_cast<const frag*>(qp + i * KMF + hh * KW);
+      }
     }
   }
   uint64_t vw0 = ~0ull, vw1 = ~0ull;
@@ -558,11 +584,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   auto derive_vis = [&]() {
     if (!a.parents || k_end <= L) return;
     uint64_t m0[2], m1[2];
-    const bool bad_tree = wave_ancestor_masks(par_v, a.q, s_vm[wave], s_vj[wave], lane, m0, m1);
-    if (__any(bad_tree) && lane == 0 && wave == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_TREE);
+    const int va = KS ? 0 : wave;
+    if (!KS || wave == 0) {
+      const bool bad_tree = wave_ancestor_masks(par_v, a.q, s_vm[va], s_vj[va], lane, m0, m1);
+      if (__any(bad_tree) && lane == 0 && wave == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_TREE);
+    }
+    if constexpr (KS) {
+      wait_lds();
+      tile_barrier();
+    }
     if (row_ok) {
-      vw0 = s_vm[wave][2 * t];
-      vw1 = s_vm[wave][2 * t + 1];
+      vw0 = s_vm[va][2 * t];
+      vw1 = s_vm[va][2 * t + 1];
     }
   };
 
@@ -576,7 +609,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
       for (int c = 0; c < NCHUNK; ++c) {
         const char* src = (c < R / KMF) ? qbuf + qk_lat[c % QB] + 16 * LSW * (c / QB) : qbuf + qk_pe[c - R / KMF];
-        qf[c] = *reinterpret_cast<const frag*>(src);
+        if constexpr (KS) {
+          if (c < NQF) qf[c] = *reinterpret_cast<const frag*>(src);
+          else if (kp == 0)
+            *reinterpret_cast<frag*>(s_qpe + ((rb * NQR + (c - NQF)) * 64 + lane) * 16) =
+                *reinterpret_cast<const frag*>(src);
+        } else {
+          qf[c] = *reinterpret_cast<const frag*>(src);
+        }
       }
       // every wave has its fragments before the buffers take key tiles again
       wait_vmem_lds<0>();
@@ -606,6 +646,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // ring buffer; the tile's first key is kt.  The copy of the first st_rows
   // rows of tile st_tile into st_buf is issued piece by piece between the
   // value MFMAs.
+  // Key streams: the next pair of tiles (copied between this step's score
+  // MFMAs; rows 0 = no such tile).
+  int ks_t0 = 0, ks_t1 = 0, ks_r0 = 0, ks_r1 = 0;
+  char* ks_b0 = nullptr;
+  char* ks_b1 = nullptr;
   auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, char* st_buf)
                        __attribute__((always_inline)) {
     const int kt = k_begin + tile * kBN;
@@ -628,19 +673,46 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         return buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
       }
     };
-    constexpr int QPF = NQF < KDT_SCORE_PREFETCH ? NQF : KDT_SCORE_PREFETCH;
+    // (key streams hold no accumulator block in LDS, so their scores take
+    // registers and the operand queues are shorter)
+    constexpr int QPF0 = KS ? 2 : KDT_SCORE_PREFETCH;
+    constexpr int QPF = NSTEP < QPF0 ? NSTEP : QPF0;
     frag kf[QPF];
 #pragma unroll
     for (int j = 0; j < QPF; ++j) kf[j] = *reinterpret_cast<const frag*>(score_src(c0 + j));
+    // key streams: this row block's rope fragments of the query, read from
+    // LDS QPF steps before their MFMA
+    auto qpe_src = [&](int i) { return reinterpret_cast<const frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16); };
+    frag qq[KS ? QPF : 1];
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NQF; ++j) {
+    for (int j = 0; j < NSTEP; ++j) {
       const frag cur = kf[j % QPF];
-      if (j + QPF < NQF) kf[j % QPF] = *reinterpret_cast<const frag*>(score_src(c0 + j + QPF));
-      s = MM::mma(cur, qf[j], s);
+      if (j + QPF < NSTEP) kf[j % QPF] = *reinterpret_cast<const frag*>(score_src(c0 + j + QPF));
+      if constexpr (KS) {
+        static_assert(!KS || NQF >= QPF, "rope fragments are queued behind the register ones");
+        // the slot refilled now is the one this step consumes: take it first
+        const frag qcur = j < NQF ? qf[j < NQF ? j : 0] : qq[j % QPF];
+        if (j + QPF >= NQF && j + QPF < NSTEP) qq[(j + QPF) % QPF] = *qpe_src(j + QPF - NQF);
+        s = MM::mma(cur, qcur, s);
+      } else {
+        s = MM::mma(cur, qf[j], s);
+      }
       fence_mem_mfma();
+      if constexpr (KS) {
+        // the next pair's copies, one wave-load at a time between these MFMAs
+        constexpr int NP2 = 2 * NPIECE;
+#pragma unroll
+        for (int pc = j * NP2 / NSTEP; pc < (j + 1) * NP2 / NSTEP; ++pc) {
+          if (pc < NPIECE) {
+            if (ks_r0 > 0) stage_piece(ks_t0, ks_r0, ks_b0, pc);
+          } else {
+            if (ks_r1 > 0) stage_piece(ks_t1, ks_r1, ks_b1, pc - NPIECE);
+          }
+        }
+      }
     }
     if constexpr (DS) {
       // add the partner's half of the contraction (the pair's waves hold the
@@ -742,9 +814,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       acc[db] = MM::mma(vq[i % (VPF + 1)], pfr[c], acc[db]);
       fence_mem_mfma();
       // copy pieces [i * NPIECE / STEPS, (i + 1) * NPIECE / STEPS) follow this MFMA
+      if constexpr (!KS) {
 #pragma unroll
-      for (int pc = i * NPIECE / STEPS; pc < (i + 1) * NPIECE / STEPS; ++pc)
-        stage_piece(st_tile, st_rows, st_buf, pc);
+        for (int pc = i * NPIECE / STEPS; pc < (i + 1) * NPIECE / STEPS; ++pc)
+          stage_piece(st_tile, st_rows, st_buf, pc);
+      }
     }
   };
 
@@ -779,6 +853,48 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       wait_vmem_lds<STAGE_LOADS * (NBUF - 2)>();
       tile_barrier();
     };
+    if constexpr (KS) {
+      // Key streams: step s computes tiles 2s (waves of stream 0) and 2s + 1
+      // (stream 1) from one buffer pair while the next pair's copies go to
+      // the other pair of buffers, which the step before has finished
+      // reading.  Each step waits for all of its own copies and meets the
+      // workgroup at one barrier, after which every copy of the pair has
+      // landed and every wave is done with the previous pair.
+      if (pass == 0 && spec_ok) {
+        wait_vmem_lds<0>();
+      } else {
+        wait_vmem_lds<0>();
+        stage(0, s_tiles[0]);
+        if (n_tiles > 1) stage(1, s_tiles[1]);
+      }
+      const int n_steps = (n_tiles + 1) / 2;
+      auto tile_rows = [&](int tt) { return tt < n_tiles ? min(kBN, k_end - (k_begin + tt * kBN)) : 0; };
+#pragma unroll 1
+      for (int s0 = 0; s0 < n_steps; s0 += 2) {
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const int st = s0 + hs;
+          if (st >= n_steps) break;
+          wait_vmem_lds<0>();
+          tile_barrier();
+          ks_t0 = 2 * st + 2;
+          ks_t1 = 2 * st + 3;
+          ks_r0 = tile_rows(ks_t0);
+          ks_r1 = tile_rows(ks_t1);
+          ks_b0 = s_tiles[2 - 2 * hs];
+          ks_b1 = s_tiles[3 - 2 * hs];
+          const int tt = 2 * st + kp;
+          if (compute && tt < n_tiles) {
+            tile_body(tt, s_tiles[2 * hs + kp], 0, 0, nullptr);
+          } else {
+            if (ks_r0 > 0) stage_rows(ks_t0, ks_b0, ks_r0);
+            if (ks_r1 > 0) stage_rows(ks_t1, ks_b1, ks_r1);
+          }
+        }
+      }
+      wait_vmem_lds<0>();
+      continue;
+    }
     // The first tile, the query fragments and the visibility words are all
     // waited for here, visibly to the compiler, so that it places no wait for
     // them inside the loop (where it would also drain the tile copies).
@@ -813,6 +929,63 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     wait_vmem_lds<0>();                       // the last (dummy) copies land before anything else
   }
 
+  // Key streams: the two waves of a row block share the output, stream s
+  // writing column half s.  Each leaves the other half of its accumulators,
+  // its reference and its sum in the (now idle) tile ring for its partner,
+  // then rescales both streams to the larger reference as it writes its half
+  // (the partner's accumulators are read block by block in the loops below).
+  constexpr int XS = (NBL / 2 * 16 + 2) * 64; // floats per wave
+  float* xw = reinterpret_cast<float*>(&s_tiles[0][0]) + wave * XS;
+  const float* xr = reinterpret_cast<const float*>(&s_tiles[0][0]) + (wave ^ 1) * XS;
+  float f0 = 1.0f, f1 = 0.0f;
+  if constexpr (KS) {
+    tile_barrier();                           // every wave is done with the ring
+#pragma unroll
+    for (int db = 0; db < NBL; ++db) {
+      if ((db >> 3) == kp) continue;          // (the half this wave keeps)
+      // straight from the accumulation registers (a copy through ordinary
+      // registers made the compiler spill accumulators to scratch); the
+      // four groups of block db sit 1 KB apart, each lane's 16 bytes
+      // consecutive across lanes
+      const uint32_t ad = lds_addr(xw + (((db & 7) * 4) * 64 + lane) * 4);
+      asm volatile(
+          "ds_write_b128 %0, %1\n\t"
+          "ds_write_b128 %0, %2 offset:1024\n\t"
+          "ds_write_b128 %0, %3 offset:2048\n\t"
+          "ds_write_b128 %0, %4 offset:3072"
+          :
+          : "v"(ad), "a"(__builtin_shufflevector(acc[db], acc[db], 0, 1, 2, 3)),
+            "a"(__builtin_shufflevector(acc[db], acc[db], 4, 5, 6, 7)),
+            "a"(__builtin_shufflevector(acc[db], acc[db], 8, 9, 10, 11)),
+            "a"(__builtin_shufflevector(acc[db], acc[db], 12, 13, 14, 15))
+          : "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    xw[NBL / 2 * 16 * 64 + lane] = m_ref;
+    xw[NBL / 2 * 16 * 64 + 64 + lane] = l_run;
+    wait_lds();                               // (also the asm stores above)
+    tile_barrier();
+    const float m1 = xr[NBL / 2 * 16 * 64 + lane], l1 = xr[NBL / 2 * 16 * 64 + 64 + lane];
+    const float mt = fmaxf(m_ref, m1);
+    f0 = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - mt);
+    f1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - mt);
+    l_run = l_run * f0 + l1 * f1;
+    m_ref = mt;
+  }
+  // the output blocks this wave writes (key streams: its column half)
+  auto own_block = [&](int db) { return !KS || (db >> 3) == kp; };
+  // accumulator (db, 4 g + e) of this lane, both key streams combined
+  auto acc_of = [&](int db, int g, f32x4& v) __attribute__((always_inline)) {
+    if constexpr (KS) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(xr + (((db & 7) * 4 + g) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * f0 + o[e] * f1;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e];
+    }
+  };
+
   // ---- epilogue: normalise and write (direct) or write the partial
   const float l_tot = xhalf_sum(l_run);
   const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -822,15 +995,20 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if (DIRECT) {
     T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
 #pragma unroll
-    for (int db = 0; db < NBL; ++db)
+    for (int db = 0; db < NBL; ++db) {
+      if (!own_block(db)) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        f32x4 av;
+        acc_of(db, g, av);
         float v4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
+        for (int e = 0; e < 4; ++e) v4[e] = av[e] * inv;
         store4<T>(o + (chalf * NBL + db) * 32 + 8 * g + 4 * hh, v4);
       }
-    if (hh == 0 && chalf == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
+      if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
+    }
+    if (hh == 0 && chalf == 0 && kp == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
   } else {
     // Partials stay in accumulator order: the wave's 32 rows form one block
     // of 32 x R values in which every store instruction writes one contiguous
@@ -842,27 +1020,41 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     if (a.part_bf16) {
       __bf16* o = static_cast<__bf16*>(a.part_o) + base + 8 * lane;
 #pragma unroll
-      for (int db = 0; db < NBL; ++db)
+      for (int db = 0; db < NBL; ++db) {
+        if (!own_block(db)) continue;
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
+          f32x4 a0, a1;
+          acc_of(db, 2 * gp, a0);
+          acc_of(db, 2 * gp + 1, a1);
           bf16x8 v8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] = (__bf16)(acc[db][8 * gp + e] * inv);
+          for (int e = 0; e < 4; ++e) {
+            v8[e] = (__bf16)(a0[e] * inv);
+            v8[4 + e] = (__bf16)(a1[e] * inv);
+          }
           __builtin_nontemporal_store(v8, reinterpret_cast<bf16x8*>(o + 512 * (2 * (chalf * NBL + db) + gp)));
         }
+        if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
       float* o = static_cast<float*>(a.part_o) + base + 4 * lane;
 #pragma unroll
-      for (int db = 0; db < NBL; ++db)
+      for (int db = 0; db < NBL; ++db) {
+        if (!own_block(db)) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          f32x4 av;
+          acc_of(db, g, av);
           float v4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * inv;
+          for (int e = 0; e < 4; ++e) v4[e] = av[e] * inv;
           store4_f32_nt(o + 256 * (4 * (chalf * NBL + db) + g), v4);
         }
+        if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (hh == 0 && chalf == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
+    if (hh == 0 && chalf == 0 && kp == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
   }
 }
 
@@ -1011,8 +1203,9 @@ static bool shape_supported(int dtype, int R, int P) {
   return false;
 }
 
-// Layout 3 (depth-split score pairs) is built for the bf16 rank-512 shape.
-static bool depth_split_supported(int dtype, int R, int P) { return dtype == KDT_BF16 && R == 512 && P == 64; }
+// Layouts 3 (depth-split score pairs) and 4 (two key streams) are built for
+// the bf16 rank-512 shape.
+static bool wide_layout_supported(int dtype, int R, int P) { return dtype == KDT_BF16 && R == 512 && P == 64; }
 
 static int validate(const kdt_verify_desc* d) {
   if (!d) return KDT_ERR_INVALID_ARG;
@@ -1023,7 +1216,7 @@ static int validate(const kdt_verify_desc* d) {
   if (d->max_prefix_len < 0 || d->capacity < (int64_t)d->max_prefix_len + d->q_len)
     return KDT_ERR_INVALID_ARG;
   if (d->split_keys < 0 || (d->split_keys % kBN) != 0) return KDT_ERR_INVALID_ARG;
-  if (d->layout < 0 || d->layout > 3) return KDT_ERR_INVALID_ARG;
+  if (d->layout < 0 || d->layout > 4) return KDT_ERR_INVALID_ARG;
   if (d->partials_f32 != 0 && d->partials_f32 != 1) return KDT_ERR_INVALID_ARG;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
   if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
@@ -1038,7 +1231,7 @@ static int validate(const kdt_verify_desc* d) {
   for (int64_t s : strides)
     if (s < 0 || s % vec) return KDT_ERR_UNSUPPORTED;
   if ((int64_t)d->B * d->q_len * d->H > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
-  if (d->layout == 3 && !depth_split_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
+  if (d->layout >= 3 && !wide_layout_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
   return KDT_OK;
 }
 
@@ -1055,15 +1248,18 @@ static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 // wave; up to sixty-four when a workgroup's four waves share the splits of
 // one item).  The constants are fitted to a measured grid of split sizes and
 // layouts over six workloads at R = 512, P = 64 (a 128-row tile of 32 keys
-// about 1.7 us, a start-up about 4 us, a 128-row float32 partial about 0.2 us)
+// about 1.7 us, a start-up about 4 us, a 128-row float32 partial about 0.15 us)
 // and scale with the contraction work of one wave and with the bytes a
 // partial holds.
 static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R, int P, int layout,
                           int part_bytes) {
   const int rows = layout_rows(layout);
-  const double t_tile = 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
-  const double t_start = 4.0;
-  const double t_part = 0.2 * rows / kBM * R / 512.0 * part_bytes / 4.0;
+  // layout 4: two key tiles per step, each wave doing layout 1's work for its
+  // tile in about 1.18 times layout 1's tile time, plus about 2 us to combine
+  // the two streams at the end
+  const double t_tile = layout == 4 ? 1.7 * 1.18 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+  const double t_start = layout == 4 ? 6.0 : 4.0;
+  const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 3.0, t_merge_batch = 2.0;
   const int64_t ns = (n_max + sk - 1) / sk;
   const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
@@ -1083,8 +1279,9 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   int best_layout = d->layout ? d->layout : 1;
   int64_t sk = d->split_keys;
   double best = 1e300;
-  for (int layout = 1; layout <= 3; ++layout) {
-    if (d->layout ? layout != d->layout : layout == 3) continue;
+  const bool wide_ok = wide_layout_supported(d->dtype, d->R, d->P);
+  for (int layout = 1; layout <= 4; ++layout) {
+    if (d->layout ? layout != d->layout : (layout == 3 || (layout == 4 && !wide_ok))) continue;
     const int64_t n_seq_tiles = (int64_t)d->B * ((M + layout_rows(layout) - 1) / layout_rows(layout));
     const int64_t n_tiles = (n_max + kBN - 1) / kBN;
     for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
@@ -1157,6 +1354,13 @@ static int launch_split(const VerifyArgs& a, bool direct, hipStream_t s) {
         hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 3>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
       else
         hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 3>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+      return launch_status();
+    }
+    if (a.layout == 4) {
+      if (direct)
+        hipLaunchKernelGGL((verify_split_kernel<T, R, P, true, 4>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 4>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
       return launch_status();
     }
   }
