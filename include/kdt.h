@@ -139,10 +139,13 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  * the output columns (half the value work per wave, the score work done by
  * both); 3 = as 2, but the two waves of a pair each contract half of the score
  * depth (R + P) and add each other's partial scores through LDS (no score work
- * repeated, one more workgroup barrier per key tile; bf16 with R = 512 and
- * P = 64 only, KDT_ERR_UNSUPPORTED otherwise).  0 lets the library choose
- * between 1 and 2 (and the split size) by modelling the launch; results agree
- * between layouts to rounding.
+ * repeated, one more workgroup barrier per key tile); 4 = a workgroup owns 64
+ * rows as two row blocks x two key streams: each wave owns all R output
+ * columns of its 32 rows and takes every other key tile, and the two streams
+ * of a row block are combined after the last tile.  Layouts 3 and 4: bf16
+ * with R = 512 and P = 64 only, KDT_ERR_UNSUPPORTED otherwise.  0 lets the
+ * library choose among 1, 2 and 4 (and the split size) by modelling the
+ * launch; results agree between layouts to rounding.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t dtype;                       /* kdt_dtype */
@@ -160,7 +163,7 @@ typedef struct {
   float* lse;                          /* device float32 [B, q_len, H] */
   int32_t* seq_status;                 /* device int32 [B], nullable */
   int32_t split_keys;                  /* 0 = auto, else a multiple of 32 */
-  int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split */
+  int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split, 4 = 64-row key streams */
   int32_t partials_f32;                /* 1 = keep split partial outputs in float32; 0 = in the input dtype */
   const int32_t* parents;              /* device int32 [B, q_len]; used when vis is NULL */
 } kdt_verify_desc;
@@ -185,7 +188,7 @@ typedef struct {
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
   int32_t rows;                /* q_len * H */
   int32_t direct;              /* 1: max_splits == 1, no partials, no merge */
-  int32_t layout;              /* workgroup layout used: 1, 2 or 3 */
+  int32_t layout;              /* workgroup layout used: 1 to 4 */
   int32_t part_dtype;          /* kdt_dtype of part_o */
   int64_t part_o_offset;       /* bytes into the workspace */
   int64_t part_lse_offset;

@@ -26,7 +26,12 @@
 //      and splits the output columns (half the value work per wave, no
 //      parking, a deeper tile ring);
 //   3: as 2, but the pair splits the score contraction by depth and adds the
-//      partner's partial scores through LDS.
+//      partner's partial scores through LDS;
+//   4: 64 rows as two row blocks x two key streams: each wave owns all R
+//      columns of its 32 rows and takes every other key tile (no contraction
+//      step repeated, each tile read by two waves); the query's rope part is
+//      read from LDS every tile instead of parking an accumulator block, and
+//      the two streams are combined through LDS after the last tile.
 // * Keys stream through LDS in tiles of 32 rows x (R + P); all four waves read
 //   the same tile, so each K/V byte crosses L2 -> LDS once per workgroup.
 // * Computing S^T (keys along the MFMA rows) leaves every lane holding 16
@@ -39,7 +44,7 @@
 //   read-modify-write of every accumulation register every tile).  A row whose
 //   max outgrows its reference by more than that makes its wave redo the
 //   split once against the exact max, which it has tracked meanwhile.
-// * K/V tiles rotate through three (layouts 1, 3) or four (layout 2) LDS
+// * K/V tiles rotate through three (layouts 1, 3) or four (layouts 2, 4) LDS
 //   buffers and are copied straight from HBM into LDS with
 //   buffer_load_dwordx4 ... lds, so staging costs no registers and all but one
 //   buffer are in flight while one tile is computed.  The value operand is
