@@ -1270,7 +1270,9 @@ static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R,
   const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
   const int64_t batches = ns > 16 ? (ns + 63) / 64 : 1;
   const double merge = ns > 1 ? ns * n_seq_tiles * t_part + t_merge + t_merge_batch * (double)batches : 0.0;
-  return rounds * ((sk / kBN) * t_tile + t_start) + merge;
+  // (layout 4 works in steps of two tiles: an odd tile count wastes half a step)
+  const int64_t tiles = layout == 4 ? (sk / kBN + 1) / 2 * 2 : sk / kBN;
+  return rounds * (tiles * t_tile + t_start) + merge;
 }
 
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
