@@ -41,8 +41,9 @@ def test_merge_matches_oracle_with_empty_splits(out_dtype, part_dtype, S):
     assert np.max(np.abs(got_l[fin] - rl[fin])) < 1e-5
 
 
+@pytest.mark.parametrize("layout", [0, 4])
 @pytest.mark.parametrize("partials_f32", [False, True])
-def test_partials_merge_to_full_result(partials_f32):
+def test_partials_merge_to_full_result(partials_f32, layout):
     cfg = synth.Config("merge_cfg", 12, "bf16", B=2, H=16, R=512, P=64, q_len=17, prefix=("uniform", 100, 900),
                        tree="uniform")
     inp = synth.generate(cfg)
@@ -50,7 +51,7 @@ def test_partials_merge_to_full_result(partials_f32):
     vis, _ = kdt.build_visibility(g.parents)
     part_o, part_lse, plan = kdt.verify_partials(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis,
                                                  cfg.softmax_scale, max_prefix_len=g.max_prefix_len,
-                                                 split_keys=128, partials_f32=partials_f32)
+                                                 split_keys=128, partials_f32=partials_f32, layout=layout)
     torch.cuda.synchronize()
     assert part_o.dtype == (torch.float32 if partials_f32 else torch.bfloat16)
     # each split's partial equals the oracle on that chunk of keys
@@ -78,7 +79,8 @@ def test_partials_merge_to_full_result(partials_f32):
                                   split_keys=plan.split_keys)
     torch.cuda.synchronize()
     o_full, l_full = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, vis, cfg.softmax_scale,
-                                     max_prefix_len=g.max_prefix_len, split_keys=128, partials_f32=partials_f32)
+                                     max_prefix_len=g.max_prefix_len, split_keys=128, partials_f32=partials_f32,
+                                     layout=layout)
     torch.cuda.synchronize()
     assert torch.equal(out, o_full) and torch.equal(lse, l_full)
 
