@@ -352,10 +352,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int CSC = DS ? 2 : (KS ? 1 : CS); // column split of the output
   static_assert(!DS || (NCHUNK % 2 == 0 && KW == 8), "depth split: bf16, even contraction steps");
   static_assert(!KS || (KW == 8 && R % KMF == 0), "key streams: bf16");
+  constexpr int NQR = NCHUNK - R / KMF;       // rope steps of the score contraction
+  // Layouts 1 (at rank 512) and 4 read the query's rope fragments from LDS
+  // every tile instead of holding them, which frees the registers the score
+  // tile needs while all 256 accumulation registers are taken.
+  constexpr bool QPE = KS || (CS == 1 && KW == 8 && NB == 16);
   // query fragments held in registers by one wave (score steps)
-  constexpr int NQF = DS ? NCHUNK / 2 : (KS ? R / KMF : NCHUNK);
-  constexpr int NQR = NCHUNK - R / KMF;       // rope steps (read from LDS when KS)
-  constexpr int NSTEP = KS ? NCHUNK : NQF;    // score steps of one wave
+  constexpr int NQF = DS ? NCHUNK / 2 : (QPE ? R / KMF : NCHUNK);
+  constexpr int NSTEP = QPE ? NCHUNK : NQF;   // score steps of one wave
   constexpr int NBL = NB / CSC;               // output column blocks of one wave
   constexpr int BM = KS ? kBM / 2 : kBM / CSC;    // query rows per workgroup
   constexpr int PV_STEPS = kBN / KMF;         // MFMA steps of the value contraction per tile
@@ -369,8 +373,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // the accumulator stash also needs LDS, four otherwise.  The copies are
   // inline asm the compiler does not track, so one array indexed with
   // constants serves.
-  constexpr bool STASH_LDS = (NBL == 16) && !KS;
-  constexpr int NBUF = (STASH_LDS || DS) ? 3 : 4;
+  constexpr bool STASH_LDS = (NBL == 16) && !QPE;
+  constexpr int NBUF = (CS == 1 || DS) ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) char s_tiles[NBUF][BUF_BYTES];
   // vmcnt per tile copy on every wave (a wave that issued more waits a
   // little longer, which is safe).
@@ -382,9 +386,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   constexpr int NVA = KS ? 1 : kThreads / kWave;
   __shared__ uint64_t s_vm[NVA][2 * KDT_MAX_Q_LEN];
   __shared__ int s_vj[NVA][KDT_MAX_Q_LEN];
-  // key streams: the rope part of each row block's query fragments, one
-  // 16-byte fragment per (row block, step, lane)
-  __shared__ __attribute__((aligned(16))) char s_qpe[KS ? 2 * NQR * 64 * 16 : 16];
+  // the rope part of each row block's query fragments, one 16-byte fragment
+  // per (row block, step, lane)
+  __shared__ __attribute__((aligned(16))) char s_qpe[QPE ? (BM / 32) * NQR * 64 * 16 : 16];
   // depth split: each wave's partial score tile, 16 floats per lane
   __shared__ __attribute__((aligned(16))) f32x4 s_sx[DS ? 4 * kThreads : 1];
   // One accumulator block per lane parks here while the score tile is alive
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       if (c < R / KMF) qf[j] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
       else qf[j] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
     }
-    if constexpr (KS) {
+    if constexpr (QPE) {
       // the rope fragments go to LDS (one wave of each row block writes them)
       if (kp == 0) {
 #pragma unroll
@@ -680,15 +684,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     };
     // (key streams hold no accumulator block in LDS, so their scores take
     // registers and the operand queues are shorter)
-    constexpr int QPF0 = KS ? 2 : KDT_SCORE_PREFETCH;
+    constexpr int QPF0 = QPE ? 2 : KDT_SCORE_PREFETCH;
     constexpr int QPF = NSTEP < QPF0 ? NSTEP : QPF0;
     frag kf[QPF];
 #pragma unroll
     for (int j = 0; j < QPF; ++j) kf[j] = *reinterpret_cast<const frag*>(score_src(c0 + j));
-    // key streams: this row block's rope fragments of the query, read from
-    // LDS QPF steps before their MFMA
+    // this row block's rope fragments of the query, read from LDS QPF steps
+    // before their MFMA
     auto qpe_src = [&](int i) { return reinterpret_cast<const frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16); };
-    frag qq[KS ? QPF : 1];
+    frag qq[QPE ? QPF : 1];
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.0f;
@@ -696,8 +700,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     for (int j = 0; j < NSTEP; ++j) {
       const frag cur = kf[j % QPF];
       if (j + QPF < NSTEP) kf[j % QPF] = *reinterpret_cast<const frag*>(score_src(c0 + j + QPF));
-      if constexpr (KS) {
-        static_assert(!KS || NQF >= QPF, "rope fragments are queued behind the register ones");
+      if constexpr (QPE) {
+        static_assert(!QPE || NQF >= QPF, "rope fragments are queued behind the register ones");
         // the slot refilled now is the one this step consumes: take it first
         const frag qcur = j < NQF ? qf[j < NQF ? j : 0] : qq[j % QPF];
         if (j + QPF >= NQF && j + QPF < NSTEP) qq[(j + QPF) % QPF] = *qpe_src(j + QPF - NQF);
