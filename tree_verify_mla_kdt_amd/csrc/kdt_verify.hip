@@ -18,20 +18,19 @@
 //   (fp32).
 // * A workgroup is 4 waves (one per SIMD) and owns a tile of rows of one
 //   sequence and one split of its key range, in one of three layouts:
-//   1: 128 rows, each wave 32 rows and all R output columns (its Q fragments
-//      in registers for the whole key loop, its 32 x R fp32 accumulators in
-//      the accumulation registers, one block parked in LDS while the score
-//      tile is alive);
+//   1: 128 rows, each wave 32 rows and all R output columns (its latent Q
+//      fragments in registers for the whole key loop, its rope fragments
+//      read from LDS every tile, its 32 x R fp32 accumulators in the
+//      accumulation registers);
 //   2: 64 rows, each pair of waves shares 32 rows, computes the same scores
-//      and splits the output columns (half the value work per wave, no
-//      parking, a deeper tile ring);
+//      and splits the output columns (half the value work per wave, a
+//      deeper tile ring);
 //   3: as 2, but the pair splits the score contraction by depth and adds the
 //      partner's partial scores through LDS;
 //   4: 64 rows as two row blocks x two key streams: each wave owns all R
-//      columns of its 32 rows and takes every other key tile (no contraction
-//      step repeated, each tile read by two waves); the query's rope part is
-//      read from LDS every tile instead of parking an accumulator block, and
-//      the two streams are combined through LDS after the last tile.
+//      columns of its 32 rows (registers as in layout 1) and takes every
+//      other key tile (no contraction step repeated, each tile read by two
+//      waves); the two streams are combined through LDS after the last tile.
 // * Keys stream through LDS in tiles of 32 rows x (R + P); all four waves read
 //   the same tile, so each K/V byte crosses L2 -> LDS once per workgroup.
 // * Computing S^T (keys along the MFMA rows) leaves every lane holding 16
@@ -324,7 +323,7 @@ __device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, c
 // columns.  CS = 2, for sequences of at most 64 rows (AR decoding and small
 // trees): two row blocks of 32, each owned by a pair of waves that compute the
 // same scores and softmax and split the R output columns between them.  Each
-// wave then holds half the accumulators (no stash) and does half the value
+// wave then holds half the accumulators and does half the value
 // MFMAs; the duplicated score MFMAs are spare capacity when the memory stream
 // is the bound.
 template <typename T, int R, int P, bool DIRECT, int CS>
@@ -346,8 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // output columns, and takes every other key tile (stream w % 2), so no
   // contraction step is done twice and each tile is read by two waves; the
   // two streams' softmax states and accumulators are combined once, after
-  // the last tile.  The query's rope part is read from LDS every tile, which
-  // frees the registers layout 1 gets by parking an accumulator block.
+  // the last tile.  As in layout 1, the query's rope part is read from LDS
+  // every tile.
   constexpr bool KS = (CS == 4);
   constexpr int CSC = DS ? 2 : (KS ? 1 : CS); // column split of the output
   static_assert(!DS || (NCHUNK % 2 == 0 && KW == 8), "depth split: bf16, even contraction steps");
@@ -370,10 +369,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   static_assert(R % 32 == 0 && D % KMF == 0 && (P * sizeof(T)) % 16 == 0, "shape");
 
   // Ring of NBUF key-tile buffers, NBUF - 1 copies in flight: three where
-  // the accumulator stash also needs LDS, four otherwise.  The copies are
-  // inline asm the compiler does not track, so one array indexed with
-  // constants serves.
-  constexpr bool STASH_LDS = (NBL == 16) && !QPE;
+  // the query's rope fragments (layout 1) or the partial scores (layout 3)
+  // also need LDS, four otherwise.  The copies are inline asm the compiler
+  // does not track, so one array indexed with constants serves.
+  static_assert(NBL < 16 || QPE, "a wave owning all 512 columns reads its rope fragments from LDS");
   constexpr int NBUF = (CS == 1 || DS) ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) char s_tiles[NBUF][BUF_BYTES];
   // vmcnt per tile copy on every wave (a wave that issued more waits a
@@ -391,10 +390,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   __shared__ __attribute__((aligned(16))) char s_qpe[QPE ? (BM / 32) * NQR * 64 * 16 : 16];
   // depth split: each wave's partial score tile, 16 floats per lane
   __shared__ __attribute__((aligned(16))) f32x4 s_sx[DS ? 4 * kThreads : 1];
-  // One accumulator block per lane parks here while the score tile is alive
-  // (all 512 registers are otherwise taken: 256 accumulators, Q, scores).
-  constexpr bool STASH = STASH_LDS;
-  __shared__ __attribute__((aligned(16))) f32x4 s_stash[STASH ? kThreads * 4 : 1];
 
   const int u = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = u % a.n_rt;
@@ -663,12 +658,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, char* st_buf)
                        __attribute__((always_inline)) {
     const int kt = k_begin + tile * kBN;
-    if constexpr (STASH) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        s_stash[g * kThreads + tid] = f32x4{acc[NBL - 1][4 * g], acc[NBL - 1][4 * g + 1], acc[NBL - 1][4 * g + 2],
-                                            acc[NBL - 1][4 * g + 3]};
-    }
     // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T.
     // The K fragments are read QPF steps ahead of the MFMA chain.
     auto score_src = [&](int c) __attribute__((always_inline)) -> const char* {
@@ -791,16 +780,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     if (!dead && __any(m_max > m_ref + kRefSlack)) {
       dead = true;
       s_dead = 1;
-    }
-    if constexpr (STASH) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = s_stash[g * kThreads + tid];
-        acc[NBL - 1][4 * g] = v[0];
-        acc[NBL - 1][4 * g + 1] = v[1];
-        acc[NBL - 1][4 * g + 2] = v[2];
-        acc[NBL - 1][4 * g + 3] = v[3];
-      }
     }
     const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
     float p[16];
