@@ -391,3 +391,17 @@ def test_bad_trees_from_parents_are_flagged_like_the_mask_kernel():
     bad = kdt.KDT_SEQ_BAD_TREE
     assert st1.cpu().tolist() == [0, bad, bad, bad] and st2.cpu().tolist() == st1.cpu().tolist()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2, 4])
+def test_many_sequences_more_workgroups_than_units(layout):
+    """257 short ragged sequences: the grid holds more workgroups than the GPU
+    has compute units, so several rounds run and every index mapping (XCD
+    order, row tiles, splits) is exercised past the first round."""
+    cfg = small_cfg(q=5, H=8, tree="uniform", prefix=("uniform", 0, 300), B=257, index=401)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    ro, rl = oracle_full(inp)
+    for sk in (0, 64):
+        o, l = run_gpu(g, split_keys=sk, layout=layout, from_parents=True)
+        check_close("bf16", o, ro, l, rl, f"B=257 layout={layout} split_keys={sk}")
