@@ -962,23 +962,25 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   }
   // the output blocks this wave writes (key streams: its column half)
   auto own_block = [&](int db) { return !KS || (db >> 3) == kp; };
-  // accumulator (db, 4 g + e) of this lane, both key streams combined
-  auto acc_of = [&](int db, int g, f32x4& v) __attribute__((always_inline)) {
+  // ---- epilogue: normalise and write (direct) or write the partial
+  const float l_tot = xhalf_sum(l_run);
+  const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_v = l_tot > 0.0f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
+  // key streams: the normalisation folded into the two streams' factors
+  f0 *= inv;
+  f1 *= inv;
+  // normalised output (db, 4 g + e) of this lane, both key streams combined
+  auto out_of = [&](int db, int g, f32x4& v) __attribute__((always_inline)) {
     if constexpr (KS) {
       const f32x4 o = *reinterpret_cast<const f32x4*>(xr + (((db & 7) * 4 + g) * 64 + lane) * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * f0 + o[e] * f1;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e];
+      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * inv;
     }
   };
-
-  // ---- epilogue: normalise and write (direct) or write the partial
-  const float l_tot = xhalf_sum(l_run);
-  const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_v = l_tot > 0.0f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
   if (!row_ok) return;
   if (DIRECT) {
     T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
@@ -988,10 +990,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 av;
-        acc_of(db, g, av);
-        float v4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = av[e] * inv;
+        out_of(db, g, av);
+        const float v4[4] = {av[0], av[1], av[2], av[3]};
         store4<T>(o + (chalf * NBL + db) * 32 + 8 * g + 4 * hh, v4);
       }
       if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
@@ -1013,13 +1013,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
           f32x4 a0, a1;
-          acc_of(db, 2 * gp, a0);
-          acc_of(db, 2 * gp + 1, a1);
+          out_of(db, 2 * gp, a0);
+          out_of(db, 2 * gp + 1, a1);
           bf16x8 v8;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v8[e] = (__bf16)(a0[e] * inv);
-            v8[4 + e] = (__bf16)(a1[e] * inv);
+            v8[e] = (__bf16)a0[e];
+            v8[4 + e] = (__bf16)a1[e];
           }
           __builtin_nontemporal_store(v8, reinterpret_cast<bf16x8*>(o + 512 * (2 * (chalf * NBL + db) + gp)));
         }
@@ -1033,10 +1033,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 av;
-          acc_of(db, g, av);
-          float v4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = av[e] * inv;
+          out_of(db, g, av);
+          const float v4[4] = {av[0], av[1], av[2], av[3]};
           store4_f32_nt(o + 256 * (4 * (chalf * NBL + db) + g), v4);
         }
         if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
