@@ -127,7 +127,9 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  *
  * Split-prefix execution.  The key range of each sequence is cut into splits of
  * `split_keys` keys (0 = the library's choice; otherwise a multiple of 32, the
- * key tile).
+ * key tile).  split_keys cache rows of either region (c_kv_ss or k_pe_ss
+ * elements apart) must span less than 2^31 bytes, or the call returns
+ * KDT_ERR_UNSUPPORTED; the library's choice stays within that.
  * Each split produces a normalised partial output and its log-sum-exp in the
  * workspace; a second kernel merges the splits by the log-sum-exp identity.
  * When every sequence fits in one split the merge is skipped and the first

@@ -284,9 +284,11 @@ template <int ROWS, int NCH>
 constexpr int region_wave_loads() { return (ROWS * NCH / 64 + kThreads / 64 - 1) / (kThreads / 64); }
 
 // The jj-th wave-load of this wave for one region (nothing if this wave has
-// fewer).  stage_region issues them all.
+// fewer).  stage_region issues them all.  The region's first row sits at byte
+// base_off of buffer rs, rows ss bytes apart; lds is its LDS byte address.
 template <int ROWS, int NCH>
-__device__ __forceinline__ void stage_one(i32x4 rs, uint32_t ss, int nrows, char* lds, int wave, int lane, int jj) {
+__device__ __forceinline__ void stage_one(i32x4 rs, uint32_t base_off, uint32_t ss, int nrows, uint32_t lds, int wave,
+                                          int lane, int jj) {
   constexpr int SLOTS = ROWS * NCH;
   static_assert(SLOTS % 64 == 0, "tile region must be whole wave loads");
   constexpr int WAVES = kThreads / 64;
@@ -299,24 +301,25 @@ __device__ __forceinline__ void stage_one(i32x4 rs, uint32_t ss, int nrows, char
       const int row = j;
       const int src_row = row < nrows ? row : nrows - 1;
       voff = (uint32_t)(lane ^ swz_of<NCH>(row)) * 16;
-      soff = (uint32_t)src_row * ss;
+      soff = base_off + (uint32_t)src_row * ss;
     } else {
       const int slot = j * 64 + lane;
       const int row = slot / NCH, pc = slot - row * NCH;
       const int c = pc ^ swz_of<NCH>(row);
       const int src_row = row < nrows ? row : nrows - 1;
       voff = (uint32_t)src_row * ss + (uint32_t)c * 16;
-      soff = 0;
+      soff = base_off;
     }
-    dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds_addr(lds + j * 1024)), voff,
-                 __builtin_amdgcn_readfirstlane(soff));
+    dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds + j * 1024), voff, __builtin_amdgcn_readfirstlane(soff));
   }
 }
 
 template <int ROWS, int NCH>
-__device__ __forceinline__ void stage_region(i32x4 rs, uint32_t ss, int nrows, char* lds, int wave, int lane) {
+__device__ __forceinline__ void stage_region(i32x4 rs, uint32_t base_off, uint32_t ss, int nrows, uint32_t lds,
+                                             int wave, int lane) {
 #pragma unroll
-  for (int jj = 0; jj < region_wave_loads<ROWS, NCH>(); ++jj) stage_one<ROWS, NCH>(rs, ss, nrows, lds, wave, lane, jj);
+  for (int jj = 0; jj < region_wave_loads<ROWS, NCH>(); ++jj)
+    stage_one<ROWS, NCH>(rs, base_off, ss, nrows, lds, wave, lane, jj);
 }
 
 // CS (column split) = 1: the four waves own 32 rows each, all R output
@@ -416,14 +419,20 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
   const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
   const uint32_t pe_ss = (uint32_t)(a.k_pe_ss * (int64_t)sizeof(T));
-  // Copy of key tile `tile` (first key k_begin + tile * kBN) with its first
-  // `nrows` rows real; later rows repeat row nrows - 1.
-  auto stage_rows = [&](int tile, char* buf, int nrows) {
-    const int kt = k_begin + tile * kBN;
-    stage_region<kBN, RC>(make_rsrc(kv_lat + (int64_t)kt * lat_ss, (uint32_t)nrows * lat_ss), lat_ss,
-                          nrows, buf, wave, lane);
-    stage_region<kBN, PC>(make_rsrc(kv_pe + (int64_t)kt * pe_ss, (uint32_t)nrows * pe_ss), pe_ss,
-                          nrows, buf + LAT_BYTES, wave, lane);
+  // One buffer descriptor per region for the whole split, so that a tile
+  // copy only adds its row offset.  It spans the split's rows below the cache
+  // capacity (the host keeps split_keys rows of either region under 2^31
+  // bytes); every row a copy reads is one of them.
+  const int64_t span = max((int64_t)0, min((int64_t)a.split_keys, a.capacity - (int64_t)k_begin));
+  const i32x4 rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span * lat_ss));
+  const i32x4 rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span * pe_ss));
+  // Copy of key tile `tile` (first key k_begin + tile * kBN) into the tile
+  // buffer at LDS address lds, with its first `nrows` rows real; later rows
+  // repeat row nrows - 1.
+  auto stage_rows = [&](int tile, uint32_t lds, int nrows) {
+    const uint32_t r0 = (uint32_t)(tile * kBN);
+    stage_region<kBN, RC>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane);
+    stage_region<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane);
   };
   // Speculative copies of the first two tiles as if the split were full:
   // rows below the cache capacity are always inside the caller's buffer, so
@@ -439,8 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     par_v[1] = lane + 64 < a.q ? pp[lane + 64] : -1;
   }
   if (spec) {
-    stage_rows(0, s_tiles[0], kBN);
-    stage_rows(1, s_tiles[1], kBN);
+    stage_rows(0, lds_addr(s_tiles[0]), kBN);
+    stage_rows(1, lds_addr(s_tiles[1]), kBN);
   }
 
   // The query fragments and visibility words do not depend on the prefix
@@ -469,9 +478,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
                        (b * a.q_lat_sb + (int64_t)base_row * a.q_lat_sh) * (int64_t)sizeof(T);
       const char* qp = reinterpret_cast<const char*>(a.q_pe) +
                        (b * a.q_pe_sb + (int64_t)base_row * a.q_pe_sh) * (int64_t)sizeof(T);
-      stage_region<kBN, RC>(make_rsrc(ql, (uint32_t)nrows * ql_ss), ql_ss, nrows, s_tiles[2 + blk], wave, lane);
-      stage_region<kBN, PC>(make_rsrc(qp, (uint32_t)nrows * qp_ss), qp_ss, nrows, s_tiles[2 + blk] + LAT_BYTES,
+      stage_region<kBN, RC>(make_rsrc(ql, (uint32_t)nrows * ql_ss), 0, ql_ss, nrows, lds_addr(s_tiles[2 + blk]),
                             wave, lane);
+      stage_region<kBN, PC>(make_rsrc(qp, (uint32_t)nrows * qp_ss), 0, qp_ss, nrows,
+                            lds_addr(s_tiles[2 + blk]) + LAT_BYTES, wave, lane);
     }
   } else {
     const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
@@ -523,20 +533,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
   const bool spec_ok = spec && k_begin + 2 * kBN <= k_end;
 
-  auto stage = [&](int tile, char* buf) { stage_rows(tile, buf, min(kBN, k_end - (k_begin + tile * kBN))); };
+  auto stage = [&](int tile, uint32_t lds) { stage_rows(tile, lds, min(kBN, k_end - (k_begin + tile * kBN))); };
   // The same copy, one wave-load at a time (pieces 0 .. NPIECE - 1), so that
   // the copies can be issued between value MFMAs: a wave waiting for the
   // texture unit to accept a copy then still has MFMAs in flight.
   constexpr int LAT_PIECES = region_wave_loads<kBN, RC>();
   constexpr int NPIECE = LAT_PIECES + region_wave_loads<kBN, PC>();
-  auto stage_piece = [&](int tile, int nrows, char* buf, int piece) __attribute__((always_inline)) {
-    const int kt = k_begin + tile * kBN;
+  auto stage_piece = [&](int tile, int nrows, uint32_t lds, int piece) __attribute__((always_inline)) {
+    const uint32_t r0 = (uint32_t)(tile * kBN);
     if (piece < LAT_PIECES)
-      stage_one<kBN, RC>(make_rsrc(kv_lat + (int64_t)kt * lat_ss, (uint32_t)nrows * lat_ss), lat_ss, nrows, buf,
-                         wave, lane, piece);
+      stage_one<kBN, RC>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane, piece);
     else
-      stage_one<kBN, PC>(make_rsrc(kv_pe + (int64_t)kt * pe_ss, (uint32_t)nrows * pe_ss), pe_ss, nrows,
-                         buf + LAT_BYTES, wave, lane, piece - LAT_PIECES);
+      stage_one<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane, piece - LAT_PIECES);
   };
 
 
@@ -653,9 +661,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // Key streams: the next pair of tiles (copied between this step's score
   // MFMAs; rows 0 = no such tile).
   int ks_t0 = 0, ks_t1 = 0, ks_r0 = 0, ks_r1 = 0;
-  char* ks_b0 = nullptr;
-  char* ks_b1 = nullptr;
-  auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, char* st_buf)
+  uint32_t ks_b0 = 0, ks_b1 = 0;          // (LDS addresses)
+  auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, uint32_t st_buf)
                        __attribute__((always_inline)) {
     const int kt = k_begin + tile * kBN;
     // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T.
@@ -852,8 +859,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         wait_vmem_lds<0>();
       } else {
         wait_vmem_lds<0>();
-        stage(0, s_tiles[0]);
-        if (n_tiles > 1) stage(1, s_tiles[1]);
+        stage(0, lds_addr(s_tiles[0]));
+        if (n_tiles > 1) stage(1, lds_addr(s_tiles[1]));
       }
       const int n_steps = (n_tiles + 1) / 2;
       auto tile_rows = [&](int tt) { return tt < n_tiles ? min(kBN, k_end - (k_begin + tt * kBN)) : 0; };
@@ -869,11 +876,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           ks_t1 = 2 * st + 3;
           ks_r0 = tile_rows(ks_t0);
           ks_r1 = tile_rows(ks_t1);
-          ks_b0 = s_tiles[2 - 2 * hs];
-          ks_b1 = s_tiles[3 - 2 * hs];
+          ks_b0 = lds_addr(s_tiles[2 - 2 * hs]);
+          ks_b1 = lds_addr(s_tiles[3 - 2 * hs]);
           const int tt = 2 * st + kp;
           if (compute && tt < n_tiles) {
-            tile_body(tt, s_tiles[2 * hs + kp], 0, 0, nullptr);
+            tile_body(tt, s_tiles[2 * hs + kp], 0, 0, 0u);
           } else {
             if (ks_r0 > 0) stage_rows(ks_t0, ks_b0, ks_r0);
             if (ks_r1 > 0) stage_rows(ks_t1, ks_b1, ks_r1);
@@ -890,14 +897,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       wait_vmem_lds<0>();                     // the speculative copies were right
     } else {
       wait_vmem_lds<0>();                     // speculative copies land before their buffers are reused
-      stage(0, s_tiles[0]);
-      if (n_tiles > 1) stage(1, s_tiles[1]);
-      else stage_rows(0, s_tiles[1], 1);
+      stage(0, lds_addr(s_tiles[0]));
+      if (n_tiles > 1) stage(1, lds_addr(s_tiles[1]));
+      else stage_rows(0, lds_addr(s_tiles[1]), 1);
     }
 #pragma unroll
     for (int k = 2; k < NBUF - 1; ++k) {
-      if (k < n_tiles) stage(k, s_tiles[k]);
-      else stage_rows(0, s_tiles[k], 1);
+      if (k < n_tiles) stage(k, lds_addr(s_tiles[k]));
+      else stage_rows(0, lds_addr(s_tiles[k]), 1);
     }
 #pragma unroll 1
     for (int tile = 0; tile < n_tiles; tile += NBUF) {
@@ -909,7 +916,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         const bool real = t + NBUF - 1 < n_tiles;
         const int st = real ? t + NBUF - 1 : t;
         const int st_rows = real ? min(kBN, k_end - (k_begin + st * kBN)) : 1;
-        char* sb = s_tiles[(k + NBUF - 1) % NBUF];
+        const uint32_t sb = lds_addr(s_tiles[(k + NBUF - 1) % NBUF]);
         if (compute) tile_body(t, s_tiles[k], st, st_rows, sb);
         else stage_rows(st, sb, st_rows);
       }
@@ -1262,6 +1269,11 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int M = d->q_len * d->H;
   const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
   const int part_dtype = (d->dtype == KDT_BF16 && !d->partials_f32) ? KDT_BF16 : KDT_F32;
+  // The split kernel addresses a split's cache rows by 32-bit byte offsets
+  // from its first row: split_keys rows of either region stay under 2^31 bytes.
+  const int64_t row_bytes = (d->c_kv_ss > d->k_pe_ss ? d->c_kv_ss : d->k_pe_ss) * elem_size(d->dtype);
+  const int64_t max_sk = row_bytes > 0 ? 0x7FFFFFFF / row_bytes / kBN * kBN : (int64_t)1 << 40;
+  if (max_sk < kBN || d->split_keys > max_sk) return KDT_ERR_UNSUPPORTED;
   // candidate layouts: the requested one, or both; candidate split sizes:
   // the requested one, or every distinct split count up to 4096
   int best_layout = d->layout ? d->layout : 1;
@@ -1275,6 +1287,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
     for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
       int64_t k = d->split_keys ? d->split_keys : ((n_max + s - 1) / s + kBN - 1) / kBN * kBN;
       if (!d->split_keys && (n_max + k - 1) / k != s) continue;   // covered by a smaller s
+      if (k > max_sk) continue;
       const double c = launch_cost(n_seq_tiles, n_max, k, d->R, d->P, layout, elem_size(part_dtype));
       if (c < best * 0.999) {                 // ties go to fewer splits, then layout 1
         best = c;
@@ -1286,7 +1299,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   }
   p->layout = best_layout;
   p->part_dtype = part_dtype;
-  if (sk <= 0) return KDT_ERR_INVALID_ARG;   // (no candidate: cannot happen for a validated descriptor)
+  if (sk <= 0) return KDT_ERR_UNSUPPORTED;   // no split size fits the row offsets
   const int64_t ns = (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
