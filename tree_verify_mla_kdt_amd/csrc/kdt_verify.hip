@@ -246,6 +246,19 @@ __device__ __forceinline__ void dma16_to_lds(i32x4 rs, uint32_t lds, uint32_t vo
       : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
       : "memory", "m0");
 }
+// The same with the scalar offset soff_a + soff_b: the add fills the wait
+// state the copy needs after the m0 write, in place of the s_nop.
+__device__ __forceinline__ void dma16_to_lds2(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff_a,
+                                              uint32_t soff_b) {
+  uint32_t soff;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_add_u32 %0, %3, %4\n\t"
+      "buffer_load_dwordx4 %2, %5, %0 offen lds"
+      : "=&s"(soff)
+      : "s"(lds), "v"(voff), "s"(soff_a), "s"(soff_b), "s"(rs)
+      : "memory", "m0", "scc");
+}
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (N < 64): this wave's older tile copies have
 // landed in LDS and its own LDS reads have returned.  The 6-bit vmcnt field
@@ -286,7 +299,9 @@ constexpr int region_wave_loads() { return (ROWS * NCH / 64 + kThreads / 64 - 1)
 // The jj-th wave-load of this wave for one region (nothing if this wave has
 // fewer).  stage_region issues them all.  The region's first row sits at byte
 // base_off of buffer rs, rows ss bytes apart; lds is its LDS byte address.
-template <int ROWS, int NCH>
+// FUSED: the offset add inside the copy's asm (fewer instructions where the
+// copies share the wave's issue slots with a dependent MFMA chain).
+template <int ROWS, int NCH, bool FUSED = false>
 __device__ __forceinline__ void stage_one(i32x4 rs, uint32_t base_off, uint32_t ss, int nrows, uint32_t lds, int wave,
                                           int lane, int jj) {
   constexpr int SLOTS = ROWS * NCH;
@@ -295,22 +310,29 @@ __device__ __forceinline__ void stage_one(i32x4 rs, uint32_t base_off, uint32_t 
   {
     const int j = wave + jj * WAVES;
     if ((SLOTS / 64) % WAVES != 0 && j >= SLOTS / 64) return;
-    uint32_t voff, soff;
     if constexpr (NCH == 64) {
       // one row per instruction: the row (and its swizzle) is wave-uniform
       const int row = j;
-      const int src_row = row < nrows ? row : nrows - 1;
-      voff = (uint32_t)(lane ^ swz_of<NCH>(row)) * 16;
-      soff = base_off + (uint32_t)src_row * ss;
+      const uint32_t voff = (uint32_t)(lane ^ swz_of<NCH>(row)) * 16;
+      if constexpr (FUSED) {
+        // min(row, nrows - 1) * ss as min(row * ss, (nrows - 1) * ss), the
+        // first product fixed per wave and piece
+        const uint32_t roff = min((uint32_t)row * ss, (uint32_t)(nrows - 1) * ss);
+        dma16_to_lds2(rs, __builtin_amdgcn_readfirstlane(lds + j * 1024), voff,
+                      __builtin_amdgcn_readfirstlane(base_off), __builtin_amdgcn_readfirstlane(roff));
+      } else {
+        const int src_row = row < nrows ? row : nrows - 1;
+        dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds + j * 1024), voff,
+                     __builtin_amdgcn_readfirstlane(base_off + (uint32_t)src_row * ss));
+      }
     } else {
       const int slot = j * 64 + lane;
       const int row = slot / NCH, pc = slot - row * NCH;
       const int c = pc ^ swz_of<NCH>(row);
       const int src_row = row < nrows ? row : nrows - 1;
-      voff = (uint32_t)src_row * ss + (uint32_t)c * 16;
-      soff = base_off;
+      const uint32_t voff = (uint32_t)src_row * ss + (uint32_t)c * 16;
+      dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds + j * 1024), voff, __builtin_amdgcn_readfirstlane(base_off));
     }
-    dma16_to_lds(rs, __builtin_amdgcn_readfirstlane(lds + j * 1024), voff, __builtin_amdgcn_readfirstlane(soff));
   }
 }
 
@@ -542,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   auto stage_piece = [&](int tile, int nrows, uint32_t lds, int piece) __attribute__((always_inline)) {
     const uint32_t r0 = (uint32_t)(tile * kBN);
     if (piece < LAT_PIECES)
-      stage_one<kBN, RC>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane, piece);
+      stage_one<kBN, RC, KS>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane, piece);
     else
       stage_one<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane, piece - LAT_PIECES);
   };
@@ -711,11 +733,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         constexpr int NP2 = 2 * NPIECE;
 #pragma unroll
         for (int pc = j * NP2 / NSTEP; pc < (j + 1) * NP2 / NSTEP; ++pc) {
-          if (pc < NPIECE) {
-            if (ks_r0 > 0) stage_piece(ks_t0, ks_r0, ks_b0, pc);
-          } else {
-            if (ks_r1 > 0) stage_piece(ks_t1, ks_r1, ks_b1, pc - NPIECE);
-          }
+          if (pc < NPIECE) stage_piece(ks_t0, ks_r0, ks_b0, pc);
+          else stage_piece(ks_t1, ks_r1, ks_b1, pc - NPIECE);
         }
       }
     }
@@ -872,18 +891,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           if (st >= n_steps) break;
           wait_vmem_lds<0>();
           tile_barrier();
-          ks_t0 = 2 * st + 2;
-          ks_t1 = 2 * st + 3;
-          ks_r0 = tile_rows(ks_t0);
-          ks_r1 = tile_rows(ks_t1);
+          // the next pair; past the last tile a dummy copy (row 0 of tile 0,
+          // always inside the split) goes to a buffer no later step reads,
+          // so the copies between the score MFMAs need no branch
+          const int r0 = tile_rows(2 * st + 2), r1 = tile_rows(2 * st + 3);
+          ks_t0 = r0 > 0 ? 2 * st + 2 : 0;
+          ks_t1 = r1 > 0 ? 2 * st + 3 : 0;
+          ks_r0 = r0 > 0 ? r0 : 1;
+          ks_r1 = r1 > 0 ? r1 : 1;
           ks_b0 = lds_addr(s_tiles[2 - 2 * hs]);
           ks_b1 = lds_addr(s_tiles[3 - 2 * hs]);
           const int tt = 2 * st + kp;
           if (compute && tt < n_tiles) {
             tile_body(tt, s_tiles[2 * hs + kp], 0, 0, 0u);
           } else {
-            if (ks_r0 > 0) stage_rows(ks_t0, ks_b0, ks_r0);
-            if (ks_r1 > 0) stage_rows(ks_t1, ks_b1, ks_r1);
+            stage_rows(ks_t0, ks_b0, ks_r0);
+            stage_rows(ks_t1, ks_b1, ks_r1);
           }
         }
       }
