@@ -99,6 +99,27 @@ def test_plan_rejects_bad_descriptors(field, value, code):
     assert rc == code
 
 
+def test_split_rows_fit_32bit_offsets():
+    """The split kernel addresses a split's cache rows by 32-bit byte offsets
+    from its first row, so split_keys rows of either region must span less
+    than 2^31 bytes: a larger forced split is unsupported, and the automatic
+    plan stays below the limit."""
+    row_bytes = 576 * 2                                   # bf16 rows of R + P = 576
+    limit = (2 ** 31 - 1) // row_bytes // 32 * 32
+    rc, p = _plan(_desc(split_keys=limit))
+    assert rc == 0 and p.split_keys == limit
+    assert _plan(_desc(split_keys=limit + 32))[0] == 2
+    # a 4M-key prefix: the library's choice splits it below the limit
+    rc, p = _plan(_desc(max_prefix_len=4_000_000, capacity=4_000_065))
+    assert rc == 0 and 0 < p.split_keys <= limit and p.max_splits >= 3
+    # a 32 MB row stride leaves one 32-key tile per split; 64 MB none (32 rows
+    # of it are exactly 2^31 bytes)
+    big = 1 << 24                                         # elements per row
+    rc, p = _plan(_desc(c_kv_ss=big, k_pe_ss=big, c_kv_sb=big * 4224, k_pe_sb=big * 4224))
+    assert rc == 0 and p.split_keys == 32
+    assert _plan(_desc(c_kv_ss=2 * big, k_pe_ss=64, c_kv_sb=2 * big * 4224))[0] == 2
+
+
 def test_masks_or_parents_required():
     assert _plan(_desc(vis=0))[0] == 1                 # neither masks nor parents
     rc, _ = _plan(_desc(vis=0, parents=FAKE))          # masks derived from parents
