@@ -405,3 +405,21 @@ def test_many_sequences_more_workgroups_than_units(layout):
     for sk in (0, 64):
         o, l = run_gpu(g, split_keys=sk, layout=layout, from_parents=True)
         check_close("bf16", o, ro, l, rl, f"B=257 layout={layout} split_keys={sk}")
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3, 4])
+def test_tight_cache_capacity(layout):
+    """The cache holds exactly max_b(L_b + q_len) rows, not a multiple of the
+    32-key tile: the last split of the longest sequence ends at the cache's
+    last row, so its copy descriptor spans only rows inside the cache and the
+    start-up copies that assume two full tiles are not used there."""
+    cfg = small_cfg(q=17, H=16, tree="uniform", B=3, index=431)
+    inp = synth.generate(cfg, prefix_override=[699, 301, 13], cap_round=1)
+    assert inp.S_cap == 699 + 17 and inp.S_cap % 32 != 0
+    g = GpuInputs(inp)
+    ro, rl = oracle_full(inp)
+    for sk in (0, 32, 96):
+        for fp in (False, True):
+            o, l = run_gpu(g, split_keys=sk, layout=layout, from_parents=fp)
+            check_close("bf16", o, ro, l, rl, f"tight capacity layout={layout} split_keys={sk} parents={fp}")
+
