@@ -1271,9 +1271,9 @@ static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R,
                           int part_bytes) {
   const int rows = layout_rows(layout);
   // layout 4: two key tiles per step, each wave doing layout 1's work for its
-  // tile in about 1.18 times layout 1's tile time, plus about 2 us to combine
+  // tile in about 1.1 times layout 1's tile time, plus about 2 us to combine
   // the two streams at the end
-  const double t_tile = layout == 4 ? 1.7 * 1.18 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+  const double t_tile = layout == 4 ? 1.7 * 1.1 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
   const double t_start = layout == 4 ? 6.0 : 4.0;
   const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 3.0, t_merge_batch = 2.0;
