@@ -423,3 +423,30 @@ def test_tight_cache_capacity(layout):
             o, l = run_gpu(g, split_keys=sk, layout=layout, from_parents=fp)
             check_close("bf16", o, ro, l, rl, f"tight capacity layout={layout} split_keys={sk} parents={fp}")
 
+
+@pytest.mark.parametrize("layout", [0, 1, 2, 4])
+def test_large_row_stride_offsets(layout):
+    """Cache rows 2 MB apart (2^20 bf16 elements, only the first R + P of each
+    holding data): the largest split allowed, 992 keys, then spans close to
+    2^31 bytes, the limit of the kernel's 32-bit row offsets, so the largest
+    offsets its copies compute are exercised.  The automatic split size and
+    that largest one must both match the oracle."""
+    cfg = small_cfg(q=17, H=16, tree="uniform", B=1, prefix=("fixed", 2000), index=451)
+    inp = synth.generate(cfg)
+    g = GpuInputs(inp)
+    stride = 1 << 20
+    big = torch.empty((1, g.cache.shape[1], stride), dtype=g.cache.dtype, device=g.cache.device)   # 4.3 GB
+    big[..., :cfg.R + cfg.P] = g.cache
+    g.c_kv = big[..., :cfg.R]
+    g.k_pe = big[..., cfg.R:cfg.R + cfg.P]
+    limit = (2 ** 31 - 1) // (stride * 2) // 32 * 32
+    assert limit == 992
+    ro, rl = oracle_full(inp)
+    try:
+        for sk in (0, limit):
+            o, l = run_gpu(g, split_keys=sk, layout=layout)
+            check_close("bf16", o, ro, l, rl, f"2 MB row stride layout={layout} split_keys={sk}")
+    finally:
+        del g, big
+        torch.cuda.empty_cache()
+
