@@ -294,11 +294,14 @@ int kdt_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t
  * log-probabilities, best first; every node at depth d - 1 has those K tokens
  * as candidate children.  The root (node 0) is the verified token with logw
  * 0; a child of rank j has logw = logw(parent) + logprob[d][j] (double).
- * Nodes are created in order of decreasing logw (equal logw: the candidate
- * offered first, candidates being offered lazily: a created node offers its
- * parent's next-ranked child, then its own best child) until q_len nodes exist
- * or no candidate remains.  Budget slots left over are padding: parent 0,
- * token -1, depth 1, logw -inf, no links.
+ * Nodes are created as by a plain heap onto which every created node pushes
+ * all K of its children: in order of decreasing logw until q_len nodes exist
+ * or no candidate remains, equal logw going to the child of the earlier
+ * created parent, then to the lower rank (the push order).  The device holds
+ * only each parent's best remaining child, which gives the same tree because
+ * the log-probabilities are sorted best first (the result is unspecified for
+ * unsorted lists).  Budget slots left over are padding: parent 0, token -1,
+ * depth 1, logw -inf, no links.
  *   topk_tokens    int32 [B, D, K]   (read only)
  *   topk_logprobs  float [B, D, K]   sorted best first per position (read only)
  *   root_tokens    int32 [B]         the verified token of each request

@@ -78,13 +78,13 @@ Readings where the pages are silent (each also listed in the design notes):
     position, shared by every node at depth d - 1: a block drafter predicts
     positions, not paths).  The root (node 0, the verified token) has logw 0;
     the child of rank j of a node at depth d - 1 has logw = logw(node) +
-    logprob[d][j].  Nodes are created in order of decreasing logw until the
-    budget of q nodes is reached or no candidate is left; a node's children
-    are offered lazily (a popped candidate offers its next sibling, then its
-    own first child), which creates the same nodes in the same order as
-    offering all K children at once.  Equal logw: the earlier offered
-    candidate wins.  Budget slots left over are padding: a child of the root
-    with token -1 (no prediction matches it), depth 1, logw -inf.
+    logprob[d][j].  This is a plain heap: when a node is created (the root
+    first) all K of its children go on the heap, best rank first, and nodes
+    are created by popping the heap until the budget of q nodes is reached or
+    the heap is empty.  Equal logw: the candidate pushed earlier wins, i.e.
+    the child of the earlier created parent, then the lower rank.  Budget
+    slots left over are padding: a child of the root with token -1 (no
+    prediction matches it), depth 1, logw -inf.
   * Rotary embedding (NeoX form): for i < P/2 the pair (x[i], x[i + P/2]) is
     rotated by pos * theta^(-2i/P); theta is a parameter (the pages name
     YaRN for the real model as a later swap, so plain NeoX is built here).
@@ -383,16 +383,20 @@ def build_tree(topk_tokens, topk_logprobs, root_tokens, q):
         logw = [0.0]
         tokens = [int(root_tokens[b])]
         last_child = {}
-        heap = []            # (-logw, order offered, depth, rank, parent node)
+        heap = []            # (-logw, push order, depth, rank, parent node)
         order = 0
 
-        def offer(w, d, j, par):
+        def push_children(node):
+            """A created node puts all K of its children on the heap, best rank first."""
             nonlocal order
-            heapq.heappush(heap, (-w, order, d, j, par))
-            order += 1
+            d = depth[node] + 1
+            if d > D:
+                return
+            for j in range(K):
+                heapq.heappush(heap, (-(logw[node] + float(lp[b, d - 1, j])), order, d, j, node))
+                order += 1
 
-        if D >= 1 and K >= 1:
-            offer(0.0 + float(lp[b, 0, 0]), 1, 0, 0)
+        push_children(0)
         while len(parents) < q and heap:
             negw, _, d, j, par = heapq.heappop(heap)
             node = len(parents)
@@ -405,10 +409,7 @@ def build_tree(topk_tokens, topk_logprobs, root_tokens, q):
             else:
                 out["first_child"][b, par] = node
             last_child[par] = node
-            if j + 1 < K:                                  # next sibling of this candidate
-                offer(logw[par] + float(lp[b, d - 1, j + 1]), d, j + 1, par)
-            if d < D:                                      # first child of the new node
-                offer(logw[node] + float(lp[b, d, 0]), d + 1, 0, node)
+            push_children(node)
         n = len(parents)
         out["n_nodes"][b] = n
         out["parents"][b, :n] = parents

@@ -66,6 +66,23 @@ def oracle_full(inp: synth.Inputs, vis=None):
                               inp.prefix_lens, vis, inp.cfg.softmax_scale)
 
 
+def oracle_by_seq(inp: synth.Inputs, vis=None):
+    """The full oracle output, computed one sequence at a time (the float64
+    copy of one sequence's cache at a time keeps host memory small)."""
+    if vis is None:
+        vis, _ = oracle.build_visibility(inp.parents)
+    cfg = inp.cfg
+    R = cfg.R
+    q_lat, q_pe = inp.f64("q_lat"), inp.f64("q_pe")
+    o = np.zeros(q_lat.shape, np.float64)
+    lse = np.zeros(q_lat.shape[:3], np.float64)
+    for b in range(cfg.B):
+        cb = synth.to_f64(inp.cache[b], cfg.dtype)
+        o[b:b + 1], lse[b:b + 1] = oracle.verify_attn(q_lat[b:b + 1], q_pe[b:b + 1], cb[None, :, :R], cb[None, :, R:],
+                                                      inp.prefix_lens[b:b + 1], vis[b:b + 1], cfg.softmax_scale)
+    return o, lse
+
+
 def oracle_rows(inp: synth.Inputs, rows, vis=None):
     if vis is None:
         vis, _ = oracle.build_visibility(inp.parents)

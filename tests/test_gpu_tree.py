@@ -56,9 +56,10 @@ def test_golden_trees_on_device():
 
 
 @pytest.mark.parametrize("D,K,q", [(6, 4, 128), (12, 3, 65), (3, 8, 100)])
-def test_exact_ties_follow_offer_order(D, K, q):
+def test_exact_ties_follow_push_order(D, K, q):
     """Log-probabilities from {-1, -2, -3} (exact in float and double): most
-    logw values tie, so the offer order decides nearly every step."""
+    logw values tie, so the plain heap's push order (parent creation index,
+    then rank) decides nearly every step."""
     rng = synth.rng_for(555 + D)
     B = 12
     lp = -np.sort(rng.integers(1, 4, size=(B, D, K)), axis=-1).astype(np.float32)

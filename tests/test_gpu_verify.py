@@ -2,8 +2,8 @@
 
 Full element-by-element comparisons at sizes the oracle finishes in seconds
 (several key tiles, ragged tails, several row tiles), every configuration at
-its full size (sampled rows where the full oracle would take too long), the
-AR (q_len = 1) case, forced split counts, and the invariants: masked keys get
+its full size (every row; the largest ones run the oracle one sequence at a
+time), the AR (q_len = 1) case, forced split counts, and the invariants: masked keys get
 exactly zero weight (bit-identical output), chain == successive AR calls,
 prefix permutation, gather-then-AR == tree row.
 """
@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from tree_verify_mla_kdt_amd import kdt, synth
-from gpu_util import (GpuInputs, check_close, oracle_full, oracle_rows, require_gpu, sample_rows, to_f64)
+from gpu_util import (GpuInputs, check_close, oracle_by_seq, oracle_full, oracle_rows, require_gpu, sample_rows,
+                      to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,15 +199,14 @@ def test_config_batched_full():
 
 
 @pytest.mark.parametrize("name", ["long_ctx", "ragged_deep"])
-def test_config_large_sampled_rows(name):
+def test_config_large_full(name):
+    """Every row of the two largest configurations against the float64 oracle
+    (run one sequence at a time: a few seconds of host time)."""
     inp = synth.generate(synth.CONFIGS[name])
     g = GpuInputs(inp)
     o, l = _both_routes(g)
-    rows = sample_rows(inp, 48)
-    ro, rl = oracle_rows(inp, rows)
-    go = np.stack([o[b, t, h] for (b, t, h) in rows])
-    gl = np.asarray([l[b, t, h] for (b, t, h) in rows])
-    check_close("bf16", go, ro, gl, rl, name)
+    ro, rl = oracle_by_seq(inp)
+    check_close("bf16", o, ro, l, rl, name)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
 
 
@@ -216,13 +216,8 @@ def test_ar_degenerate_q1(name):
     inp = synth.generate(cfg)
     g = GpuInputs(inp)
     o, l = _both_routes(g)
-    if name == "max_budget":
-        ro, rl = oracle_full(inp)
-        check_close("bf16", o, ro, l, rl, f"{name} q=1")
-    else:
-        rows = sample_rows(inp, 32)
-        ro, rl = oracle_rows(inp, rows)
-        check_close("bf16", np.stack([o[r] for r in rows]), ro, np.asarray([l[r] for r in rows]), rl, name)
+    ro, rl = oracle_by_seq(inp)
+    check_close("bf16", o, ro, l, rl, f"{name} q=1")
 
 
 # ---------------------------------------------------------------- invariants

@@ -5,9 +5,11 @@ dyadic log-probabilities so every sum is exact), by brute force (on small
 inputs the tree is exactly the q - 1 best paths of the whole candidate tree,
 since log-probabilities are <= 0 and a path never outranks its ancestors), by
 closed forms (one candidate per position gives a chain, one position a star,
-and budgets beyond the candidate tree leave padding), by the textbook variant
-that offers all K children at once (same nodes in the same order), and by the
-link invariants of the first-child / next-sibling encoding.
+and budgets beyond the candidate tree leave padding), by the lazy-offer variant
+a device builder uses (same nodes in the same order, exact ties included, when
+ties go by parent creation index and rank), and by the link invariants of the
+first-child / next-sibling encoding.  The oracle itself is the plain heap: a
+created node pushes all K children, and equal logw pops in push order.
 """
 import heapq
 import itertools
@@ -88,14 +90,17 @@ def test_closed_forms():
     assert np.array_equal(r["tokens"][:, 0], roots)
 
 
-def _all_children_variant(tok, lp, root, q):
-    """The textbook form: a created node offers all K children at once."""
+def _lazy_variant(tok, lp, root, q):
+    """The lazy form a device builder can use: a created node offers only its
+    best child, and a popped candidate offers its next-ranked sibling.  Ties
+    are broken by (creation index of the parent, rank), which is the push
+    order of the plain heap, so with log-probabilities sorted best first the
+    same nodes are created in the same order even under exact ties."""
     D, K = tok.shape
     parents, depth, logw, tokens = [-1], [0], [0.0], [int(root)]
-    heap, order = [], 0
-    for j in range(K):
-        heapq.heappush(heap, (-(0.0 + float(lp[0, j])), order, 1, j, 0))
-        order += 1
+    heap = []
+    if D >= 1:
+        heapq.heappush(heap, (-(0.0 + float(lp[0, 0])), (0, 0), 1, 0, 0))
     while len(parents) < q and heap:
         negw, _, d, j, par = heapq.heappop(heap)
         node = len(parents)
@@ -103,25 +108,68 @@ def _all_children_variant(tok, lp, root, q):
         depth.append(d)
         logw.append(-negw)
         tokens.append(int(tok[d - 1, j]))
+        if j + 1 < K:
+            heapq.heappush(heap, (-(logw[par] + float(lp[d - 1, j + 1])), (par, j + 1), d, j + 1, par))
         if d < D:
-            for jj in range(K):
-                heapq.heappush(heap, (-(logw[node] + float(lp[d, jj])), order, d + 1, jj, node))
-                order += 1
+            heapq.heappush(heap, (-(logw[node] + float(lp[d, 0])), (node, 0), d + 1, 0, node))
     return parents, depth, logw, tokens
 
 
-@pytest.mark.parametrize("D,K,q", [(8, 4, 65), (16, 2, 33), (4, 8, 128), (12, 3, 100)])
-def test_lazy_offers_equal_offering_all_children(D, K, q):
-    tok, lp, roots = synth.tree_topk_inputs(8, D, K, seed=100 + D + K)
+def _tie_inputs(B, D, K, seed):
+    """Log-probabilities from {-1, -2, -3}, sorted best first: exact in float
+    and double, so most logw values tie and the tie rule decides."""
+    rng = synth.rng_for(seed)
+    lp = -np.sort(rng.integers(1, 4, size=(B, D, K)), axis=-1).astype(np.float32)
+    tok = np.tile(np.arange(K, dtype=np.int32), (B, D, 1)) + 100 * np.arange(D, dtype=np.int32)[None, :, None]
+    return tok, lp, np.arange(B, dtype=np.int32)
+
+
+def _check_variant(tok, lp, roots, q):
     r = oracle.build_tree(tok, lp, roots, q)
     for b in range(tok.shape[0]):
-        p, d, w, t = _all_children_variant(tok[b], lp[b], roots[b], q)
+        p, d, w, t = _lazy_variant(tok[b], lp[b], roots[b], q)
         n = len(p)
         assert int(r["n_nodes"][b]) == n
         assert r["parents"][b, :n].tolist() == p
         assert r["depth"][b, :n].tolist() == d
         assert r["tokens"][b, :n].tolist() == t
         assert r["logw"][b, :n].tolist() == w
+
+
+@pytest.mark.parametrize("D,K,q", [(8, 4, 65), (16, 2, 33), (4, 8, 128), (12, 3, 100)])
+def test_lazy_offers_equal_plain_heap(D, K, q):
+    tok, lp, roots = synth.tree_topk_inputs(8, D, K, seed=100 + D + K)
+    _check_variant(tok, lp, roots, q)
+
+
+@pytest.mark.parametrize("D,K,q", [(6, 4, 128), (12, 3, 65), (3, 8, 100), (2, 2, 7), (5, 5, 40)])
+def test_lazy_offers_equal_plain_heap_exact_ties(D, K, q):
+    tok, lp, roots = _tie_inputs(12, D, K, 555 + D)
+    _check_variant(tok, lp, roots, q)
+
+
+def test_all_ties_golden_case_differs_from_offer_order():
+    """The tie rule matters: breaking ties by the order candidates are offered
+    lazily (instead of by push order) gives a different tree on the hand case."""
+    c = [c for c in json.load(open(GOLDEN))["cases"] if c["name"].startswith("all ties")][0]
+    tok, lp = np.array(c["topk_tokens"]), np.array(c["topk_logprobs"])
+    D, K = tok.shape
+    parents, logw, heap, order = [-1], [0.0], [], 0
+    heapq.heappush(heap, (-float(lp[0, 0]), 0, 1, 0, 0))
+    order = 1
+    while len(parents) < c["q"] and heap:
+        negw, _, d, j, par = heapq.heappop(heap)
+        node = len(parents)
+        parents.append(par)
+        logw.append(-negw)
+        if j + 1 < K:
+            heapq.heappush(heap, (-(logw[par] + float(lp[d - 1, j + 1])), order, d, j + 1, par))
+            order += 1
+        if d < D:
+            heapq.heappush(heap, (-(logw[node] + float(lp[d, 0])), order, d + 1, 0, node))
+            order += 1
+    assert parents != c["parents"]
+    assert oracle.build_tree(tok[None], lp[None], [c["root_token"]], c["q"])["parents"][0].tolist() == c["parents"]
 
 
 @pytest.mark.parametrize("D,K,q", [(8, 4, 65), (15, 2, 128), (3, 16, 128), (1, 1, 1), (2, 1, 17)])

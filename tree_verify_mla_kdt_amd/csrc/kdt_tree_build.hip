@@ -15,10 +15,18 @@
 // The root (the verified token) has logw 0; a child of rank j has
 // logw = logw(parent) + logprob[d][j], in double precision.  Nodes are created
 // in order of decreasing logw until the budget of q nodes is reached or no
-// candidate remains; candidates are offered lazily (a created node offers its
-// parent's next-ranked child, then its own best child), and equal logw goes to
-// the candidate offered first.  Leftover budget slots are padding: children
-// of the root with token -1, depth 1, logw -inf.
+// candidate remains: a plain heap onto which each created node pushes all K
+// of its children, equal logw going to the child of the earlier created
+// parent, then to the lower rank (the heap's push order).  Leftover budget
+// slots are padding: children of the root with token -1, depth 1, logw -inf.
+//
+// Lazy offers: with the log-probabilities sorted best first, a node's
+// children leave that heap in rank order, so only each parent's best
+// remaining child can be the next node.  The kernel therefore holds just
+// those: a created node offers its own best child, and a candidate, once
+// created, offers its next-ranked sibling.  Ties are keyed on (parent index,
+// rank), the push order of the full heap, so both create the same nodes in
+// the same order, ties included.
 //
 // gfx950 mapping: one wave64 per request.  The live candidates are kept
 // sorted best first across the lanes, one per lane, so the best candidate is
@@ -43,9 +51,9 @@ namespace kdt {
 constexpr int kTreeMaxK = 64;                   // ranks per position the build can use
 constexpr int kTreeLpMax = (KDT_MAX_Q_LEN - 1) * kTreeMaxK;   // staged log-probabilities
 
-// One candidate: logw, its parent's logw, offer order (ties: smaller wins;
-// INT_MAX marks an empty lane), depth | rank << 8 | parent << 16, and the
-// log-probabilities of its next sibling and of its first child.
+// One candidate: logw, its parent's logw, tie key parent * kTreeMaxK + rank
+// (smaller wins; INT_MAX marks an empty lane), depth | rank << 8 | parent << 16,
+// and the log-probabilities of its next sibling and of its first child.
 struct Cand {
   double w, base;
   int order, pk;
@@ -118,10 +126,8 @@ __global__ __launch_bounds__(64) void build_tree_kernel(
   // the sorted frontier: lane i holds the i-th best live candidate
   Cand c{-INFINITY, 0.0, INT_MAX, 0, 0.0f, 0.0f};
   int n = 1;                                    // nodes created (the root)
-  int next_order = 0;
   if (Du >= 1) {                                // the root's best child
     if (lane == 0) c = Cand{0.0 + (double)s_lp[0], 0.0, 0, 1, Ku > 1 ? s_lp[1] : 0.0f, Du > 1 ? s_lp[Ku] : 0.0f};
-    next_order = 1;
   }
 #pragma unroll 1
   while (n < q) {
@@ -145,12 +151,10 @@ __global__ __launch_bounds__(64) void build_tree_kernel(
     const float l_s2 = s_lp[j + 2 < Ku ? (d - 1) * Ku + j + 2 : 0];
     const float l_c1 = s_lp[has_c && Ku > 1 ? d * Ku + 1 : 0];
     const float l_c0 = s_lp[d + 1 < Du ? (d + 1) * Ku : 0];
-    const Cand sib{has_s ? base + (double)lsib : -INFINITY, base, has_s ? next_order : INT_MAX,
+    const Cand sib{has_s ? base + (double)lsib : -INFINITY, base, has_s ? par * kTreeMaxK + j + 1 : INT_MAX,
                    d | (j + 1) << 8 | par << 16, j + 2 < Ku ? l_s2 : 0.0f, lch};
-    next_order += has_s ? 1 : 0;
-    const Cand ch{has_c ? w + (double)lch : -INFINITY, w, has_c ? next_order : INT_MAX, (d + 1) | node << 16,
+    const Cand ch{has_c ? w + (double)lch : -INFINITY, w, has_c ? node * kTreeMaxK : INT_MAX, (d + 1) | node << 16,
                   Ku > 1 ? l_c1 : 0.0f, d + 1 < Du ? l_c0 : 0.0f};
-    next_order += has_c ? 1 : 0;
     const bool sib_first = better(sib.w, sib.order, ch.w, ch.order);
     const double hi_w = sib_first ? sib.w : ch.w, lo_w = sib_first ? ch.w : sib.w;
     const double hi_b = sib_first ? sib.base : ch.base, lo_b = sib_first ? ch.base : sib.base;
