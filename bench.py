@@ -56,6 +56,9 @@ def parse():
                          "them from the parents)")
     ap.add_argument("--partials-f32", action="store_true",
                     help="keep the split partials in float32 (default: the input dtype)")
+    ap.add_argument("--merge-mode", type=int, default=0,
+                    help="0: separate merge kernel (the library's default), "
+                         "1: merge inside the split kernel when the launch allows")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying HIP graphs (for counter runs)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB", "CAL_WRITE_DB"),
@@ -195,10 +198,10 @@ def main():
     c0 = copies[0]
     desc, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
                                      prefix_lens, vis_arg, cfg.softmax_scale, max_prefix, out, lse, None,
-                                     args.split_keys, args.layout, args.partials_f32, par_arg)
+                                     args.split_keys, args.layout, args.partials_f32, par_arg, args.merge_mode)
     plan = kdt.verify_plan(desc)
-    ws_bytes = max(int(plan.workspace_bytes), int(plan.part_lse_offset + B * plan.max_splits * plan.rows * 4))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_bytes = max(int(plan.workspace_bytes), int(plan.partials_bytes))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)   # (merge counters start at zero)
 
     def step(i):
         c = copies[i % n_copies]
@@ -207,7 +210,7 @@ def main():
         kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                         cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
                         split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
-                        parents=par_arg)
+                        parents=par_arg, merge_mode=args.merge_mode)
         kdt.gather_accepted(c["cache"], prefix_lens, accepted, n_acc, q, new_prefix_lens=new_pl)
 
     def split_only(i):
@@ -285,7 +288,7 @@ def main():
             kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                             cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
                             split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
-                            parents=par_arg)
+                            parents=par_arg, merge_mode=args.merge_mode)
         if args.separate_visibility:
             kdt.build_visibility(parents, vis=vis, depth=depth)
         g_ver = capture(verify_only, range(n_copies))
@@ -404,6 +407,7 @@ def main():
                    "rope_dim": P, "q_len": q, "prefix_len_max": max_prefix,
                    "split_keys": plan.split_keys, "splits": plan.max_splits, "layout": plan.layout,
                    "partials": "bf16" if plan.part_dtype == kdt.KDT_BF16 else "f32",
+                   "merge": "direct" if plan.direct else ("fused" if plan.fused_merge else "separate kernel"),
                    "step": ("build_visibility + verify (split + merge) + gather_accepted" if args.separate_visibility
                             else "verify (split kernel deriving the masks from the parents + merge) + gather_accepted"),
                    "input_copies": n_copies, "kernel_only": bool(args.kernel_only)},

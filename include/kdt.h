@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDT_ABI_VERSION 3
+#define KDT_ABI_VERSION 4
 #define KDT_MAX_Q_LEN 128           /* tree tokens per sequence (two 64-bit mask words) */
 
 typedef enum {
@@ -131,9 +131,18 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  * elements apart) must span less than 2^31 bytes, or the call returns
  * KDT_ERR_UNSUPPORTED; the library's choice stays within that.
  * Each split produces a normalised partial output and its log-sum-exp in the
- * workspace; a second kernel merges the splits by the log-sum-exp identity.
- * When every sequence fits in one split the merge is skipped and the first
- * kernel writes out/lse directly.
+ * workspace, and the splits are merged by the log-sum-exp identity.  When every
+ * sequence fits in one split there is no merge: the kernel writes out/lse
+ * directly.  Otherwise a second kernel does the merge (merge_mode 0, the
+ * default), or, with merge_mode 1 and a launch whose workgroups all fit on the
+ * device's compute units at once (one per unit), the merge runs inside the
+ * same kernel: the split workgroups of a row tile meet at a state word in the
+ * workspace, wait for one another for at most merge_wait_us microseconds, and
+ * share the merge; a workgroup that stops waiting leaves its share to the last
+ * one to arrive, so every call completes whatever the scheduling.  The result
+ * is the same bit for bit either way.  (One launch instead of two, but on
+ * MI355X the hand-offs between compute units of different XCDs cost more than
+ * the second launch saves, so it is not the default.)
  *
  * Workgroup layout (`layout`): 1 = a workgroup owns 128 rows (q_len*H rows of
  * one sequence), each of its four waves 32 rows and all R output columns;
@@ -168,10 +177,15 @@ typedef struct {
   int32_t layout;                      /* 0 = auto, 1 = 128-row, 2 = 64-row column split, 3 = 64-row depth split, 4 = 64-row key streams */
   int32_t partials_f32;                /* 1 = keep split partial outputs in float32; 0 = in the input dtype */
   const int32_t* parents;              /* device int32 [B, q_len]; used when vis is NULL */
+  int32_t merge_mode;                  /* 0 = separate merge kernel, 1 = merge inside the split kernel when the launch allows */
+  int32_t merge_wait_us;               /* longest wait of a split workgroup for the rest of its row tile
+                                          (0 = the default, 2000; < 0 = no wait, the last one out merges
+                                          whatever was left: for tests of that path) */
 } kdt_verify_desc;
 
-/* Host-only planning: no device access.  The partial buffers live in the
- * workspace at the given byte offsets:
+/* Host-only planning: no device memory is touched (the compute-unit count of
+ * the current device is queried once per device).  The partial buffers live
+ * in the workspace at the given byte offsets:
  *   part_o   part_dtype [B, max_splits, NBLK, 32*R]  normalised partial outputs, tiled
  *   part_lse float32 [B, max_splits, q_len*H]        natural-log partial LSE (-inf: empty split)
  * Row index within a sequence is m = t*H + h.  NBLK = ceil(q_len*H / 32): rows
@@ -184,7 +198,14 @@ typedef struct {
  * unspecified values.  part_dtype is KDT_F32 for float32 inputs or when
  * partials_f32 is set, else KDT_BF16 (rounded to nearest even: one more
  * rounding of the output's own precision, which halves the partial traffic).
- * Sequence b uses splits 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1. */
+ * Sequence b uses splits 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1.
+ * Merge state (when the merge is fused): one 32-bit word per row tile, uint32
+ * [B, NRT] at counter_offset, NRT = ceil(q_len*H / rows per workgroup of the
+ * layout): two counts and a generation bit.  The words must be zero before
+ * the first kdt_verify_attn call that uses the workspace (allocate it zeroed);
+ * every call leaves the counts at zero again (the generation bit alternates),
+ * so one workspace serves any sequence of calls on one stream.  Calls that
+ * share a workspace must not overlap in time. */
 typedef struct {
   int32_t split_keys;          /* keys per split (multiple of 32) */
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
@@ -194,17 +215,23 @@ typedef struct {
   int32_t part_dtype;          /* kdt_dtype of part_o */
   int64_t part_o_offset;       /* bytes into the workspace */
   int64_t part_lse_offset;
-  size_t workspace_bytes;      /* 0 when direct */
+  size_t workspace_bytes;      /* what kdt_verify_attn needs: 0 when direct, else partials and counters */
+  size_t partials_bytes;       /* what kdt_verify_partials needs (part_o and part_lse; also when direct) */
+  int32_t fused_merge;         /* 1: kdt_verify_attn merges inside the split kernel (one launch) */
+  int32_t reserved;
+  int64_t counter_offset;      /* bytes into the workspace of the merge counters */
 } kdt_verify_plan;
 
 int kdt_verify_get_plan(const kdt_verify_desc* d, kdt_verify_plan* plan);
 
-/* Full verify: split stage, then the merge (or direct output when one split
- * suffices).  `workspace` may be NULL only when the plan says workspace_bytes == 0. */
+/* Full verify: split stage and merge (or direct output when one split
+ * suffices).  `workspace` may be NULL only when the plan says workspace_bytes
+ * == 0; its merge counters must be zero before its first use (see above). */
 int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
 /* Split stage only: always writes the partial buffers (part_o, part_lse) in the
- * workspace, even when one split would do; `out`/`lse` are not touched. */
+ * workspace (at least plan.partials_bytes), even when one split would do;
+ * `out`/`lse` are not touched and nothing is merged. */
 int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -229,8 +256,9 @@ int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32_t H, int32
 
 /* ------------------------------------------------------------------------
  * kdt_gather_accepted — post-accept compaction of the accepted path's latents.
- * [Checkpoint, "The Message"]: "after accept gather accepted-path latents"
- * (cache append + post-verify compaction).
+ * [Checkpoint, "The Message"]: once the tree is accepted, the latents of the
+ * accepted path are gathered into the rows right after the prefix (the KV
+ * cache scheme's compaction after the verify).
  *
  * For every layer l < num_layers, sequence b and k < n_accepted[b]:
  *     row L_b + k  <-  (previous contents of) row L_b + accepted[b, k]

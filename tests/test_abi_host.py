@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
 
 
 def test_version_and_status_strings():
-    assert kdt.lib().kdt_abi_version() == 3
+    assert kdt.lib().kdt_abi_version() == kdt.ABI_VERSION == 4
     for code in range(5):
         assert kdt.status_str(code)
     assert kdt.status_str(99) == "unknown status"
@@ -68,16 +68,26 @@ def test_plan_sizes_and_layout():
     nblk = -(-M // 32)
     assert p.part_dtype == kdt.KDT_BF16            # bf16 inputs: bf16 partials unless asked otherwise
     assert p.part_lse_offset >= 1 * p.max_splits * nblk * 32 * 512 * 2 and p.part_lse_offset % 256 == 0
-    assert p.workspace_bytes == p.part_lse_offset + p.max_splits * M * 4
+    assert p.partials_bytes == p.part_lse_offset + p.max_splits * M * 4
+    # merge state words (one int32 per row tile) after the partials, 256-byte aligned
+    n_rt = -(-M // (128 if p.layout == 1 else 64))
+    assert p.counter_offset % 256 == 0 and p.counter_offset >= p.partials_bytes
+    assert p.workspace_bytes == p.counter_offset + n_rt * 4
+    assert p.fused_merge == 0                      # the separate merge kernel is the default
+    rc, ps = _plan(_desc(merge_mode=1, split_keys=p.split_keys, layout=p.layout))
+    assert rc == 0 and ps.partials_bytes == p.partials_bytes and ps.workspace_bytes == p.workspace_bytes
+    assert _plan(_desc(merge_mode=2))[0] == 1
     rc, p32 = _plan(_desc(partials_f32=1, split_keys=p.split_keys))
     assert rc == 0 and p32.part_dtype == kdt.KDT_F32 and p32.max_splits == p.max_splits
     assert p32.part_lse_offset >= p.max_splits * nblk * 32 * 512 * 4
     assert _plan(_desc(partials_f32=2))[0] == 1
     rc, p = _plan(_desc(split_keys=128))
     assert rc == 0 and p.split_keys == 128 and p.max_splits == 33
-    # a single split: no workspace
+    # a single split: no workspace for kdt_verify_attn, partials still sized
     rc, p = _plan(_desc(split_keys=8192))
     assert rc == 0 and p.direct == 1 and p.max_splits == 1
+    assert p.workspace_bytes == 0 and p.fused_merge == 0
+    assert p.partials_bytes == p.part_lse_offset + M * 4
 
 
 @pytest.mark.parametrize("field,value,code", [

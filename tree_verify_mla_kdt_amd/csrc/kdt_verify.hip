@@ -63,6 +63,8 @@
 //   their shared K/V stream in that XCD's L2.
 #include <math.h>
 
+#include <atomic>
+
 #include "kdt_common.hpp"
 
 namespace kdt {
@@ -138,6 +140,12 @@ struct VerifyArgs {
   int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len, layout;
   int q_rows_uniform;   // query rows m = t * H + h sit at one byte stride (q_lat and q_pe)
   int part_bf16;        // partial outputs in bf16 (else float32)
+  // Merge inside the split kernel (partial mode only): the split workgroups
+  // of a row tile meet at a bounded wait on their state word
+  // counters[b * n_rt + rt] and share the merge.
+  int fuse;
+  int32_t* counters;
+  int64_t spin_ticks;   // longest wait, in 100 MHz ticks (0: do not wait)
 };
 
 // The value of C-layout register v of a 32x32 MFMA result held by a lane in
@@ -171,12 +179,25 @@ template <>
 __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const float* v) {
   *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
 }
-// Streaming float32 store of four values, for partials the merge reads from
-// memory: written through whole lines instead of left dirty in L2 for the
-// end-of-kernel write-back.  (Not for the direct output, whose 8-byte
-// per-row pieces only form whole lines in L2.)
-__device__ __forceinline__ void store4_f32_nt(float* dst, const float* v) {
-  __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
+// Device-coherent 16-byte store and load (cache policy sc1: the access is
+// coherent at device scope, across the XCDs' separate L2 caches; the store is
+// also streaming, nt).  The split workgroups exchange partials this way inside
+// one launch: a writer's stores are complete once its vmcnt reaches zero, and
+// a reader's sc1 loads then see them, without the whole-L2 write-back and
+// invalidation of a device-scope fence.  base must be wave-uniform.
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ void store16_coherent(void* base, uint32_t off, V v) {
+  static_assert(sizeof(V) == 16, "16-byte store");
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4v, v), coherent_rsrc(base), off, 0, 18);
+}
+template <typename V>
+__device__ __forceinline__ V load16_coherent(const void* base, uint32_t off) {
+  static_assert(sizeof(V) == 16, "16-byte load");
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(coherent_rsrc(base), off, 0, 16));
 }
 
 // LDS image of one key tile.  Two regions: kBN rows of the c_kv part (RC
@@ -342,6 +363,249 @@ __device__ __forceinline__ void stage_region(i32x4 rs, uint32_t base_off, uint32
 #pragma unroll
   for (int jj = 0; jj < region_wave_loads<ROWS, NCH>(); ++jj)
     stage_one<ROWS, NCH>(rs, base_off, ss, nrows, lds, wave, lane, jj);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-split merge: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
+// Partials are in accumulator order (32-row blocks, see the split kernel's
+// epilogue), so one wave handles one (sequence, block, column group) of 8
+// float32 or 16 bf16 columns: every lane reads 16 bytes per split and the
+// wave's reads are one contiguous 1 KB run.  Splits are consumed sixteen at a
+// time with a running maximum, so sixteen loads per lane are in flight (one
+// memory round trip for up to sixteen splits).  Splits with lse_k = -inf are
+// skipped by selection, never by multiplication: their partial output may
+// never have been written.
+template <typename PT>
+struct PartLoad;
+template <>
+struct PartLoad<float> {
+  static constexpr int NV = 4;                  // values per lane per split
+  typedef f32x4 raw;
+  __device__ static __forceinline__ float get(const raw& r, int i) { return r[i]; }
+};
+template <>
+struct PartLoad<__bf16> {
+  static constexpr int NV = 8;
+  typedef bf16x8 raw;
+  __device__ static __forceinline__ float get(const raw& r, int i) { return (float)r[i]; }
+};
+
+// One merge item: the rows of 32-row block blk of sequence b (m < M) and
+// column group cg (8 float32 or 16 bf16 partial columns), over splits
+// 0 .. ns - 1.  Without WIDE one wave does the item: every lane reads 16
+// bytes per split, the wave's reads of one split one contiguous 1 KB run.
+// WIDE: the four waves of the workgroup share the item, wave w loading the
+// w-th quarter of the splits at once, and wave 0 combines the four (max, sum,
+// columns) states through s_st (4 * (NV + 2) * 64 floats of LDS); every wave
+// of the workgroup must then call it with the same item.  COH: the partials
+// were stored by other workgroups of the running launch and are read with
+// device-coherent loads.
+template <typename T, typename PT, bool WIDE, bool COH>
+__device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const float* __restrict__ part_lse,
+                                           int max_splits, int ns, int M, int H, int R, int n_blk, int b, int blk,
+                                           int cg, T* __restrict__ out, int64_t out_sb, int64_t out_st,
+                                           int64_t out_sh, float* __restrict__ lse, float* s_st, int wave,
+                                           int lane) {
+  constexpr int U = 16;
+  constexpr int NV = PartLoad<PT>::NV;
+  constexpr int CW = 2 * NV;                    // columns per item
+  typedef typename PartLoad<PT>::raw raw;
+  const int hh = lane >> 5;
+  const int m = blk * 32 + (lane & 31);
+  const bool row_ok = m < M;
+  const int per = WIDE ? (ns + 3) / 4 : ns;
+  const int kb = WIDE ? wave * per : 0;
+  const int ke = row_ok ? min(ns, kb + per) : kb;   // padding rows load nothing
+  const float* pl = part_lse + (int64_t)b * max_splits * M + (row_ok ? m : 0);
+  const int64_t split_stride = (int64_t)n_blk * 32 * R;
+  const PT* po_blk = part_o + ((int64_t)b * max_splits * n_blk + blk) * (32 * R);
+  float mx = -INFINITY, z = 0.0f;
+  float acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+  for (int k0 = kb; k0 < ke; k0 += U) {
+    float lk[U];
+    raw ok[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int k = k0 + j;
+      const uint32_t off = (uint32_t)((k * split_stride + 32 * CW * cg + NV * lane) * sizeof(PT));
+      if constexpr (COH) {
+        lk[j] = k < ke ? __hip_atomic_load(pl + (int64_t)k * M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : -INFINITY;
+        if (k < ke) ok[j] = load16_coherent<raw>(po_blk, off);
+      } else {
+        lk[j] = k < ke ? pl[(int64_t)k * M] : -INFINITY;
+        if (k < ke) ok[j] = *reinterpret_cast<const raw*>(reinterpret_cast<const char*>(po_blk) + off);
+      }
+    }
+    float cm = lk[0];
+#pragma unroll
+    for (int j = 1; j < U; ++j) cm = fmaxf(cm, lk[j]);
+    if (cm > mx) {
+      const float sc = __expf(mx - cm);   // 0 while mx is still -inf
+      z *= sc;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] *= sc;
+      mx = cm;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const bool live = lk[j] != -INFINITY;
+      const float w = live ? __expf(lk[j] - mx) : 0.0f;
+      z += w;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = live ? acc[i] + w * PartLoad<PT>::get(ok[j], i) : acc[i];
+    }
+  }
+  bool writer = row_ok;
+  if constexpr (WIDE) {
+    float* st = s_st + wave * (NV + 2) * 64 + lane;
+    st[0] = mx;
+    st[64] = z;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) st[64 * (2 + i)] = acc[i];
+    __syncthreads();
+    writer = row_ok && wave == 0;
+    if (writer) {
+      // combine the four states against their common max (a wave without a
+      // finite split has max -inf and no weight)
+      float mw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mw[w] = s_st[w * (NV + 2) * 64 + lane];
+      const float mt = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+      mx = mt;
+      z = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float* sw = s_st + w * (NV + 2) * 64 + lane;
+        const float f = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - mt);
+        z += f * sw[64];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] += f * sw[64 * (2 + i)];
+      }
+    }
+    __syncthreads();                            // s_st is free for the next item
+  }
+  if (writer) {
+    const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+    const int t = m / H, h = m - t * H;
+    T* o = out + b * out_sb + t * out_st + h * out_sh + CW * cg + 4 * hh;
+#pragma unroll
+    for (int q4 = 0; q4 < NV / 4; ++q4) {     // value i of the lane is column CW*cg + 8*(i/4) + 4*hh + i%4
+      const float v4[4] = {acc[4 * q4] * inv, acc[4 * q4 + 1] * inv, acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv};
+      store4<T>(o + 8 * q4, v4);
+    }
+    if (cg == 0 && hh == 0) lse[(int64_t)b * M + m] = z > 0.0f ? mx + logf(z) : -INFINITY;
+  }
+}
+
+// Number of splits sequence b uses: ceil((L + q) / split_keys) in [1, max_splits]
+// (max_splits when split_keys is 0).
+__device__ __forceinline__ int splits_of(int64_t n_keys, int split_keys, int max_splits) {
+  if (split_keys <= 0) return max_splits;
+  const int64_t ns = (n_keys + split_keys - 1) / split_keys;
+  return ns < 1 ? 1 : (ns > max_splits ? max_splits : (int)ns);
+}
+
+template <typename T, typename PT, int R>
+__device__ __forceinline__ void merge_share(const VerifyArgs& a, int b, int rt, int ns, int BM, int unit,
+                                            int n_units, float* s_st, int wave, int lane) {
+  constexpr int NV = PartLoad<PT>::NV;
+  constexpr int n_cg = R / (2 * NV);
+  const int blk0 = rt * (BM / 32);
+  const int nb = min(BM / 32, a.n_blk - blk0);    // blocks of this row tile holding real rows
+  const int n_items = nb * n_cg;
+  const PT* po = static_cast<const PT*>(a.part_o);
+  T* out = static_cast<T*>(a.out);
+  if (a.max_splits > 16) {
+    // a workgroup per item: unit = workgroup
+    for (int i = unit; i < n_items; i += n_units)
+      merge_item<T, PT, true, true>(po, a.part_lse, a.max_splits, ns, a.M, a.H, R, a.n_blk, b, blk0 + i / n_cg,
+                                    i % n_cg, out, a.out_sb, a.out_st, a.out_sh, a.lse, s_st, wave, lane);
+  } else {
+    // a wave per item: unit = workgroup, its waves taking consecutive items
+    for (int i = 4 * unit + wave; i < n_items; i += 4 * n_units)
+      merge_item<T, PT, false, true>(po, a.part_lse, a.max_splits, ns, a.M, a.H, R, a.n_blk, b, blk0 + i / n_cg,
+                                     i % n_cg, out, a.out_sb, a.out_st, a.out_sh, a.lse, s_st, wave, lane);
+  }
+}
+
+// The merge of one row tile's partials inside the split kernel.  The split
+// workgroups of (sequence b, row tile rt) share one 32-bit state word: bits
+// 0-15 count arrivals, bits 16-30 count workgroups that gave up waiting, and
+// bit 31 is a generation bit.  Partials and their log-sum-exps are stored
+// device-coherent (sc1); a workgroup whose waves have all seen their stores
+// complete adds one arrival:
+//  * the last to arrive (it reads ns - 1 arrivals back) knows every partial
+//    is in place; it writes the word back with zero counts and the generation
+//    flipped, which both releases the others and leaves the word ready for
+//    the next call, then merges its share of the row tile's items, or every
+//    item if some workgroup gave up before it arrived;
+//  * the others wait, for at most spin_ticks of the 100 MHz clock, for the
+//    generation to flip, then merge their share.  A workgroup that runs out
+//    of time adds one to the give-up count with a compare-and-swap that only
+//    succeeds while the generation has not flipped, and leaves: the last
+//    arriver then sees the count and merges everything.  If the swap finds
+//    the generation flipped, the workgroup merges its share after all.
+// The merge reads the partials with device-coherent loads.  Every workgroup
+// leaves after a bounded wait whatever the others do, so the grid always
+// drains.  An item is merged by the same code in the same order whoever
+// merges it (twice, identically, when the last arriver takes over), so the
+// output does not depend on who did.  The wait is short when all split
+// workgroups of a row tile are resident at once, which the host ensures by
+// fusing only when the grid fits the compute units.  Items: with more than
+// sixteen splits in the launch a workgroup per item (its waves sharing the
+// splits, as in merge_kernel), otherwise a wave per item.
+template <typename T, int R>
+__device__ __forceinline__ void fused_merge(const VerifyArgs& a, int b, int rt, int split, int ns, int BM,
+                                            float* s_st, int tid) {
+  __shared__ int s_mode;
+  const int wave = tid >> 6, lane = tid & 63;
+  uint32_t* word = reinterpret_cast<uint32_t*>(a.counters) + ((int64_t)b * a.n_rt + rt);
+  wait_vmem_lds<0>();                                   // this wave's partial stores are complete
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    // mode: 0 = leave, 1 = merge this workgroup's share, 2 = merge every item
+    int mode = 1;
+    const uint32_t old = __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t gen = old & 0x80000000u;
+    if ((int)(old & 0xFFFFu) == ns - 1) {
+      __hip_atomic_store(word, gen ^ 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old & 0x7FFF0000u) mode = 2;
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        uint32_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v & 0x80000000u) != gen) break;
+        if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) >= a.spin_ticks) {
+          // give up, unless the generation flips first
+          while ((v & 0x80000000u) == gen &&
+                 !__hip_atomic_compare_exchange_strong(word, &v, v + 0x10000u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)) {
+          }
+          if ((v & 0x80000000u) == gen) mode = 0;   // the swap succeeded: registered, leave
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    s_mode = mode;
+  }
+  __syncthreads();
+  asm volatile("" ::: "memory");
+  const int mode = s_mode;
+  if (mode == 0) return;
+  if (a.part_bf16) {
+    if (mode == 1) merge_share<T, __bf16, R>(a, b, rt, ns, BM, split, ns, s_st, wave, lane);
+    else merge_share<T, __bf16, R>(a, b, rt, ns, BM, 0, 1, s_st, wave, lane);
+  } else {
+    if (mode == 1) merge_share<T, float, R>(a, b, rt, ns, BM, split, ns, s_st, wave, lane);
+    else merge_share<T, float, R>(a, b, rt, ns, BM, 0, 1, s_st, wave, lane);
+  }
 }
 
 // CS (column split) = 1: the four waves own 32 rows each, all R output
@@ -539,8 +803,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if (bad) {
     // skipped sequence: zero output, lse = -inf (direct) or an empty partial
     if (tid == 0 && rt == 0 && split == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_LEN);
-    if (row_ok && hh == 0 && chalf == 0) {
-      if (DIRECT) {
+    if (row_ok && hh == 0 && chalf == 0 && (!a.fuse || split == 0)) {
+      if (DIRECT || a.fuse) {
         a.lse[(int64_t)b * a.M + m] = -INFINITY;
         T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
         for (int d = 0; d < R; ++d) o[d] = (T)0.0f;
@@ -1011,52 +1275,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * inv;
     }
   };
-  if (!row_ok) return;
-  if (DIRECT) {
-    T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
-#pragma unroll
-    for (int db = 0; db < NBL; ++db) {
-      if (!own_block(db)) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 av;
-        out_of(db, g, av);
-        const float v4[4] = {av[0], av[1], av[2], av[3]};
-        store4<T>(o + (chalf * NBL + db) * 32 + 8 * g + 4 * hh, v4);
-      }
-      if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
-    }
-    if (hh == 0 && chalf == 0 && kp == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
-  } else {
-    // Partials stay in accumulator order: the wave's 32 rows form one block
-    // of 32 x R values in which every store instruction writes one contiguous
-    // 1 KB run (float32: register group (db, g) of every lane; bf16: groups
-    // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).  Streaming
-    // stores: the merge reads them from memory anyway.
-    const int blk = rt * (BM / 32) + rb;
-    const int64_t base = (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R);
-    if (a.part_bf16) {
-      __bf16* o = static_cast<__bf16*>(a.part_o) + base + 8 * lane;
-#pragma unroll
-      for (int db = 0; db < NBL; ++db) {
-        if (!own_block(db)) continue;
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          f32x4 a0, a1;
-          out_of(db, 2 * gp, a0);
-          out_of(db, 2 * gp + 1, a1);
-          bf16x8 v8;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v8[e] = (__bf16)a0[e];
-            v8[4 + e] = (__bf16)a1[e];
-          }
-          __builtin_nontemporal_store(v8, reinterpret_cast<bf16x8*>(o + 512 * (2 * (chalf * NBL + db) + gp)));
-        }
-        if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      float* o = static_cast<float*>(a.part_o) + base + 4 * lane;
+  // a sequence with one split needs no merge: the fused launch writes its
+  // output directly too
+  const int ns_b = splits_of((int64_t)N, a.split_keys, a.max_splits);
+  const bool direct_now = DIRECT || (a.fuse && ns_b == 1);
+  if (direct_now) {
+    if (row_ok) {
+      T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
 #pragma unroll
       for (int db = 0; db < NBL; ++db) {
         if (!own_block(db)) continue;
@@ -1065,153 +1290,109 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           f32x4 av;
           out_of(db, g, av);
           const float v4[4] = {av[0], av[1], av[2], av[3]};
-          store4_f32_nt(o + 256 * (4 * (chalf * NBL + db) + g), v4);
+          store4<T>(o + (chalf * NBL + db) * 32 + 8 * g + 4 * hh, v4);
         }
-        if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
+      }
+      if (hh == 0 && chalf == 0 && kp == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
+    }
+  } else if (!DIRECT) {
+    if (row_ok) {
+      // Partials stay in accumulator order: the wave's 32 rows form one block
+      // of 32 x R values in which every store instruction writes one contiguous
+      // 1 KB run (float32: register group (db, g) of every lane; bf16: groups
+      // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).  Streaming,
+      // device-coherent stores: the merge reads them from other compute units.
+      const int blk = rt * (BM / 32) + rb;
+      const int64_t base = (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R);
+      if (a.part_bf16) {
+        __bf16* o = static_cast<__bf16*>(a.part_o) + base;
+#pragma unroll
+        for (int db = 0; db < NBL; ++db) {
+          if (!own_block(db)) continue;
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            f32x4 a0, a1;
+            out_of(db, 2 * gp, a0);
+            out_of(db, 2 * gp + 1, a1);
+            bf16x8 v8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v8[e] = (__bf16)a0[e];
+              v8[4 + e] = (__bf16)a1[e];
+            }
+            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (2 * (chalf * NBL + db) + gp)), v8);
+          }
+          if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        float* o = static_cast<float*>(a.part_o) + base;
+#pragma unroll
+        for (int db = 0; db < NBL; ++db) {
+          if (!own_block(db)) continue;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 av;
+            out_of(db, g, av);
+            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (4 * (chalf * NBL + db) + g)), av);
+          }
+          if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    if (hh == 0 && chalf == 0 && kp == 0) a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = lse_v;
+    if (row_ok && hh == 0 && chalf == 0 && kp == 0)
+      __hip_atomic_store(a.part_lse + ((int64_t)b * a.max_splits + split) * a.M + m, lse_v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if (a.fuse) {
+      fused_merge<T, R>(a, b, rt, split, ns_b, BM, reinterpret_cast<float*>(&s_tiles[0][0]), tid);
+    }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Cross-split merge: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
-// Partials are in accumulator order (32-row blocks, see the split kernel's
-// epilogue), so one wave handles one (sequence, block, column group) of 8
-// float32 or 16 bf16 columns: every lane reads 16 bytes per split and the
-// wave's reads are one contiguous 1 KB run.  Splits are consumed sixteen at a
-// time with a running maximum, so sixteen loads per lane are in flight (one
-// memory round trip for up to sixteen splits).  Splits with lse_k = -inf are
-// skipped by selection, never by multiplication: their partial output may
-// never have been written.
-template <typename PT>
-struct PartLoad;
-template <>
-struct PartLoad<float> {
-  static constexpr int NV = 4;                  // values per lane per split
-  typedef f32x4 raw;
-  __device__ static __forceinline__ float get(const raw& r, int i) { return r[i]; }
-};
-template <>
-struct PartLoad<__bf16> {
-  static constexpr int NV = 8;
-  typedef bf16x8 raw;
-  __device__ static __forceinline__ float get(const raw& r, int i) { return (float)r[i]; }
-};
-
-// WIDE: one (sequence, block, column group) per workgroup, its splits cut
-// into four contiguous ranges, one per wave, which all load at once; the four
-// partial states (max, sum, weighted columns) are then combined through LDS
-// by wave 0.  Used when there are more splits than one wave loads in one
-// round trip.  Otherwise one item per wave.
+// WIDE: one (sequence, block, column group) per workgroup; used when there
+// are more splits than one wave loads in one round trip.  Otherwise one item
+// per wave.
 template <typename T, typename PT, bool WIDE>
 __global__ __launch_bounds__(256) void merge_kernel(
     const PT* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
     int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys,
     T* __restrict__ out, int64_t out_sb, int64_t out_st, int64_t out_sh, float* __restrict__ lse) {
-  constexpr int U = 16;
   constexpr int NV = PartLoad<PT>::NV;
-  constexpr int CW = 2 * NV;                    // columns per wave
-  typedef typename PartLoad<PT>::raw raw;
-  __shared__ float s_st[WIDE ? 4 * (NV + 2) * 64 : 1];   // per wave: max, sum, NV columns per lane
-  const int n_cg = R / CW;
+  __shared__ float s_st[WIDE ? 4 * (NV + 2) * 64 : 1];
+  const int n_cg = R / (2 * NV);
   const int wave = threadIdx.x >> 6;
   const int64_t wid = WIDE ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  const int lane = threadIdx.x & 63, hh = lane >> 5;
+  const int lane = threadIdx.x & 63;
   if (wid >= (int64_t)B * n_blk * n_cg) return;  // (uniform over the workgroup when WIDE)
   const int cg = (int)(wid % n_cg);
   const int64_t bblk = wid / n_cg;
   const int blk = (int)(bblk % n_blk), b = (int)(bblk / n_blk);
   const int M = q * H;
-  const int m = blk * 32 + (lane & 31);
-  const bool row_ok = m < M;
-  if (!WIDE && !row_ok) return;
-  int ns = max_splits;
-  if (split_keys > 0) {
-    const int64_t n = (int64_t)prefix_lens[b] + q;
-    ns = (int)((n + split_keys - 1) / split_keys);
-    ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
-  }
-  const int per = WIDE ? (ns + 3) / 4 : ns;
-  const int kb = WIDE ? wave * per : 0;
-  const int ke = row_ok ? min(ns, kb + per) : kb;   // padding rows of a wide block load nothing
-  const float* pl = part_lse + (int64_t)b * max_splits * M + (row_ok ? m : 0);
-  const int64_t split_stride = (int64_t)n_blk * 32 * R;
-  const PT* po = part_o + ((int64_t)b * max_splits * n_blk + blk) * (32 * R) + 32 * CW * cg + NV * lane;
-  float mx = -INFINITY, z = 0.0f;
-  float acc[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-  for (int k0 = kb; k0 < ke; k0 += U) {
-    float lk[U];
-    raw ok[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int k = k0 + j;
-      lk[j] = k < ke ? pl[(int64_t)k * M] : -INFINITY;
-      if (k < ke) ok[j] = *reinterpret_cast<const raw*>(po + k * split_stride);
-    }
-    float cm = lk[0];
-#pragma unroll
-    for (int j = 1; j < U; ++j) cm = fmaxf(cm, lk[j]);
-    if (cm > mx) {
-      const float sc = __expf(mx - cm);   // 0 while mx is still -inf
-      z *= sc;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i] *= sc;
-      mx = cm;
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const bool live = lk[j] != -INFINITY;
-      const float w = live ? __expf(lk[j] - mx) : 0.0f;
-      z += w;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i] = live ? acc[i] + w * PartLoad<PT>::get(ok[j], i) : acc[i];
-    }
-  }
-  if constexpr (WIDE) {
-    float* st = s_st + wave * (NV + 2) * 64 + lane;
-    st[0] = mx;
-    st[64] = z;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) st[64 * (2 + i)] = acc[i];
-    __syncthreads();
-    if (wave != 0 || !row_ok) return;
-    // combine the four states against their common max (a wave without a
-    // finite split has max -inf and no weight)
-    float mw[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mw[w] = s_st[w * (NV + 2) * 64 + lane];
-    const float mt = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-    mx = mt;
-    z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float* sw = s_st + w * (NV + 2) * 64 + lane;
-      const float f = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - mt);
-      z += f * sw[64];
-#pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i] += f * sw[64 * (2 + i)];
-    }
-  }
-  const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-  const int t = m / H, h = m - t * H;
-  T* o = out + b * out_sb + t * out_st + h * out_sh + CW * cg + 4 * hh;
-#pragma unroll
-  for (int q4 = 0; q4 < NV / 4; ++q4) {       // value i of the lane is column CW*cg + 8*(i/4) + 4*hh + i%4
-    const float v4[4] = {acc[4 * q4] * inv, acc[4 * q4 + 1] * inv, acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv};
-    store4<T>(o + 8 * q4, v4);
-  }
-  if (cg == 0 && hh == 0) lse[(int64_t)b * M + m] = z > 0.0f ? mx + logf(z) : -INFINITY;
+  const int ns = split_keys > 0 ? splits_of((int64_t)prefix_lens[b] + q, split_keys, max_splits) : max_splits;
+  merge_item<T, PT, WIDE, false>(part_o, part_lse, max_splits, ns, M, H, R, n_blk, b, blk, cg, out, out_sb, out_st,
+                                 out_sh, lse, s_st, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 
 static int elem_size(int dtype) { return dtype == KDT_F32 ? 4 : dtype == KDT_BF16 ? 2 : 0; }
+
+// Compute units of the current device (host query, cached per device; kCU
+// when the runtime cannot say).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kCU;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kCU;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+constexpr int kDefaultWaitUs = 2000;     // longest wait of a split workgroup in the fused merge
 
 static bool shape_supported(int dtype, int R, int P) {
   if (dtype == KDT_BF16) return (R == 512 && P == 64) || (R == 64 && P == 16);
@@ -1234,6 +1415,7 @@ static int validate(const kdt_verify_desc* d) {
   if (d->split_keys < 0 || (d->split_keys % kBN) != 0) return KDT_ERR_INVALID_ARG;
   if (d->layout < 0 || d->layout > 4) return KDT_ERR_INVALID_ARG;
   if (d->partials_f32 != 0 && d->partials_f32 != 1) return KDT_ERR_INVALID_ARG;
+  if (d->merge_mode != 0 && d->merge_mode != 1) return KDT_ERR_INVALID_ARG;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
   if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
   if (!shape_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
@@ -1333,12 +1515,23 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int64_t o_bytes = (int64_t)d->B * ns * ((M + 31) / 32) * 32 * d->R * elem_size(part_dtype);
   p->part_o_offset = 0;
   p->part_lse_offset = (o_bytes + 255) / 256 * 256;
-  p->workspace_bytes = (size_t)(p->part_lse_offset + n_part_rows * 4);
+  p->partials_bytes = (size_t)(p->part_lse_offset + n_part_rows * 4);
+  // merge inside the split kernel on request, when every split workgroup can
+  // be resident at once (one workgroup per compute unit)
+  const int64_t n_rt = (M + layout_rows(p->layout) - 1) / layout_rows(p->layout);
+  const int64_t grid = (int64_t)d->B * n_rt * ns;
+  p->fused_merge = (!p->direct && d->merge_mode == 1 && grid <= device_cus()) ? 1 : 0;
+  p->counter_offset = ((int64_t)p->partials_bytes + 255) / 256 * 256;
+  p->workspace_bytes = p->direct ? 0 : (size_t)(p->counter_offset + (int64_t)d->B * n_rt * 4);
   return KDT_OK;
 }
 
-static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, void* ws) {
+static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, void* ws, bool fuse) {
   VerifyArgs a;
+  a.fuse = fuse ? 1 : 0;
+  a.counters = (ws && fuse) ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.counter_offset) : nullptr;
+  const int64_t wait_us = d->merge_wait_us == 0 ? kDefaultWaitUs : (d->merge_wait_us < 0 ? 0 : d->merge_wait_us);
+  a.spin_ticks = wait_us * 100;          // 100 MHz
   a.q_lat = d->q_lat; a.q_lat_sb = d->q_lat_sb; a.q_lat_st = d->q_lat_st; a.q_lat_sh = d->q_lat_sh;
   a.q_pe = d->q_pe; a.q_pe_sb = d->q_pe_sb; a.q_pe_st = d->q_pe_st; a.q_pe_sh = d->q_pe_sh;
   a.c_kv = d->c_kv; a.c_kv_sb = d->c_kv_sb; a.c_kv_ss = d->c_kv_ss;
@@ -1454,9 +1647,9 @@ extern "C" int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t
   if (!p.direct && (!workspace || ws_bytes < p.workspace_bytes)) return KDT_ERR_WORKSPACE;
   if (!p.direct && !kdt::aligned16(workspace)) return KDT_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const kdt::VerifyArgs a = kdt::make_args(d, p, p.direct ? nullptr : workspace);
+  const kdt::VerifyArgs a = kdt::make_args(d, p, p.direct ? nullptr : workspace, p.fused_merge != 0);
   int r = kdt::dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
-  if (r != KDT_OK || p.direct) return r;
+  if (r != KDT_OK || p.direct || p.fused_merge) return r;
   return kdt::launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, p.part_dtype, a.part_o, a.part_lse, p.max_splits,
                            d->prefix_lens, p.split_keys, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
 }
@@ -1466,8 +1659,8 @@ extern "C" int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, si
   kdt_verify_plan p;
   const int rc = kdt::make_plan(d, &p);
   if (rc != KDT_OK) return rc;
-  if (!workspace || ws_bytes < p.workspace_bytes || !kdt::aligned16(workspace)) return KDT_ERR_WORKSPACE;
-  const kdt::VerifyArgs a = kdt::make_args(d, p, workspace);
+  if (!workspace || ws_bytes < p.partials_bytes || !kdt::aligned16(workspace)) return KDT_ERR_WORKSPACE;
+  const kdt::VerifyArgs a = kdt::make_args(d, p, workspace, false);
   return kdt::dispatch_split(d->dtype, d->R, d->P, a, false, static_cast<hipStream_t>(stream));
 }
 

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdt.so")
 
 KDT_F32, KDT_BF16 = 0, 1
-ABI_VERSION = 3                       # the KDT_ABI_VERSION this binding was written for
+ABI_VERSION = 4                       # the KDT_ABI_VERSION this binding was written for
 KDT_SEQ_BAD_TREE, KDT_SEQ_BAD_LEN, KDT_SEQ_BAD_INDEX = 1, 2, 4
 MAX_Q_LEN = 128
 
@@ -40,13 +40,16 @@ class VerifyDesc(ctypes.Structure):
         ("seq_status", _c_p),
         ("split_keys", _c_i32), ("layout", _c_i32), ("partials_f32", _c_i32),
         ("parents", _c_p),
+        ("merge_mode", _c_i32), ("merge_wait_us", _c_i32),
     ]
 
 
 class VerifyPlan(ctypes.Structure):
     _fields_ = [
         ("split_keys", _c_i32), ("max_splits", _c_i32), ("rows", _c_i32), ("direct", _c_i32),
-        ("layout", _c_i32), ("part_dtype", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64), ("workspace_bytes", ctypes.c_size_t),
+        ("layout", _c_i32), ("part_dtype", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64),
+        ("workspace_bytes", ctypes.c_size_t), ("partials_bytes", ctypes.c_size_t), ("fused_merge", _c_i32),
+        ("reserved", _c_i32), ("counter_offset", _c_i64),
     ]
 
 
@@ -139,7 +142,7 @@ def build_visibility(parents: torch.Tensor, vis=None, depth=None, seq_status=Non
 
 
 def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                 seq_status, split_keys, layout=0, partials_f32=False, parents=None):
+                 seq_status, split_keys, layout=0, partials_f32=False, parents=None, merge_mode=0, merge_wait_us=0):
     B, q, H, R = q_lat.shape
     P = q_pe.shape[-1]
     d = VerifyDesc()
@@ -161,11 +164,14 @@ def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_p
     d.split_keys = int(split_keys)
     d.layout = int(layout)
     d.partials_f32 = 1 if partials_f32 else 0
+    d.merge_mode = int(merge_mode)
+    d.merge_wait_us = int(merge_wait_us)
     return d
 
 
 def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                    seq_status, split_keys, layout=0, partials_f32=False, parents=None):
+                    seq_status, split_keys, layout=0, partials_f32=False, parents=None, merge_mode=0,
+                    merge_wait_us=0):
     for t in (q_lat, q_pe, c_kv, k_pe):
         if t.stride(-1) != 1:
             raise ValueError("innermost dimension must be contiguous")
@@ -186,7 +192,7 @@ def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
     if lse is None:
         lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
     d = _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
-                     seq_status, split_keys, layout, partials_f32, parents)
+                     seq_status, split_keys, layout, partials_f32, parents, merge_mode, merge_wait_us)
     return d, out, lse
 
 
@@ -198,16 +204,21 @@ def verify_plan(desc: VerifyDesc) -> VerifyPlan:
 
 def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
                 lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
-                parents=None):
+                parents=None, merge_mode=0, merge_wait_us=0):
     """Tree-verify attention.  c_kv [B, S, R] and k_pe [B, S, P] may be views of
     one fused [B, S, R+P] cache.  vis may be None when parents [B, q] int32 is
-    given (the split kernel then derives the masks).  Returns
+    given (the split kernel then derives the masks).  merge_mode 1 merges the
+    splits inside the split kernel (when the launch fits the device); a
+    caller-given workspace must then have been allocated zeroed (its merge
+    state words; every call leaves their counts at zero).  Without a workspace
+    a zeroed one is allocated per call.  Returns
     (out [B, q, H, R], lse [B, q, H])."""
     d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
-                                  out, lse, seq_status, split_keys, layout, partials_f32, parents)
+                                  out, lse, seq_status, split_keys, layout, partials_f32, parents, merge_mode,
+                                  merge_wait_us)
     p = verify_plan(d)
     if p.workspace_bytes and (workspace is None or workspace.numel() * workspace.element_size() < p.workspace_bytes):
-        workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
+        workspace = torch.zeros(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("kdt_verify_attn", lib().kdt_verify_attn(ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
@@ -258,7 +269,7 @@ def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
                               None, None, seq_status, split_keys, layout, partials_f32, parents)
     p = verify_plan(d)
     B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
-    need = max(int(p.workspace_bytes), p.part_lse_offset + B * S * M * 4, 1)
+    need = max(int(p.partials_bytes), 1)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
     ws_bytes = workspace.numel() * workspace.element_size()
