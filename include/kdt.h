@@ -234,6 +234,22 @@ int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, 
  * `out`/`lse` are not touched and nothing is merged. */
 int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as kdt_verify_attn, with the workspace taken from a fixed
+ * device array inside the library instead of from the caller.  Each GPU that
+ * loads the library holds its own copy of that array (KDT_NOALLOC_MAX_WORKSPACE
+ * bytes) until the process ends; its address is looked up once per device, on
+ * the first call with that device current.  Nothing is allocated or freed.
+ * Every call on one GPU uses the same array, so calls that overlap in time on
+ * one GPU (several streams, several host threads) race and must be
+ * serialised by the caller.  Returns KDT_ERR_WORKSPACE when the plan's
+ * workspace_bytes exceeds KDT_NOALLOC_MAX_WORKSPACE (force a larger
+ * split_keys, or use kdt_verify_attn), and KDT_ERR_UNSUPPORTED for
+ * merge_mode 1 (its state words would have to start at zero). */
+#define KDT_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+int kdt_verify_attn_noalloc(const kdt_verify_desc* d, void* stream);
+
 /* ------------------------------------------------------------------------
  * kdt_merge_partials — cross-split log-sum-exp merge.
  *   lse[b,m] = ln sum_k exp(part_lse[b,k,m]);

@@ -64,6 +64,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "kdt_common.hpp"
 
@@ -1633,6 +1634,38 @@ static int launch_merge(int dtype, int B, int q, int H, int R, int part_dtype, c
                         out, osb, ost, osh, lse, s);
 }
 
+// The verify with a given workspace (NULL when the plan is direct).
+static int verify_run(const kdt_verify_desc* d, const kdt_verify_plan& p, void* workspace, hipStream_t s) {
+  const VerifyArgs a = make_args(d, p, p.direct ? nullptr : workspace, p.fused_merge != 0);
+  int r = dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
+  if (r != KDT_OK || p.direct || p.fused_merge) return r;
+  return launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, p.part_dtype, a.part_o, a.part_lse, p.max_splits,
+                      d->prefix_lens, p.split_keys, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
+}
+
+// Workspace of kdt_verify_attn_noalloc: a fixed device array, one per GPU
+// (each device that loads the library holds its own copy until the process
+// ends).  Host code never uses the array's name as an address: the device
+// address of each GPU's copy is looked up once, with that GPU current, and
+// kept.
+constexpr size_t kScratchBytes = KDT_NOALLOC_MAX_WORKSPACE;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+static void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace kdt
 
 extern "C" int kdt_verify_get_plan(const kdt_verify_desc* d, kdt_verify_plan* plan) {
@@ -1646,12 +1679,22 @@ extern "C" int kdt_verify_attn(const kdt_verify_desc* d, void* workspace, size_t
   if (rc != KDT_OK) return rc;
   if (!p.direct && (!workspace || ws_bytes < p.workspace_bytes)) return KDT_ERR_WORKSPACE;
   if (!p.direct && !kdt::aligned16(workspace)) return KDT_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const kdt::VerifyArgs a = kdt::make_args(d, p, p.direct ? nullptr : workspace, p.fused_merge != 0);
-  int r = kdt::dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
-  if (r != KDT_OK || p.direct || p.fused_merge) return r;
-  return kdt::launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, p.part_dtype, a.part_o, a.part_lse, p.max_splits,
-                           d->prefix_lens, p.split_keys, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
+  return kdt::verify_run(d, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kdt_verify_attn_noalloc(const kdt_verify_desc* d, void* stream) {
+  kdt_verify_plan p;
+  const int rc = kdt::make_plan(d, &p);
+  if (rc != KDT_OK) return rc;
+  // the merge state words of the in-kernel merge would have to start at zero
+  if (d->merge_mode != 0) return KDT_ERR_UNSUPPORTED;
+  if (p.workspace_bytes > kdt::kScratchBytes) return KDT_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (!p.direct) {
+    ws = kdt::scratch_ptr();
+    if (!ws) return KDT_ERR_LAUNCH;
+  }
+  return kdt::verify_run(d, p, ws, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int kdt_verify_partials(const kdt_verify_desc* d, void* workspace, size_t ws_bytes,

@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.kdt_verify_get_plan.argtypes = [ctypes.POINTER(VerifyDesc), ctypes.POINTER(VerifyPlan)]
         L.kdt_verify_attn.argtypes = [ctypes.POINTER(VerifyDesc), _c_p, ctypes.c_size_t, _c_p]
         L.kdt_verify_partials.argtypes = [ctypes.POINTER(VerifyDesc), _c_p, ctypes.c_size_t, _c_p]
+        L.kdt_verify_attn_noalloc.argtypes = [ctypes.POINTER(VerifyDesc), _c_p]
         L.kdt_merge_partials.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p,
                                          _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]
         L.kdt_gather_accepted.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
@@ -88,7 +89,8 @@ def lib() -> ctypes.CDLL:
         L.kdt_absorb_o.argtypes = [_c_i32] * 6 + [_c_p, _c_p, _c_p, _c_p]
         L.kdt_append_tree_kv.argtypes = [_c_i32] * 5 + [_c_p, _c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_i64, _c_i64,
                                                         _c_i64, _c_p, _c_p]
-        for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_partials",
+        for fn in ("kdt_build_visibility", "kdt_verify_get_plan", "kdt_verify_attn", "kdt_verify_attn_noalloc",
+                   "kdt_verify_partials",
                    "kdt_merge_partials", "kdt_gather_accepted", "kdt_tree_accept", "kdt_build_tree",
                    "kdt_absorb_q", "kdt_absorb_o", "kdt_append_tree_kv"):
             getattr(L, fn).restype = ctypes.c_int
@@ -221,6 +223,21 @@ def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_pr
         workspace = torch.zeros(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("kdt_verify_attn", lib().kdt_verify_attn(ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+NOALLOC_MAX_WORKSPACE = 32 << 20              # KDT_NOALLOC_MAX_WORKSPACE
+
+
+def verify_attn_noalloc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
+                        lse=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
+                        parents=None):
+    """kdt_verify_attn_noalloc: the same as verify_attn, with the library's own
+    fixed device workspace (no allocation; calls on one GPU must not
+    overlap).  out and lse should be given when nothing may be allocated."""
+    d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
+                                  out, lse, seq_status, split_keys, layout, partials_f32, parents)
+    _check("kdt_verify_attn_noalloc", lib().kdt_verify_attn_noalloc(ctypes.byref(d), _stream(stream)))
     return out, lse
 
 
