@@ -505,10 +505,11 @@ __device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const 
 
 // Number of splits sequence b uses: ceil((L + q) / split_keys) in [1, max_splits]
 // (max_splits when split_keys is 0).
+// (n_keys >= 1 and below 2^32 + 1: 32-bit arithmetic, no overflow)
 __device__ __forceinline__ int splits_of(int64_t n_keys, int split_keys, int max_splits) {
-  if (split_keys <= 0) return max_splits;
-  const int64_t ns = (n_keys + split_keys - 1) / split_keys;
-  return ns < 1 ? 1 : (ns > max_splits ? max_splits : (int)ns);
+  if (split_keys <= 0 || n_keys <= 0) return max_splits > 0 && n_keys <= 0 ? 1 : max_splits;
+  const uint32_t ns = (uint32_t)(n_keys - 1) / (uint32_t)split_keys + 1u;
+  return ns > (uint32_t)max_splits ? max_splits : (int)ns;
 }
 
 template <typename T, typename PT, int R>
@@ -948,6 +949,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // Key streams: the next pair of tiles (copied between this step's score
   // MFMAs; rows 0 = no such tile).
   int ks_t0 = 0, ks_t1 = 0, ks_r0 = 0, ks_r1 = 0;
+  // Key streams: accumulator block db of stream kp holds output column block
+  // col_block(db) = (db + 8 kp) mod 16, so that every wave keeps blocks 0-7
+  // and hands blocks 8-15 to its partner at the end (register indices fixed
+  // at compile time on both streams); the value operand of block db is read
+  // at LDS offset 64 db + rot_off[db >= 8] instead of 64 col_block(db).
+  const int rot_off[2] = {512 * kp, -512 * kp};
+  auto col_block = [&](int db) { return KS ? ((db + 8 * kp) & 15) : chalf * NBL + db; };
   uint32_t ks_b0 = 0, ks_b1 = 0;          // (LDS addresses)
   auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, uint32_t st_buf)
                        __attribute__((always_inline)) {
@@ -1025,8 +1033,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
       } else {
         // bf16: two transposing reads (lane bases computed before the loop)
-        const int dg = chalf * NBL + db;      // global output column block
-        const int o = 64 * dg + c * 16 * RC * 16;
+        const int dg = chalf * NBL + db;      // output column block (key streams: rotated, below)
+        const int o = (KS ? 64 * db + rot_off[db >= NBL / 2] : 64 * dg) + c * 16 * RC * 16;
         const bf16x4 lo = lds_read_tr16(buf + pv_base[0][dg & 3] + o);
         const bf16x4 hi = lds_read_tr16(buf + pv_base[1][dg & 3] + o);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1224,12 +1232,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   if constexpr (KS) {
     tile_barrier();                           // every wave is done with the ring
 #pragma unroll
-    for (int db = 0; db < NBL; ++db) {
-      if ((db >> 3) == kp) continue;          // (the half this wave keeps)
-      // straight from the accumulation registers (a copy through ordinary
-      // registers made the compiler spill accumulators to scratch); the
-      // four groups of block db sit 1 KB apart, each lane's 16 bytes
-      // consecutive across lanes
+    for (int db = NBL / 2; db < NBL; ++db) {  // (blocks 0-7 are the half this wave keeps)
+      // straight from the accumulation registers; the four groups of block
+      // db sit 1 KB apart, each lane's 16 bytes consecutive across lanes
       const uint32_t ad = lds_addr(xw + (((db & 7) * 4) * 64 + lane) * 4);
       asm volatile(
           "ds_write_b128 %0, %1\n\t"
@@ -1255,8 +1260,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     l_run = l_run * f0 + l1 * f1;
     m_ref = mt;
   }
-  // the output blocks this wave writes (key streams: its column half)
-  auto own_block = [&](int db) { return !KS || (db >> 3) == kp; };
+  // the accumulator blocks this wave writes (key streams: blocks 0-7, its
+  // column half)
+  auto own_block = [&](int db) { return !KS || db < NBL / 2; };
   // ---- epilogue: normalise and write (direct) or write the partial
   const float l_tot = xhalf_sum(l_run);
   const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -1268,6 +1274,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // normalised output (db, 4 g + e) of this lane, both key streams combined
   auto out_of = [&](int db, int g, f32x4& v) __attribute__((always_inline)) {
     if constexpr (KS) {
+      // the partner's accumulator block db + 8 (the same output columns)
       const f32x4 o = *reinterpret_cast<const f32x4*>(xr + (((db & 7) * 4 + g) * 64 + lane) * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * f0 + o[e] * f1;
@@ -1291,7 +1298,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           f32x4 av;
           out_of(db, g, av);
           const float v4[4] = {av[0], av[1], av[2], av[3]};
-          store4<T>(o + (chalf * NBL + db) * 32 + 8 * g + 4 * hh, v4);
+          store4<T>(o + col_block(db) * 32 + 8 * g + 4 * hh, v4);
         }
         if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
       }
@@ -1322,7 +1329,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
               v8[e] = (__bf16)a0[e];
               v8[4 + e] = (__bf16)a1[e];
             }
-            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (2 * (chalf * NBL + db) + gp)), v8);
+            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (2 * col_block(db) + gp)), v8);
           }
           if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
         }
@@ -1335,7 +1342,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
           for (int g = 0; g < 4; ++g) {
             f32x4 av;
             out_of(db, g, av);
-            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (4 * (chalf * NBL + db) + g)), av);
+            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (4 * col_block(db) + g)), av);
           }
           if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
         }
