@@ -5,14 +5,19 @@
 One step = the whole hot path over one batch: visibility masks from parent
 pointers (derived inside the split kernel; --separate-visibility runs the
 visibility kernel first instead), split-prefix verify attention + log-sum-exp
-merge, and the accepted-path gather.  Inputs are seeded synthetic tensors of the workload's
-shape, resident in HBM before timing starts; the step rotates over enough input
-copies (> 256 MB) that the Infinity Cache cannot hold them all.
+merge, and the accepted-path gather.  Inputs are seeded synthetic tensors of the
+workload's shape, resident in HBM before timing starts.  Step i reads input copy
+i mod n, in a ring that warm-up and timed steps continue without a break, and
+n is chosen so that between two uses of one copy the other copies move more
+than 320 MB: no step, timed or not, can find its inputs in the 256 MB Infinity
+Cache, whatever --steps is.
 
 Printed: one JSON line (metric, tree-tokens/s, ms per step, ...) with
-  roofline     the verify-split kernel: algorithmic flops per launch / its mean
-               launch time, timed with HIP events on the stream it runs on,
-               against the MI355X dense bf16 MFMA peak;
+  roofline     the verify-split kernel against the roofline that binds the
+               workload (matrix cores when its flops per algorithmic byte are
+               above the ridge point, 2.5 PFLOP/s / 8 TB/s, else HBM):
+               algorithmic flops (or bytes) per launch / its mean launch time,
+               timed with HIP events on the stream it runs on;
   cpu_baseline the float64 CPU oracle timed on the same workload (rank 0, N=1).
 """
 from __future__ import annotations
@@ -175,9 +180,10 @@ def main():
             return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    # --- resident inputs, rotated over > Infinity Cache size
+    # --- resident inputs: a ring of copies; between two uses of one copy the
+    # other n - 1 move more than the Infinity Cache holds
     per_copy = inp.cache.nbytes + inp.q_lat.nbytes + inp.q_pe.nbytes
-    n_copies = max(2, min(64, -(-(INFINITY_CACHE_BYTES + (32 << 20)) // per_copy)))
+    n_copies = max(2, min(128, 1 + -(-(INFINITY_CACHE_BYTES + (64 << 20)) // per_copy)))
     base = {"cache": t_of(inp.cache), "q_lat": t_of(inp.q_lat), "q_pe": t_of(inp.q_pe)}
     copies = [{k: v.clone() for k, v in base.items()} for _ in range(n_copies)]
     parents = torch.from_numpy(inp.parents).to(dev)
@@ -246,22 +252,20 @@ def main():
         print(json.dumps({"eager_steps": args.steps, "warmup": args.warmup, "workload": args.workload,
                           "kernel_only": bool(args.kernel_only)}), flush=True)
         return
+    # one pass over the ring, the warm-up steps 0 .. W-1 and the timed steps
+    # W .. W+K-1 (step i reads copy i mod n): captured first (each capture
+    # runs its steps once), then replayed in ring order
     g_all = capture(fn, range(n_copies))
-    g_one = [capture(fn, [i]) for i in range(max(args.steps % n_copies, args.warmup % n_copies, 1))]
-
-    def run_steps(k):
-        full, rem = divmod(k, n_copies)
-        for _ in range(full):
-            g_all.replay()
-        for i in range(rem):
-            g_one[i].replay()
-
-    run_steps(args.warmup)
+    g_warm = capture(fn, range(args.warmup)) if args.warmup > 0 else None
+    g_timed = capture(fn, range(args.warmup, args.warmup + args.steps))
+    g_all.replay()
+    if g_warm is not None:
+        g_warm.replay()
     torch.cuda.synchronize()
 
     # --- timed region: exactly K steps
     t0 = time.perf_counter()
-    run_steps(args.steps)
+    g_timed.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -278,6 +282,31 @@ def main():
     e1.record(cur)
     torch.cuda.synchronize()
     split_ms = e0.elapsed_time(e1) / (reps * n_copies)
+
+    # --- the same split kernel writing float32 partials (the bf16 partials
+    # are the default for bf16 inputs; this is what the extra rounding saves)
+    split_f32_us = None
+    if cfg.dtype == "bf16" and not args.partials_f32:
+        d32, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
+                                        prefix_lens, vis_arg, cfg.softmax_scale, max_prefix, out, lse, None,
+                                        args.split_keys, args.layout, True, par_arg)
+        p32 = kdt.verify_plan(d32)
+        ws32 = torch.zeros(max(int(p32.partials_bytes), int(p32.workspace_bytes)), dtype=torch.uint8, device=dev)
+
+        def split_only32(i):
+            c = copies[i % n_copies]
+            kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens,
+                                vis_arg, cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws32,
+                                split_keys=args.split_keys, layout=args.layout, partials_f32=True, parents=par_arg)
+        g32 = capture(split_only32, range(n_copies))
+        g32.replay()
+        e0.record(cur)
+        for _ in range(reps):
+            g32.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        split_f32_us = e0.elapsed_time(e1) * 1e3 / (reps * n_copies)
+        del g32, ws32
 
     # --- one verify call (split + merge) on its own: per-call mean over one
     # replay of a graph of n_copies calls, median and p90 over replays
@@ -379,8 +408,16 @@ def main():
     kv_bytes = int(np.sum(inp.prefix_lens.astype(np.int64) + q)) * (R + P) * esz
     alg_bytes = (kv_bytes + B * q * H * (R + P) * esz + B * q * H * R * esz + B * q * H * 4
                  + B * q * W * 8 + B * q * 4)
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    achieved = flops / (split_ms * 1e-3) / 1e12
+    peak_flops = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    # the roofline that binds the workload: matrix cores above the ridge
+    # point (peak flops / peak bandwidth), HBM below it
+    mfma_bound = flops / alg_bytes >= peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        bound, unit, peak = "mfma", "TFLOP/s", peak_flops
+        achieved = flops / (split_ms * 1e-3) / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
+        achieved = alg_bytes / (split_ms * 1e-3) / 1e9
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_verify_split_{args.workload.replace(':', '_')}.json")
@@ -411,10 +448,13 @@ def main():
                    "step": ("build_visibility + verify (split + merge) + gather_accepted" if args.separate_visibility
                             else "verify (split kernel deriving the masks from the parents + merge) + gather_accepted"),
                    "input_copies": n_copies, "kernel_only": bool(args.kernel_only)},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "verify_split_kernel", "kernel_ms": split_ms,
-                     "flops_per_launch": flops, "visible_pairs": pairs},
+                     "flops_per_launch": flops, "bytes_per_launch": alg_bytes, "visible_pairs": pairs,
+                     "mfma_frac": flops / (split_ms * 1e-3) / 1e12 / peak_flops,
+                     "hbm_frac": alg_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "split_kernel_us_f32_partials": split_f32_us,
         "verify_attn_us": verify_us,
         "verify_tree_tokens_per_s": (B * q / (verify_us["median"] * 1e-6)) if verify_us else None,
         "mfma_util": flops / (ms_per_step * 1e-3) / 1e12 / peak,
