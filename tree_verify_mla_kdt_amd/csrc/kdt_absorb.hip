@@ -11,7 +11,7 @@
 //
 //  * absorb_q:  q_lat[m, h, :] = w_kc_t[h] (R x dn) . q[m, h, :dn], and
 //               q_pe[m, h, :] = NeoX rope of q[m, h, dn:] at L_b + depth(t),
-//    for rows m = (b, t).
+//    for rows m = (b, t), in one launch (the rope in the same workgroups).
 //  * absorb_o:  o[m, h, :] = w_vc[h] (dv x R) . o_lat[m, h, :].
 //  * append:    cache row L_b + t gets the token's latent and its rotary key
 //               rotated at L_b + depth(t).
@@ -46,12 +46,44 @@ struct RowSrc {
   }
 };
 
+// Rotation of pair i at position pos: the pair (x[i], x[i + P/2]) turns by
+// pos * theta^(-2i/P).  The angle is formed and reduced to [-pi, pi] in double
+// precision (positions reach 10^5 and more); the sine and cosine of the
+// reduced angle are taken in single precision.
+__device__ __forceinline__ void rope_angle(int P, int i, double pos, double log2_theta, float& c, float& s) {
+  const double ang = pos * exp2(-(2.0 * i / P) * log2_theta);
+  const double two_pi = 6.283185307179586476925286766559;
+  const float red = (float)(ang - two_pi * rint(ang / two_pi));
+  s = sinf(red);
+  c = cosf(red);
+}
+
+__device__ __forceinline__ void rope_apply(const __bf16* src, __bf16* dst, int half, int i, float c, float s) {
+  const float x1 = (float)src[i], x2 = (float)src[i + half];
+  dst[i] = (__bf16)(x1 * c - x2 * s);
+  dst[i + half] = (__bf16)(x2 * c + x1 * s);
+}
+
+// The rotary part of the query split, done by the absorb_q launch itself:
+// q_pe[b, t, h, :] = rope(q[b, t, h, dn:], L_b + depth[b, t]) (off when q_pe
+// is null, as for absorb_o).
+struct RopeArgs {
+  const int32_t* prefix_lens;
+  const int32_t* depth;
+  double log2_theta;
+  __bf16* q_pe;
+  int dn, P;
+};
+
 // C^T[n][m] = sum_k W[h][n][k] X[m][k]; W is [H, N, K] contiguous, the output
 // [rows, H, N] contiguous.  KS = K / 16 contraction steps, NCB output blocks
-// of 32 per workgroup (their weight fragments stay in registers).
+// of 32 per workgroup (their weight fragments stay in registers).  With
+// rope.q_pe set, the workgroups of head h and row group z also rotate the
+// query's rope part for those rows, the pairs shared among the gridDim.y
+// workgroups of the group.
 template <int KS, int NCB>
 __global__ __launch_bounds__(256) void absorb_gemm_kernel(RowSrc x, const __bf16* __restrict__ w, int M, int H,
-                                                          int N, __bf16* __restrict__ out) {
+                                                          int N, __bf16* __restrict__ out, RopeArgs rope) {
   constexpr int K = KS * 16;
   const int h = blockIdx.x;
   const int nb0 = blockIdx.y * NCB;            // first 32-wide output block of this workgroup
@@ -94,42 +126,17 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(RowSrc x, const __bf16
             bf16x4_t{(__bf16)acc[cb][4 * g], (__bf16)acc[cb][4 * g + 1], (__bf16)acc[cb][4 * g + 2],
                      (__bf16)acc[cb][4 * g + 3]};
   }
-}
-
-// Rotation of pair i at position pos: the pair (x[i], x[i + P/2]) turns by
-// pos * theta^(-2i/P).  The angle is formed and reduced to [-pi, pi] in double
-// precision (positions reach 10^5 and more); the sine and cosine of the
-// reduced angle are taken in single precision.
-__device__ __forceinline__ void rope_angle(int P, int i, double pos, double log2_theta, float& c, float& s) {
-  const double ang = pos * exp2(-(2.0 * i / P) * log2_theta);
-  const double two_pi = 6.283185307179586476925286766559;
-  const float red = (float)(ang - two_pi * rint(ang / two_pi));
-  s = sinf(red);
-  c = cosf(red);
-}
-
-__device__ __forceinline__ void rope_apply(const __bf16* src, __bf16* dst, int half, int i, float c, float s) {
-  const float x1 = (float)src[i], x2 = (float)src[i + half];
-  dst[i] = (__bf16)(x1 * c - x2 * s);
-  dst[i + half] = (__bf16)(x2 * c + x1 * s);
-}
-
-// q_pe[b, t, h, :] = rope(q[b, t, h, dn:], L_b + depth[b, t]); one thread per
-// (row, head, pair)
-__global__ __launch_bounds__(256) void rope_q_kernel(RowSrc q, int dn, int P, int H, int M,
-                                                     const int32_t* __restrict__ prefix_lens,
-                                                     const int32_t* __restrict__ depth, double log2_theta,
-                                                     __bf16* __restrict__ q_pe) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int half = P / 2;
-  if (gid >= (int64_t)M * H * half) return;
-  const int i = (int)(gid % half);
-  const int64_t mh = gid / half;
-  const int h = (int)(mh % H), m = (int)(mh / H);
-  const int b = m / q.T;
-  float c, s;
-  rope_angle(P, i, (double)prefix_lens[b] + (double)depth[m], log2_theta, c, s);
-  rope_apply(q.row(m, h) + dn, q_pe + ((int64_t)m * H + h) * P, half, i, c, s);
+  if (rope.q_pe) {
+    const int half = rope.P / 2, ny = gridDim.y;
+    const int i0 = (int)blockIdx.y * half / ny, np = ((int)blockIdx.y + 1) * half / ny - i0;
+    const int m0 = (int)blockIdx.z * kAbsorbRowBlocks * 32, m1 = min(M, m0 + kAbsorbRowBlocks * 32);
+    for (int e = threadIdx.x; e < (m1 - m0) * np; e += 256) {
+      const int m = m0 + e / np, i = i0 + e % np;
+      float c, s;
+      rope_angle(rope.P, i, (double)rope.prefix_lens[m / x.T] + (double)rope.depth[m], rope.log2_theta, c, s);
+      rope_apply(x.row(m, h) + rope.dn, rope.q_pe + ((int64_t)m * H + h) * rope.P, half, i, c, s);
+    }
+  }
 }
 
 // cache row L_b + t <- [c_kv_new[b, t] | rope(k_rope_new[b, t], L_b + depth[b, t])]
@@ -158,25 +165,27 @@ __global__ __launch_bounds__(256) void append_kernel(const __bf16* __restrict__ 
 }
 
 template <int KS, int NCB>
-static int launch_gemm(const RowSrc& x, const __bf16* w, int M, int H, int N, __bf16* out, hipStream_t s) {
+static int launch_gemm(const RowSrc& x, const __bf16* w, int M, int H, int N, __bf16* out, const RopeArgs& rope,
+                       hipStream_t s) {
   if (N % (32 * NCB)) return KDT_ERR_UNSUPPORTED;
   const int groups = ((M + 31) / 32 + kAbsorbRowBlocks - 1) / kAbsorbRowBlocks;
   if (groups > 65535) return KDT_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((absorb_gemm_kernel<KS, NCB>), dim3(H, N / (32 * NCB), groups), dim3(256), 0, s, x, w, M, H,
-                     N, out);
+                     N, out, rope);
   return launch_status();
 }
 
 // dispatch on the contraction length: the weight fragments of a workgroup
 // (NCB x KS x 4 registers) stay within 64 registers where possible, so that
 // two waves fit on a SIMD
-static int gemm(const RowSrc& x, const __bf16* w, int K, int M, int H, int N, __bf16* out, hipStream_t s) {
+static int gemm(const RowSrc& x, const __bf16* w, int K, int M, int H, int N, __bf16* out, const RopeArgs& rope,
+                hipStream_t s) {
   switch (K) {
-    case 32: return launch_gemm<2, 2>(x, w, M, H, N, out, s);
-    case 64: return launch_gemm<4, 2>(x, w, M, H, N, out, s);
-    case 128: return launch_gemm<8, 2>(x, w, M, H, N, out, s);
-    case 256: return launch_gemm<16, 1>(x, w, M, H, N, out, s);
-    case 512: return launch_gemm<32, 1>(x, w, M, H, N, out, s);
+    case 32: return launch_gemm<2, 2>(x, w, M, H, N, out, rope, s);
+    case 64: return launch_gemm<4, 2>(x, w, M, H, N, out, rope, s);
+    case 128: return launch_gemm<8, 2>(x, w, M, H, N, out, rope, s);
+    case 256: return launch_gemm<16, 1>(x, w, M, H, N, out, rope, s);
+    case 512: return launch_gemm<32, 1>(x, w, M, H, N, out, rope, s);
     default: return KDT_ERR_UNSUPPORTED;
   }
 }
@@ -198,12 +207,9 @@ extern "C" int kdt_absorb_q(int32_t dtype, int32_t B, int32_t T, int32_t H, int3
   hipStream_t s = static_cast<hipStream_t>(stream);
   const kdt::RowSrc x{static_cast<const __bf16*>(q), q_sb, q_st, q_sh, T};
   const int M = B * T;
-  int rc = kdt::gemm(x, static_cast<const __bf16*>(w_kc_t), dn, M, H, R, static_cast<__bf16*>(q_lat), s);
-  if (rc != KDT_OK) return rc;
-  const int64_t pairs = (int64_t)M * H * (P / 2);
-  hipLaunchKernelGGL(kdt::rope_q_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, x, (int)dn, (int)P,
-                     (int)H, M, prefix_lens, depth, log2((double)rope_theta), static_cast<__bf16*>(q_pe));
-  return kdt::launch_status();
+  const kdt::RopeArgs rope{prefix_lens, depth, log2((double)rope_theta), static_cast<__bf16*>(q_pe), (int)dn,
+                           (int)P};
+  return kdt::gemm(x, static_cast<const __bf16*>(w_kc_t), dn, M, H, R, static_cast<__bf16*>(q_lat), rope, s);
 }
 
 extern "C" int kdt_absorb_o(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t R, int32_t dv,
@@ -215,7 +221,7 @@ extern "C" int kdt_absorb_o(int32_t dtype, int32_t B, int32_t T, int32_t H, int3
   if ((int64_t)B * T > 0x7FFFFFFF / 64) return KDT_ERR_UNSUPPORTED;
   const kdt::RowSrc x{static_cast<const __bf16*>(o_lat), (int64_t)T * H * R, (int64_t)H * R, R, T};
   return kdt::gemm(x, static_cast<const __bf16*>(w_vc), R, B * T, H, dv, static_cast<__bf16*>(o),
-                   static_cast<hipStream_t>(stream));
+                   kdt::RopeArgs{nullptr, nullptr, 0.0, nullptr, 0, 0}, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int kdt_append_tree_kv(int32_t dtype, int32_t B, int32_t T, int32_t R, int32_t P, const void* c_kv_new,
