@@ -125,9 +125,17 @@ int kdt_build_visibility(const int32_t* parents, int32_t B, int32_t q_len,
  * q_len > capacity is skipped (out rows zero, lse = -inf) and flagged
  * KDT_SEQ_BAD_LEN.
  *
- * Split-prefix execution.  The key range of each sequence is cut into splits of
- * `split_keys` keys (0 = the library's choice; otherwise a multiple of 32, the
- * key tile).  split_keys cache rows of either region (c_kv_ss or k_pe_ss
+ * Split-prefix execution.  The key range of each sequence is cut into splits.
+ * With `split_keys` a multiple of 32 (the key tile) every split has split_keys
+ * keys.  With 0 (the library's choice) the splits are adaptive: the plan
+ * chooses max_splits splits for the longest sequence the launch allows
+ * (tiles_max = ceil((max_prefix_len + q_len) / 32) key tiles), and a sequence of
+ * T = ceil((prefix_lens[b] + q_len) / 32) tiles gets w = ceil(T * max_splits /
+ * tiles_max) splits' worth of tiles, tps = ceil(T / w) tiles per split, split s
+ * covering tiles [s * tps, min(T, (s + 1) * tps)) (ceil(T / tps) splits), so
+ * that short and long sequences alike give every split workgroup about the
+ * same work; total_prefix_len lets the plan count the workgroups that really
+ * have work.  split_keys cache rows of either region (c_kv_ss or k_pe_ss
  * elements apart) must span less than 2^31 bytes, or the call returns
  * KDT_ERR_UNSUPPORTED; the library's choice stays within that.
  * Each split produces a normalised partial output and its log-sum-exp in the
@@ -181,6 +189,8 @@ typedef struct {
   int32_t merge_wait_us;               /* longest wait of a split workgroup for the rest of its row tile
                                           (0 = the default, 2000; < 0 = no wait, the last one out merges
                                           whatever was left: for tests of that path) */
+  int64_t total_prefix_len;            /* host hint, sum of prefix_lens[] (0 = unknown: taken as
+                                          B * max_prefix_len); only the plan depends on it */
 } kdt_verify_desc;
 
 /* Host-only planning: no device memory is touched (the compute-unit count of
@@ -198,7 +208,10 @@ typedef struct {
  * unspecified values.  part_dtype is KDT_F32 for float32 inputs or when
  * partials_f32 is set, else KDT_BF16 (rounded to nearest even: one more
  * rounding of the output's own precision, which halves the partial traffic).
- * Sequence b uses splits 0 .. ceil((prefix_lens[b] + q_len) / split_keys) - 1.
+ * Sequence b uses splits 0 .. n_b - 1, n_b = ceil((prefix_lens[b] + q_len) /
+ * split_keys) for fixed splits (tiles_max == 0), or the adaptive count above;
+ * the part_lse rows of its other splits are written -inf by kdt_verify_partials
+ * (so a merge over all max_splits splits is always right).
  * Merge state (when the merge is fused): one 32-bit word per row tile, uint32
  * [B, NRT] at counter_offset, NRT = ceil(q_len*H / rows per workgroup of the
  * layout): two counts and a generation bit.  The words must be zero before
@@ -218,7 +231,7 @@ typedef struct {
   size_t workspace_bytes;      /* what kdt_verify_attn needs: 0 when direct, else partials and counters */
   size_t partials_bytes;       /* what kdt_verify_partials needs (part_o and part_lse; also when direct) */
   int32_t fused_merge;         /* 1: kdt_verify_attn merges inside the split kernel (one launch) */
-  int32_t reserved;
+  int32_t tiles_max;           /* > 0: adaptive splits (above), the longest sequence's key tiles; 0: fixed */
   int64_t counter_offset;      /* bytes into the workspace of the merge counters */
 } kdt_verify_plan;
 
@@ -255,7 +268,8 @@ int kdt_verify_attn_noalloc(const kdt_verify_desc* d, void* stream);
  *   lse[b,m] = ln sum_k exp(part_lse[b,k,m]);
  *   out[b,m,:] = sum_k exp(part_lse[b,k,m] - lse[b,m]) * part_o[b,k,m,:]
  * over k < n_splits, where n_splits = max_splits when split_keys == 0, else
- * ceil((prefix_lens[b] + q_len) / split_keys) clamped to [1, max_splits].
+ * ceil((prefix_lens[b] + q_len) / split_keys) clamped to [1, max_splits]
+ * (partials of adaptive splits: merge with split_keys == 0).
  * Splits with part_lse = -inf carry no weight; a row with no finite split gets
  * out = 0 and lse = -inf.  out is written in `dtype` (bf16: round to nearest
  * even).  part_o (elements of `part_dtype`, KDT_F32 or KDT_BF16) and part_lse

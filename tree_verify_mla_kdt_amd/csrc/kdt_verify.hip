@@ -63,6 +63,7 @@
 //   their shared K/V stream in that XCD's L2.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -139,6 +140,11 @@ struct VerifyArgs {
   int32_t* seq_status;
   float scale_log2;
   int B, q, H, M, W, n_rt, n_blk, max_splits, split_keys, max_prefix_len, layout;
+  // 0: fixed splits of split_keys keys; > 0: adaptive splits, this being the
+  // key tiles of the longest sequence the launch allows (see split_range)
+  int tiles_max;
+  int group_mul;        // order of the (sequence, split) groups (coprime to B * max_splits)
+  int compact;          // number the pieces with work (adaptive splits over several sequences)
   int q_rows_uniform;   // query rows m = t * H + h sit at one byte stride (q_lat and q_pe)
   int part_bf16;        // partial outputs in bf16 (else float32)
   // Merge inside the split kernel (partial mode only): the split workgroups
@@ -398,7 +404,8 @@ struct PartLoad<__bf16> {
 // WIDE: the four waves of the workgroup share the item, wave w loading the
 // w-th quarter of the splits at once, and wave 0 combines the four (max, sum,
 // columns) states through s_st (4 * (NV + 2) * 64 floats of LDS); every wave
-// of the workgroup must then call it with the same item.  COH: the partials
+// of the workgroup must then call it with the same item.  Splits at or past
+// ns are skipped.  COH: the partials
 // were stored by other workgroups of the running launch and are read with
 // device-coherent loads.
 template <typename T, typename PT, bool WIDE, bool COH>
@@ -414,7 +421,9 @@ __device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const 
   const int hh = lane >> 5;
   const int m = blk * 32 + (lane & 31);
   const bool row_ok = m < M;
-  const int per = WIDE ? (ns + 3) / 4 : ns;
+  // (WIDE: the quarters are of max_splits, so the grouping of the sums, and
+  // so the result, does not depend on how many splits the sequence uses)
+  const int per = WIDE ? (max_splits + 3) / 4 : ns;
   const int kb = WIDE ? wave * per : 0;
   const int ke = row_ok ? min(ns, kb + per) : kb;   // padding rows load nothing
   const float* pl = part_lse + (int64_t)b * max_splits * M + (row_ok ? m : 0);
@@ -503,13 +512,35 @@ __device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const 
   }
 }
 
-// Number of splits sequence b uses: ceil((L + q) / split_keys) in [1, max_splits]
-// (max_splits when split_keys is 0).
-// (n_keys >= 1 and below 2^32 + 1: 32-bit arithmetic, no overflow)
-__device__ __forceinline__ int splits_of(int64_t n_keys, int split_keys, int max_splits) {
-  if (split_keys <= 0 || n_keys <= 0) return max_splits > 0 && n_keys <= 0 ? 1 : max_splits;
-  const uint32_t ns = (uint32_t)(n_keys - 1) / (uint32_t)split_keys + 1u;
-  return ns > (uint32_t)max_splits ? max_splits : (int)ns;
+// The splits of a sequence of n_keys = L + q keys (1 <= n_keys < 2^31):
+//  * fixed (tiles_max == 0): splits of split_keys keys; split s covers keys
+//    [s split_keys, min(n_keys, (s + 1) split_keys)), ns = ceil(n_keys / split_keys);
+//  * adaptive (tiles_max > 0, the key tiles of the longest sequence the launch
+//    allows, whose max_splits splits have split_keys keys or fewer): a
+//    sequence of T = ceil(n_keys / 32) tiles gets ceil(T max_splits / tiles_max)
+//    splits' worth of tiles, tps = ceil(T / that) per split, so every split of
+//    every sequence holds about as many tiles as one of the longest sequence;
+//    split s covers tiles [s tps, min(T, (s + 1) tps)), ns = ceil(T / tps).
+// Splits at or past ns are empty (k_begin >= n_keys).
+struct SplitRange {
+  int k_begin, k_end, ns;
+};
+__device__ __forceinline__ SplitRange split_range(int n_keys, int split, int split_keys, int max_splits,
+                                                  int tiles_max) {
+  SplitRange r;
+  if (tiles_max <= 0) {
+    r.ns = (int)min((uint32_t)max_splits, (uint32_t)(n_keys - 1) / (uint32_t)split_keys + 1u);
+    r.k_begin = split * split_keys;
+    r.k_end = min(n_keys, r.k_begin + split_keys);
+  } else {
+    const uint32_t T = (uint32_t)(n_keys - 1) / kBN + 1u;
+    const uint32_t want = (uint32_t)(((uint64_t)T * (uint64_t)max_splits + tiles_max - 1) / (uint64_t)tiles_max);
+    const uint32_t tps = (T - 1) / max(want, 1u) + 1u;
+    r.ns = (int)((T - 1) / tps + 1u);
+    r.k_begin = (int)min((uint32_t)split * tps, T) * kBN;
+    r.k_end = min(n_keys, (int)(min((uint32_t)(split + 1) * tps, T) * kBN));
+  }
+  return r;
 }
 
 template <typename T, typename PT, int R>
@@ -533,6 +564,62 @@ __device__ __forceinline__ void merge_share(const VerifyArgs& a, int b, int rt, 
       merge_item<T, PT, false, true>(po, a.part_lse, a.max_splits, ns, a.M, a.H, R, a.n_blk, b, blk0 + i / n_cg,
                                      i % n_cg, out, a.out_sb, a.out_st, a.out_sh, a.lse, s_st, wave, lane);
   }
+}
+
+// Work compaction (adaptive splits over several sequences): the (sequence,
+// split, row tile) pieces with work are numbered in that order, and
+// workgroup i < W (W pieces in all) takes piece xcd_remap(i, W): the working
+// workgroups are spread evenly over the XCDs, and the row tiles of one split
+// stay together on one XCD (they read the same keys); workgroups i >= W have
+// none.  A sequence with an invalid prefix length counts one split (its
+// workgroups flag it and write the empty result).  Each wave works it out
+// from the prefix lengths itself, 64 sequences per pass.
+struct Piece {
+  int b, split, rt, L;
+  bool work;
+};
+__device__ __forceinline__ int pieces_of(const VerifyArgs& a, int L) {
+  const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
+  return a.n_rt * (bad ? 1 : split_range(L + a.q, 0, a.split_keys, a.max_splits, a.tiles_max).ns);
+}
+__device__ __forceinline__ Piece compact_piece(const VerifyArgs& a, int lane) {
+  Piece pc{0, 0, 0, 0, false};
+  int total = 0;
+  for (int j0 = 0; j0 < a.B; j0 += 64) {
+    const int j = j0 + lane;
+    int c = j < a.B ? pieces_of(a, a.prefix_lens[j]) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+    total += c;
+  }
+  const int i = blockIdx.x;
+  if (i >= total) return pc;
+  const int p = xcd_remap(i, total);
+  int base = 0;
+  for (int j0 = 0; j0 < a.B; j0 += 64) {
+    const int j = j0 + lane;
+    const int L = j < a.B ? a.prefix_lens[j] : 0;
+    const int c = j < a.B ? pieces_of(a, L) : 0;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const uint64_t past = __ballot(base + incl > p);
+    if (past) {
+      const int k = __builtin_ctzll(past);
+      const int rem = p - (base + __shfl(incl, k) - __shfl(c, k));
+      pc.b = j0 + k;
+      pc.L = __shfl(L, k);
+      pc.split = rem / a.n_rt;
+      pc.rt = rem - pc.split * a.n_rt;
+      pc.work = true;
+      return pc;
+    }
+    base += __shfl(incl, 63);
+  }
+  return pc;
 }
 
 // The merge of one row tile's partials inside the split kernel.  The split
@@ -682,13 +769,29 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // depth split: each wave's partial score tile, 16 floats per lane
   __shared__ __attribute__((aligned(16))) f32x4 s_sx[DS ? 4 * kThreads : 1];
 
-  const int u = xcd_remap(blockIdx.x, gridDim.x);
-  const int rt = u % a.n_rt;
-  const int split = (u / a.n_rt) % a.max_splits;
-  const int b = u / (a.n_rt * a.max_splits);
-
+  // Logical work unit u: the row tiles of one (sequence, split) group are
+  // consecutive (they read the same keys, and xcd_remap keeps consecutive
+  // units on one XCD, sharing its L2); the groups are visited in the order
+  // g = g' * group_mul mod (B * max_splits), group_mul coprime to the group
+  // count, so that each XCD's block of units mixes sequences and splits
+  // (with adaptive splits a short sequence's high splits have no work).
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  int rt, split, b, L_known = 0;
+  if (a.compact) {
+    const Piece pc = compact_piece(a, lane);
+    if (!pc.work) return;
+    rt = __builtin_amdgcn_readfirstlane(pc.rt);
+    split = __builtin_amdgcn_readfirstlane(pc.split);
+    b = __builtin_amdgcn_readfirstlane(pc.b);
+    L_known = __builtin_amdgcn_readfirstlane(pc.L);
+  } else {
+    const int u = xcd_remap(blockIdx.x, gridDim.x);
+    rt = u % a.n_rt;
+    const int g = (int)((int64_t)(u / a.n_rt) * a.group_mul % ((int64_t)a.B * a.max_splits));
+    split = g % a.max_splits;
+    b = g / a.max_splits;
+  }
   const int r = lane & 31, hh = lane >> 5;
   // row block, output column half (and depth half), key stream
   const int rb = KS ? (wave >> 1) : wave / CSC, chalf = KS ? 0 : wave % CSC, kp = KS ? (wave & 1) : 0;
@@ -702,7 +805,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // the key stream starts at once, then the query fragments and visibility
   // words, then the prefix length (a scalar load: the index is uniform, so
   // waiting for it waits for no vector load).  All four latencies overlap.
-  const int k_begin = split * a.split_keys;
+  // the split's first key as for a sequence of the longest length the
+  // launch allows (right for it and for every split of fixed size; the
+  // speculative copies below use it)
+  const bool L_bad_known = a.compact && (L_known < 0 || L_known > a.max_prefix_len ||
+                                         (int64_t)L_known + a.q > a.capacity);
+  const int k_spec = a.compact ? (L_bad_known ? 0
+                                              : split_range(L_known + a.q, split, a.split_keys, a.max_splits,
+                                                            a.tiles_max).k_begin)
+                               : split * a.split_keys;
+  int k_begin = k_spec;
   const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
   const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
   const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
@@ -711,9 +823,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // copy only adds its row offset.  It spans the split's rows below the cache
   // capacity (the host keeps split_keys rows of either region under 2^31
   // bytes); every row a copy reads is one of them.
-  const int64_t span = max((int64_t)0, min((int64_t)a.split_keys, a.capacity - (int64_t)k_begin));
-  const i32x4 rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span * lat_ss));
-  const i32x4 rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span * pe_ss));
+  auto span_of = [&](int kb) {
+    return max((int64_t)0, min((int64_t)a.split_keys, a.capacity - (int64_t)kb));
+  };
+  i32x4 rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
+  i32x4 rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
   // Copy of key tile `tile` (first key k_begin + tile * kBN) into the tile
   // buffer at LDS address lds, with its first `nrows` rows real; later rows
   // repeat row nrows - 1.
@@ -796,10 +910,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     vw0 = vr[0];
     vw1 = a.W > 1 ? vr[1] : 0ull;
   }
-  const int L = ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
+  const int L = a.compact ? L_known : ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
 
   const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
   const int N = L + a.q;
+  const SplitRange sr = split_range(bad ? 1 : N, split, a.split_keys, a.max_splits, a.tiles_max);
+  k_begin = sr.k_begin;
 
   if (bad || k_begin >= N) wait_vmem_lds<0>();   // no copy may outlive the workgroup
   if (bad) {
@@ -811,15 +927,34 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
         for (int d = 0; d < R; ++d) o[d] = (T)0.0f;
       } else {
-        a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = -INFINITY;
+        // (compaction gives a skipped sequence one split: it writes them all)
+        for (int k = split; k < (a.compact ? a.max_splits : split + 1); ++k)
+          a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
       }
     }
     return;
   }
-  if (k_begin >= N) return;                   // this split does not exist for sequence b
-  const int k_end = min(N, k_begin + a.split_keys);
+  if (!DIRECT && a.compact && !a.fuse && split == 0 && row_ok && hh == 0 && chalf == 0 && kp == 0) {
+    // compaction runs no workgroup for the splits this sequence does not
+    // use: their partials are marked empty here
+    for (int k = sr.ns; k < a.max_splits; ++k) a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
+  }
+  if (k_begin >= N) {
+    // this split does not exist for sequence b: an empty partial, so that a
+    // merge over all max_splits splits is always right
+    if (!DIRECT && !a.fuse && row_ok && hh == 0 && chalf == 0 && kp == 0)
+      a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = -INFINITY;
+    return;
+  }
+  const int k_end = sr.k_end;
   const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
-  const bool spec_ok = spec && k_begin + 2 * kBN <= k_end;
+  const bool spec_ok = spec && k_begin == k_spec && k_begin + 2 * kBN <= k_end;
+  if (k_begin != k_spec) {
+    // (adaptive splits of a shorter sequence: the speculative copies read
+    // other rows, and are waited for and replaced below)
+    rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
+    rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
+  }
 
   auto stage = [&](int tile, uint32_t lds) { stage_rows(tile, lds, min(kBN, k_end - (k_begin + tile * kBN))); };
   // The same copy, one wave-load at a time (pieces 0 .. NPIECE - 1), so that
@@ -1285,7 +1420,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   };
   // a sequence with one split needs no merge: the fused launch writes its
   // output directly too
-  const int ns_b = splits_of((int64_t)N, a.split_keys, a.max_splits);
+  const int ns_b = sr.ns;
   const bool direct_now = DIRECT || (a.fuse && ns_b == 1);
   if (direct_now) {
     if (row_ok) {
@@ -1363,7 +1498,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
 template <typename T, typename PT, bool WIDE>
 __global__ __launch_bounds__(256) void merge_kernel(
     const PT* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
-    int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys,
+    int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys, int tiles_max,
     T* __restrict__ out, int64_t out_sb, int64_t out_st, int64_t out_sh, float* __restrict__ lse) {
   constexpr int NV = PartLoad<PT>::NV;
   __shared__ float s_st[WIDE ? 4 * (NV + 2) * 64 : 1];
@@ -1376,7 +1511,12 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int64_t bblk = wid / n_cg;
   const int blk = (int)(bblk % n_blk), b = (int)(bblk / n_blk);
   const int M = q * H;
-  const int ns = split_keys > 0 ? splits_of((int64_t)prefix_lens[b] + q, split_keys, max_splits) : max_splits;
+  int ns = max_splits;
+  if (split_keys > 0) {
+    const int L = prefix_lens[b];
+    // (a skipped sequence wrote empty partials: any count is right)
+    ns = L >= 0 && L <= 0x7FFFFFFF - q ? split_range(L + q, 0, split_keys, max_splits, tiles_max).ns : max_splits;
+  }
   merge_item<T, PT, WIDE, false>(part_o, part_lse, max_splits, ns, M, H, R, n_blk, b, blk, cg, out, out_sb, out_st,
                                  out_sh, lse, s_st, wave, lane);
 }
@@ -1457,8 +1597,19 @@ static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 // about 1.7 us, a start-up about 4 us, a 128-row float32 partial about 0.15 us)
 // and scale with the contraction work of one wave and with the bytes a
 // partial holds.
-static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R, int P, int layout,
-                          int part_bytes) {
+// Modelled time (microseconds) of one launch, split kernel plus merge, for a
+// layout, split size and count: `wgs` split workgroups with work (one per
+// compute unit, so ceil(wgs / kCU) rounds) of at most `tiles` key tiles each;
+// a round costs its tiles plus a start-up (the burst of query and first-tile
+// loads), every partial costs its write and its read in the merge, and
+// splitting at all adds the merge launch plus one memory round trip per
+// batch of splits the merge loads at once (sixteen per wave; up to sixty-four
+// when a workgroup's four waves share the splits of one item).  The constants
+// are fitted to a measured grid of split sizes and layouts over six workloads
+// at R = 512, P = 64 (a 128-row tile of 32 keys about 1.7 us, a start-up about
+// 4 us, a 128-row float32 partial about 0.15 us) and scale with the
+// contraction work of one wave and with the bytes a partial holds.
+static double launch_cost(int64_t wgs, int64_t splits, int64_t tiles, int R, int P, int layout, int part_bytes) {
   const int rows = layout_rows(layout);
   // layout 4: two key tiles per step, each wave doing layout 1's work for its
   // tile in about 1.1 times layout 1's tile time, plus about 2 us to combine
@@ -1467,13 +1618,12 @@ static double launch_cost(int64_t n_seq_tiles, int64_t n_max, int64_t sk, int R,
   const double t_start = layout == 4 ? 6.0 : 4.0;
   const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 3.0, t_merge_batch = 2.0;
-  const int64_t ns = (n_max + sk - 1) / sk;
-  const int64_t rounds = (ns * n_seq_tiles + kCU - 1) / kCU;
-  const int64_t batches = ns > 16 ? (ns + 63) / 64 : 1;
-  const double merge = ns > 1 ? ns * n_seq_tiles * t_part + t_merge + t_merge_batch * (double)batches : 0.0;
+  const int64_t rounds = (wgs + kCU - 1) / kCU;
+  const int64_t batches = splits > 16 ? (splits + 63) / 64 : 1;
+  const double merge = splits > 1 ? wgs * t_part + t_merge + t_merge_batch * (double)batches : 0.0;
   // (layout 4 works in steps of two tiles: an odd tile count wastes half a step)
-  const int64_t tiles = layout == 4 ? (sk / kBN + 1) / 2 * 2 : sk / kBN;
-  return rounds * (tiles * t_tile + t_start) + merge;
+  const int64_t t = layout == 4 ? (tiles + 1) / 2 * 2 : tiles;
+  return rounds * (t * t_tile + t_start) + merge;
 }
 
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
@@ -1481,27 +1631,46 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   if (rc != KDT_OK) return rc;
   const int M = d->q_len * d->H;
   const int64_t n_max = (int64_t)d->max_prefix_len + d->q_len;
+  const int64_t tiles_max = (n_max + kBN - 1) / kBN;
   const int part_dtype = (d->dtype == KDT_BF16 && !d->partials_f32) ? KDT_BF16 : KDT_F32;
   // The split kernel addresses a split's cache rows by 32-bit byte offsets
   // from its first row: split_keys rows of either region stay under 2^31 bytes.
   const int64_t row_bytes = (d->c_kv_ss > d->k_pe_ss ? d->c_kv_ss : d->k_pe_ss) * elem_size(d->dtype);
   const int64_t max_sk = row_bytes > 0 ? 0x7FFFFFFF / row_bytes / kBN * kBN : (int64_t)1 << 40;
   if (max_sk < kBN || d->split_keys > max_sk) return KDT_ERR_UNSUPPORTED;
-  // candidate layouts: the requested one, or both; candidate split sizes:
-  // the requested one, or every distinct split count up to 4096
+  // Key tiles of all sequences together: from the caller's hint (the sum of
+  // the prefix lengths), else as if every sequence had the longest length.
+  const int64_t total_keys = d->total_prefix_len > 0 ? d->total_prefix_len + (int64_t)d->B * d->q_len
+                                                     : (int64_t)d->B * n_max;
+  const int64_t total_tiles = (total_keys + kBN - 1) / kBN + d->B / 2;
+  // With the library's choice of split size the splits are adaptive: every
+  // sequence is cut into splits of about the same number of tiles as the
+  // longest one's (split_range), so the split workgroups with work number
+  // about s * total_tiles / tiles_max (each sequence rounding up), not B * s.
+  const bool adaptive = d->split_keys == 0;
   int best_layout = d->layout ? d->layout : 1;
   int64_t sk = d->split_keys;
   double best = 1e300;
   const bool wide_ok = wide_layout_supported(d->dtype, d->R, d->P);
   for (int layout = 1; layout <= 4; ++layout) {
     if (d->layout ? layout != d->layout : (layout == 3 || (layout == 4 && !wide_ok))) continue;
-    const int64_t n_seq_tiles = (int64_t)d->B * ((M + layout_rows(layout) - 1) / layout_rows(layout));
-    const int64_t n_tiles = (n_max + kBN - 1) / kBN;
-    for (int64_t s = 1; s <= n_tiles && s <= 4096; ++s) {
-      int64_t k = d->split_keys ? d->split_keys : ((n_max + s - 1) / s + kBN - 1) / kBN * kBN;
-      if (!d->split_keys && (n_max + k - 1) / k != s) continue;   // covered by a smaller s
+    const int64_t n_rt = (M + layout_rows(layout) - 1) / layout_rows(layout);
+    for (int64_t s = 1; s <= tiles_max && s <= 4096; ++s) {
+      int64_t k;
+      if (d->split_keys) {
+        k = d->split_keys;
+      } else {
+        const int64_t tps = (tiles_max + s - 1) / s;
+        if ((tiles_max + tps - 1) / tps != s) continue;      // covered by a smaller s
+        k = tps * kBN;
+      }
       if (k > max_sk) continue;
-      const double c = launch_cost(n_seq_tiles, n_max, k, d->R, d->P, layout, elem_size(part_dtype));
+      const int64_t ns = (n_max + k - 1) / k;
+      // (each sequence rounds its own split count up: half a split on average)
+      const int64_t per_seq = adaptive ? (ns * total_tiles + tiles_max - 1) / tiles_max + (d->B + 1) / 2
+                                       : (total_keys + k - 1) / k + (d->B + 1) / 2;
+      const int64_t wgs = n_rt * std::min((int64_t)d->B * ns, std::max<int64_t>(per_seq, 1));
+      const double c = launch_cost(wgs, ns, k / kBN, d->R, d->P, layout, elem_size(part_dtype));
       if (c < best * 0.999) {                 // ties go to fewer splits, then layout 1
         best = c;
         sk = k;
@@ -1517,6 +1686,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
   p->max_splits = (int32_t)ns;
+  p->tiles_max = adaptive && ns > 1 ? (int32_t)tiles_max : 0;
   p->rows = M;
   p->direct = ns == 1 ? 1 : 0;
   const int64_t n_part_rows = (int64_t)d->B * ns * M;
@@ -1532,6 +1702,24 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   p->counter_offset = ((int64_t)p->partials_bytes + 255) / 256 * 256;
   p->workspace_bytes = p->direct ? 0 : (size_t)(p->counter_offset + (int64_t)d->B * n_rt * 4);
   return KDT_OK;
+}
+
+// A stride near 0.618 of n (the golden ratio spreads the multiples evenly)
+// that is coprime to n, so g -> g * stride mod n is a permutation of 0 .. n-1.
+static int group_stride(int64_t n) {
+  if (n <= 2) return 1;
+  int64_t m = (int64_t)((double)n * 0.6180339887498949);
+  if (m < 1) m = 1;
+  auto gcd = [](int64_t x, int64_t y) {
+    while (y) {
+      const int64_t t = x % y;
+      x = y;
+      y = t;
+    }
+    return x;
+  };
+  while (gcd(m, n) != 1) ++m;
+  return (int)m;
 }
 
 static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, void* ws, bool fuse) {
@@ -1561,6 +1749,9 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.n_blk = (a.M + 31) / 32;
   a.max_splits = p.max_splits;
   a.split_keys = p.split_keys;
+  a.tiles_max = p.tiles_max;
+  a.group_mul = group_stride((int64_t)d->B * p.max_splits);
+  a.compact = p.tiles_max > 0 && d->B > 1;
   a.max_prefix_len = d->max_prefix_len;
   const int64_t es = elem_size(d->dtype);
   a.q_rows_uniform = d->q_lat_st == (int64_t)d->H * d->q_lat_sh && d->q_pe_st == (int64_t)d->H * d->q_pe_sh &&
@@ -1609,8 +1800,8 @@ static int dispatch_split(int dtype, int R, int P, const VerifyArgs& a, bool dir
 
 template <typename PT>
 static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, const float* pl, int max_splits,
-                          const int32_t* prefix_lens, int split_keys, void* out, int64_t osb, int64_t ost,
-                          int64_t osh, float* lse, hipStream_t s) {
+                          const int32_t* prefix_lens, int split_keys, int tiles_max, void* out, int64_t osb,
+                          int64_t ost, int64_t osh, float* lse, hipStream_t s) {
   const int n_blk = (q * H + 31) / 32;
   const int64_t items = (int64_t)B * n_blk * (R / (2 * PartLoad<PT>::NV));
   // more splits than one wave loads in one round trip: a workgroup per item
@@ -1619,7 +1810,7 @@ static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, c
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
 #define KDT_MERGE_LAUNCH(TO, W)                                                                              \
   hipLaunchKernelGGL((merge_kernel<TO, PT, W>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, \
-                     H, R, n_blk, prefix_lens, split_keys, static_cast<TO*>(out), osb, ost, osh, lse)
+                     H, R, n_blk, prefix_lens, split_keys, tiles_max, static_cast<TO*>(out), osb, ost, osh, lse)
   if (dtype == KDT_BF16) {
     if (wide) KDT_MERGE_LAUNCH(__bf16, true);
     else KDT_MERGE_LAUNCH(__bf16, false);
@@ -1632,13 +1823,13 @@ static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, c
 }
 
 static int launch_merge(int dtype, int B, int q, int H, int R, int part_dtype, const void* po, const float* pl,
-                        int max_splits, const int32_t* prefix_lens, int split_keys, void* out,
+                        int max_splits, const int32_t* prefix_lens, int split_keys, int tiles_max, void* out,
                         int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
   if (part_dtype == KDT_BF16)
     return launch_merge_t(dtype, B, q, H, R, static_cast<const __bf16*>(po), pl, max_splits, prefix_lens,
-                          split_keys, out, osb, ost, osh, lse, s);
+                          split_keys, tiles_max, out, osb, ost, osh, lse, s);
   return launch_merge_t(dtype, B, q, H, R, static_cast<const float*>(po), pl, max_splits, prefix_lens, split_keys,
-                        out, osb, ost, osh, lse, s);
+                        tiles_max, out, osb, ost, osh, lse, s);
 }
 
 // The verify with a given workspace (NULL when the plan is direct).
@@ -1647,7 +1838,7 @@ static int verify_run(const kdt_verify_desc* d, const kdt_verify_plan& p, void* 
   int r = dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
   if (r != KDT_OK || p.direct || p.fused_merge) return r;
   return launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, p.part_dtype, a.part_o, a.part_lse, p.max_splits,
-                      d->prefix_lens, p.split_keys, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
+                      d->prefix_lens, p.split_keys, p.tiles_max, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
 }
 
 // Workspace of kdt_verify_attn_noalloc: a fixed device array, one per GPU
@@ -1730,6 +1921,6 @@ extern "C" int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32
   if (!kdt::aligned16(part_o) || !kdt::aligned16(out) || (R % vec) || out_sb % vec || out_st % vec ||
       out_sh % vec || out_sb < 0 || out_st < 0 || out_sh < 0)
     return KDT_ERR_UNSUPPORTED;
-  return kdt::launch_merge(dtype, B, q_len, H, R, part_dtype, part_o, part_lse, max_splits, prefix_lens, split_keys,
+  return kdt::launch_merge(dtype, B, q_len, H, R, part_dtype, part_o, part_lse, max_splits, prefix_lens, split_keys, 0,
                            out, out_sb, out_st, out_sh, lse, static_cast<hipStream_t>(stream));
 }
