@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--merge-mode", type=int, default=0,
                     help="0: separate merge kernel (the library's default), "
                          "1: merge inside the split kernel when the launch allows")
+    ap.add_argument("--schedule", type=int, default=0,
+                    help="0: the library's choice, 1: splits, 2: the balanced schedule")
+    ap.add_argument("--gang-size", type=int, default=0,
+                    help="balanced schedule: row tiles per gang (0: the library's choice)")
     ap.add_argument("--no-length-hint", action="store_true",
                     help="do not tell the planner the sum of the prefix lengths (it then sizes the launch as if "
                          "every sequence had the longest length)")
@@ -196,6 +200,7 @@ def main():
     max_prefix = int(inp.prefix_lens.max())
     # the host knows its sequences' lengths: their sum sizes the launch
     total_prefix = 0 if args.no_length_hint else int(inp.prefix_lens.astype(np.int64).sum())
+    sched = dict(schedule=args.schedule, gang_size=args.gang_size)
     W = (q + 63) // 64
     vis = torch.empty((B, q, W), dtype=torch.int64, device=dev)
     # masks: from kdt_build_visibility in the step, or derived by the split
@@ -210,7 +215,7 @@ def main():
     desc, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
                                      prefix_lens, vis_arg, cfg.softmax_scale, max_prefix, out, lse, None,
                                      args.split_keys, args.layout, args.partials_f32, par_arg, args.merge_mode,
-                                     total_prefix_len=total_prefix)
+                                     total_prefix_len=total_prefix, **sched)
     plan = kdt.verify_plan(desc)
     ws_bytes = max(int(plan.workspace_bytes), int(plan.partials_bytes))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)   # (merge counters start at zero)
@@ -222,7 +227,7 @@ def main():
         kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                         cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
                         split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
-                        parents=par_arg, merge_mode=args.merge_mode, total_prefix_len=total_prefix)
+                        parents=par_arg, merge_mode=args.merge_mode, total_prefix_len=total_prefix, **sched)
         kdt.gather_accepted(c["cache"], prefix_lens, accepted, n_acc, q, new_prefix_lens=new_pl)
 
     def split_only(i):
@@ -230,7 +235,7 @@ def main():
         kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                             cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws,
                             split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
-                            parents=par_arg, total_prefix_len=total_prefix)
+                            parents=par_arg, total_prefix_len=total_prefix, **sched)
 
     # Launches are replayed from HIP graphs: one graph runs the step once per
     # input copy, so host launch overhead stays out of the measured step time.
@@ -295,7 +300,8 @@ def main():
     if cfg.dtype == "bf16" and not args.partials_f32:
         d32, _, _ = kdt._verify_prepare(c0["q_lat"], c0["q_pe"], c0["cache"][..., :R], c0["cache"][..., R:],
                                         prefix_lens, vis_arg, cfg.softmax_scale, max_prefix, out, lse, None,
-                                        args.split_keys, args.layout, True, par_arg, total_prefix_len=total_prefix)
+                                        args.split_keys, args.layout, True, par_arg, total_prefix_len=total_prefix,
+                                        **sched)
         p32 = kdt.verify_plan(d32)
         ws32 = torch.zeros(max(int(p32.partials_bytes), int(p32.workspace_bytes)), dtype=torch.uint8, device=dev)
 
@@ -304,7 +310,7 @@ def main():
             kdt.verify_partials(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens,
                                 vis_arg, cfg.softmax_scale, max_prefix_len=max_prefix, workspace=ws32,
                                 split_keys=args.split_keys, layout=args.layout, partials_f32=True, parents=par_arg,
-                                total_prefix_len=total_prefix)
+                                total_prefix_len=total_prefix, **sched)
         g32 = capture(split_only32, range(n_copies))
         g32.replay()
         e0.record(cur)
@@ -324,7 +330,7 @@ def main():
             kdt.verify_attn(c["q_lat"], c["q_pe"], c["cache"][..., :R], c["cache"][..., R:], prefix_lens, vis_arg,
                             cfg.softmax_scale, max_prefix_len=max_prefix, out=out, lse=lse, workspace=ws,
                             split_keys=args.split_keys, layout=args.layout, partials_f32=args.partials_f32,
-                            parents=par_arg, merge_mode=args.merge_mode, total_prefix_len=total_prefix)
+                            parents=par_arg, merge_mode=args.merge_mode, total_prefix_len=total_prefix, **sched)
         if args.separate_visibility:
             kdt.build_visibility(parents, vis=vis, depth=depth)
         g_ver = capture(verify_only, range(n_copies))
@@ -451,6 +457,8 @@ def main():
                    "rope_dim": P, "q_len": q, "prefix_len_max": max_prefix,
                    "split_keys": plan.split_keys, "splits": plan.max_splits, "layout": plan.layout,
                    "adaptive_splits": bool(plan.tiles_max), "length_hint": total_prefix,
+                   "schedule": (f"balanced: {plan.gangs} gangs of {plan.gang_size} row tiles" if plan.gang_size
+                                else "splits"),
                    "partials": "bf16" if plan.part_dtype == kdt.KDT_BF16 else "f32",
                    "merge": "direct" if plan.direct else ("fused" if plan.fused_merge else "separate kernel"),
                    "step": ("build_visibility + verify (split + merge) + gather_accepted" if args.separate_visibility

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDT_ABI_VERSION 4
+#define KDT_ABI_VERSION 5
 #define KDT_MAX_Q_LEN 128           /* tree tokens per sequence (two 64-bit mask words) */
 
 typedef enum {
@@ -191,6 +191,9 @@ typedef struct {
                                           whatever was left: for tests of that path) */
   int64_t total_prefix_len;            /* host hint, sum of prefix_lens[] (0 = unknown: taken as
                                           B * max_prefix_len); only the plan depends on it */
+  int32_t schedule;                    /* 0 = the library's choice, 1 = splits (fixed or adaptive),
+                                          2 = the balanced schedule (below; split_keys must be 0) */
+  int32_t gang_size;                   /* balanced schedule: row tiles per gang (0 = the library's choice) */
 } kdt_verify_desc;
 
 /* Host-only planning: no device memory is touched (the compute-unit count of
@@ -209,9 +212,23 @@ typedef struct {
  * partials_f32 is set, else KDT_BF16 (rounded to nearest even: one more
  * rounding of the output's own precision, which halves the partial traffic).
  * Sequence b uses splits 0 .. n_b - 1, n_b = ceil((prefix_lens[b] + q_len) /
- * split_keys) for fixed splits (tiles_max == 0), or the adaptive count above;
+ * split_keys) for fixed splits (tiles_max == 0), the adaptive count above, or
+ * the count the balanced schedule gives each of its row-tile groups (below);
  * the part_lse rows of its other splits are written -inf by kdt_verify_partials
  * (so a merge over all max_splits splits is always right).
+ * Balanced schedule (gang_size > 0; stream-K style): the row tiles of a
+ * sequence form groups of gang_size consecutive tiles, and every (sequence,
+ * group) pair is a stream of ceil((prefix_lens[b] + q_len) / 32) key-tile
+ * units (one for a sequence with an invalid prefix length).  The streams, laid
+ * end to end in sequence order, U units in all, are cut into ranges of A =
+ * max(ceil(U / gangs), ceil(T_max / (max_splits - 1))) units (T_max the
+ * longest stream among valid sequences; A is at most the key tiles one piece
+ * may span); range j goes to gang j mod gangs, a gang being gang_size
+ * workgroups that each take one row tile of the group and move through the
+ * same keys together.  The grid is gangs * gang_size workgroups, one per
+ * compute unit, so the work is even however the lengths are mixed.  The part
+ * of a stream inside range j is partial j - floor(s / A) of the stream's
+ * rows, s its first unit.  Merge such partials with split_keys == 0.
  * Merge state (when the merge is fused): one 32-bit word per row tile, uint32
  * [B, NRT] at counter_offset, NRT = ceil(q_len*H / rows per workgroup of the
  * layout): two counts and a generation bit.  The words must be zero before
@@ -220,7 +237,8 @@ typedef struct {
  * so one workspace serves any sequence of calls on one stream.  Calls that
  * share a workspace must not overlap in time. */
 typedef struct {
-  int32_t split_keys;          /* keys per split (multiple of 32) */
+  int32_t split_keys;          /* keys per split (multiple of 32); balanced schedule: about the keys of
+                                  one range, as planned from total_prefix_len (for information) */
   int32_t max_splits;          /* ceil((max_prefix_len + q_len) / split_keys) */
   int32_t rows;                /* q_len * H */
   int32_t direct;              /* 1: max_splits == 1, no partials, no merge */
@@ -233,6 +251,8 @@ typedef struct {
   int32_t fused_merge;         /* 1: kdt_verify_attn merges inside the split kernel (one launch) */
   int32_t tiles_max;           /* > 0: adaptive splits (above), the longest sequence's key tiles; 0: fixed */
   int64_t counter_offset;      /* bytes into the workspace of the merge counters */
+  int32_t gang_size;           /* > 0: the balanced schedule (above), row tiles per gang; 0: splits */
+  int32_t gangs;               /* balanced schedule: gangs in the launch */
 } kdt_verify_plan;
 
 int kdt_verify_get_plan(const kdt_verify_desc* d, kdt_verify_plan* plan);
@@ -269,7 +289,8 @@ int kdt_verify_attn_noalloc(const kdt_verify_desc* d, void* stream);
  *   out[b,m,:] = sum_k exp(part_lse[b,k,m] - lse[b,m]) * part_o[b,k,m,:]
  * over k < n_splits, where n_splits = max_splits when split_keys == 0, else
  * ceil((prefix_lens[b] + q_len) / split_keys) clamped to [1, max_splits]
- * (partials of adaptive splits: merge with split_keys == 0).
+ * (partials of adaptive splits or of the balanced schedule: merge with
+ * split_keys == 0).
  * Splits with part_lse = -inf carry no weight; a row with no finite split gets
  * out = 0 and lse = -inf.  out is written in `dtype` (bf16: round to nearest
  * even).  part_o (elements of `part_dtype`, KDT_F32 or KDT_BF16) and part_lse

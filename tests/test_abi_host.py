@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
 
 
 def test_version_and_status_strings():
-    assert kdt.lib().kdt_abi_version() == kdt.ABI_VERSION == 4
+    assert kdt.lib().kdt_abi_version() == kdt.ABI_VERSION == 5
     for code in range(5):
         assert kdt.status_str(code)
     assert kdt.status_str(99) == "unknown status"
@@ -128,6 +128,31 @@ def test_split_rows_fit_32bit_offsets():
     rc, p = _plan(_desc(c_kv_ss=big, k_pe_ss=big, c_kv_sb=big * 4224, k_pe_sb=big * 4224))
     assert rc == 0 and p.split_keys == 32
     assert _plan(_desc(c_kv_ss=2 * big, k_pe_ss=64, c_kv_sb=2 * big * 4224))[0] == 2
+
+
+def test_balanced_schedule_plan():
+    """The balanced schedule on request: one workgroup per compute unit (the
+    host query falls back to 256 without a device), gangs of gang_size row
+    tiles, at least two partial slots per row, and the balance rule's bound on
+    slots per stream (the longest stream over ranges of A key tiles)."""
+    rc, p = _plan(_desc(schedule=2))
+    assert rc == 0 and p.gang_size > 0 and p.gangs == 256 // p.gang_size and p.layout in (1, 2)
+    assert p.direct == 0 and p.tiles_max == 0 and p.fused_merge == 0 and p.max_splits >= 2
+    T = -(-(4096 + 65) // 32)
+    n_rt = -(-(65 * 16) // (128 if p.layout == 1 else 64))
+    U = -(-n_rt // p.gang_size) * T
+    A = -(-U // p.gangs)
+    assert p.max_splits == max(2, -(-T // A) + 1)
+    for g in (1, 3, 9):
+        rc, p = _plan(_desc(schedule=2, gang_size=g, layout=1))
+        assert rc == 0 and p.gang_size == g and p.gangs == 256 // g
+    assert _plan(_desc(schedule=2, gang_size=10, layout=1))[0] == 1     # more than the 9 row tiles
+    assert _plan(_desc(schedule=2, split_keys=256))[0] == 1             # the balanced schedule sizes its own ranges
+    assert _plan(_desc(schedule=3))[0] == 1
+    assert _plan(_desc(gang_size=-1))[0] == 1
+    assert _plan(_desc(schedule=2, layout=4))[0] == 2                   # layouts 1 and 2 only
+    rc, p = _plan(_desc(schedule=1))
+    assert rc == 0 and p.gang_size == 0
 
 
 def test_masks_or_parents_required():

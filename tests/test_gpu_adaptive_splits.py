@@ -5,7 +5,8 @@ work; with the sum of the prefix lengths as a hint the plan sizes the launch
 for the sequences it really has.  Checked against the float64 oracle at full
 size and on extreme mixes of lengths, the partials of every split against the
 oracle on the split's own keys, and the stage-by-stage route (partials, then
-the merge over all splits) bit-exact against kdt_verify_attn."""
+the merge over all splits) bit-exact against kdt_verify_attn.  (schedule 1:
+splits, where the library could choose the balanced schedule.)"""
 import numpy as np
 import pytest
 import torch
@@ -18,12 +19,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _plan(g, **kw):
+    kw.setdefault("schedule", 1)
     d, _, _ = kdt._verify_prepare(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, None, g.cfg.softmax_scale,
                                   g.max_prefix_len, None, None, None, 0, parents=g.parents, **kw)
     return kdt.verify_plan(d)
 
 
 def _run(g, **kw):
+    kw.setdefault("schedule", 1)
     out, lse = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, None, g.cfg.softmax_scale,
                                max_prefix_len=g.max_prefix_len, parents=g.parents, **kw)
     torch.cuda.synchronize()
@@ -81,7 +84,7 @@ def test_partials_follow_the_adaptive_rule_and_merge_over_all_splits():
     hint = int(inp.prefix_lens.sum())
     part_o, part_lse, p = kdt.verify_partials(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, None,
                                               cfg.softmax_scale, max_prefix_len=g.max_prefix_len,
-                                              parents=g.parents, total_prefix_len=hint, layout=1)
+                                              parents=g.parents, total_prefix_len=hint, layout=1, schedule=1)
     torch.cuda.synchronize()
     assert p.tiles_max > 0
     S, M = p.max_splits, p.rows

@@ -145,6 +145,11 @@ struct VerifyArgs {
   int tiles_max;
   int group_mul;        // order of the (sequence, split) groups (coprime to B * max_splits)
   int compact;          // number the pieces with work (adaptive splits over several sequences)
+  // Work-balanced schedule (gang > 0): gang = row tiles that move through the
+  // keys together, n_grp = such groups per sequence, gangs = gangs in the
+  // launch (the grid is gangs * gang workgroups)
+  int gang, n_grp, gangs;
+  int span_keys;        // the most keys of one piece (cache rows one buffer descriptor spans)
   int q_rows_uniform;   // query rows m = t * H + h sit at one byte stride (q_lat and q_pe)
   int part_bf16;        // partial outputs in bf16 (else float32)
   // Merge inside the split kernel (partial mode only): the split workgroups
@@ -407,8 +412,10 @@ struct PartLoad<__bf16> {
 // of the workgroup must then call it with the same item.  Splits at or past
 // ns are skipped.  COH: the partials
 // were stored by other workgroups of the running launch and are read with
-// device-coherent loads.
-template <typename T, typename PT, bool WIDE, bool COH>
+// device-coherent loads.  GATE: a split's partial row is loaded only once its
+// log-sum-exp has shown it is not empty (for partial buffers where most of
+// the max_splits slots of a row are empty; one more memory round trip).
+template <typename T, typename PT, bool WIDE, bool COH, bool GATE = false>
 __device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const float* __restrict__ part_lse,
                                            int max_splits, int ns, int M, int H, int R, int n_blk, int b, int blk,
                                            int cg, T* __restrict__ out, int64_t out_sb, int64_t out_st,
@@ -446,7 +453,8 @@ __device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const 
         if (k < ke) ok[j] = load16_coherent<raw>(po_blk, off);
       } else {
         lk[j] = k < ke ? pl[(int64_t)k * M] : -INFINITY;
-        if (k < ke) ok[j] = *reinterpret_cast<const raw*>(reinterpret_cast<const char*>(po_blk) + off);
+        if (k < ke && (!GATE || lk[j] != -INFINITY))
+          ok[j] = *reinterpret_cast<const raw*>(reinterpret_cast<const char*>(po_blk) + off);
       }
     }
     float cm = lk[0];
@@ -590,7 +598,7 @@ __device__ __forceinline__ Piece compact_piece(const VerifyArgs& a, int lane) {
     int c = j < a.B ? pieces_of(a, a.prefix_lens[j]) : 0;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
-    total += c;
+    total += __builtin_amdgcn_readfirstlane(c);     // (uniform: the exit below is a uniform branch)
   }
   const int i = blockIdx.x;
   if (i >= total) return pc;
@@ -617,9 +625,157 @@ __device__ __forceinline__ Piece compact_piece(const VerifyArgs& a, int lane) {
       pc.work = true;
       return pc;
     }
-    base += __shfl(incl, 63);
+    base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
   }
   return pc;
+}
+
+// One piece of work of a workgroup: row tile rt of sequence b over one key
+// range, written as partial `split`.  known: the prefix length L is known
+// (else the body loads it).  The key range [k_begin, k_end) and the stream's
+// piece count ns are given by the balanced schedule; the other schedules
+// take them from split_range.
+struct PieceDesc {
+  int b, rt, split, L, k_begin, k_end, ns;
+  bool known;
+};
+
+__device__ __forceinline__ bool len_bad(const VerifyArgs& a, int L) {
+  return L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
+}
+// units of one stream of sequence b: its key tiles (one for a sequence with
+// an invalid prefix length, whose workgroups flag it and write the empty
+// result)
+__device__ __forceinline__ int units_of(const VerifyArgs& a, int L) {
+  return len_bad(a, L) ? 1 : (L + a.q - 1) / kBN + 1;
+}
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Work-balanced schedule (stream-K style).  The row tiles of a sequence are
+// cut into n_grp groups of `gang` (the last may be short), and each
+// (sequence, group) pair is a stream of T_b units, one per key tile of the
+// sequence.  The streams are laid end to end, sequence-major, U units in
+// all, and gang j of the launch's G gangs takes units [j A, min(U, (j + 1) A))
+// with A = ceil(U / G), raised so that no stream meets more than max_splits
+// gangs (A >= ceil(T_max / (max_splits - 1))) and capped at span_keys / 32
+// (then gang j also takes the ranges of gangs j + G, j + 2 G, ... after its
+// own).  A gang is `gang` workgroups that are consecutive after xcd_remap,
+// so they share an XCD and its L2: member m does row tile grp * gang + m of
+// every stream the gang's range meets, so the members read the same keys at
+// about the same time.  Where a range crosses from one stream into the
+// next, its workgroups finish one piece (one partial) and start the next.
+// The piece of a stream that gang j does is the stream's partial
+// j - floor(first unit / A), and a stream has floor(last unit / A) -
+// floor(first unit / A) + 1 of them.  Every wave walks the ranges itself
+// from the prefix lengths (64 sequences per pass); all values are uniform.
+struct BalWalk {
+  int64_t A, U;    // units per gang, units in all
+  int64_t s, e;    // next unit, end of the current range
+  int64_t st;      // first unit of the current stream
+  int j;           // current gang
+  int b, grp, L, T;  // current stream: sequence, row-tile group, prefix length, units
+  int member;
+};
+
+// the stream holding unit w.s
+__device__ __forceinline__ void bal_locate(const VerifyArgs& a, BalWalk& w, int lane) {
+  int64_t base = 0;     // units of the sequences before this pass's
+  for (int j0 = 0; j0 < a.B; j0 += 64) {
+    const int j = j0 + lane;
+    const int L = j < a.B ? a.prefix_lens[j] : 0;
+    const int64_t c = j < a.B ? (int64_t)a.n_grp * units_of(a, L) : 0;
+    int64_t incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const uint64_t past = __ballot(base + incl > w.s);
+    if (past) {
+      const int k = __builtin_ctzll(past);
+      w.b = j0 + k;
+      w.L = __builtin_amdgcn_readfirstlane(__shfl(L, k));
+      w.T = units_of(a, w.L);
+      const int64_t sb = uniform64(base + __shfl(incl, k) - __shfl(c, k));
+      w.grp = (int)((w.s - sb) / w.T);
+      w.st = sb + (int64_t)w.grp * w.T;
+      return;
+    }
+    base += uniform64(__shfl(incl, 63));
+  }
+}
+
+// Sets up workgroup blockIdx.x's walk; false if it has no work.
+__device__ __forceinline__ bool bal_init(const VerifyArgs& a, BalWalk& w, int lane) {
+  int64_t useq = 0;
+  int tmax = 1;
+  for (int j0 = 0; j0 < a.B; j0 += 64) {
+    const int j = j0 + lane;
+    const int L = j < a.B ? a.prefix_lens[j] : 0;
+    int64_t c = j < a.B ? units_of(a, L) : 0;
+    int tm = c;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      c += __shfl_xor(c, d);
+      tm = max(tm, __shfl_xor(tm, d));
+    }
+    useq += uniform64(c);
+    tmax = max(tmax, __builtin_amdgcn_readfirstlane(tm));
+  }
+  w.U = (int64_t)a.n_grp * useq;
+  const int64_t G = a.gangs;
+  int64_t A = (w.U + G - 1) / G;
+  A = max(A, (int64_t)((tmax + a.max_splits - 2) / (a.max_splits - 1)));
+  A = min(A, (int64_t)(a.span_keys / kBN));
+  w.A = max(A, (int64_t)1);
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  w.j = u / a.gang;
+  w.member = u - w.j * a.gang;
+  w.s = (int64_t)w.j * w.A;
+  if (w.s >= w.U) return false;
+  w.e = min(w.U, w.s + w.A);
+  bal_locate(a, w, lane);
+  return true;
+}
+
+// The next piece of the walk (pieces of row tiles past the last are
+// skipped); false when the workgroup's ranges are done.
+__device__ __forceinline__ bool bal_next(const VerifyArgs& a, BalWalk& w, int lane, PieceDesc& pc) {
+  while (true) {
+    if (w.s >= w.e) {
+      w.j += a.gangs;
+      w.s = (int64_t)w.j * w.A;
+      if (w.s >= w.U) return false;
+      w.e = min(w.U, w.s + w.A);
+      bal_locate(a, w, lane);
+    } else if (w.s >= w.st + w.T) {
+      w.st += w.T;
+      if (++w.grp == a.n_grp) {
+        w.grp = 0;
+        ++w.b;
+        w.L = ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[w.b];
+        w.T = units_of(a, w.L);
+      }
+    }
+    const int64_t s0 = w.s;
+    const int64_t pe = min(w.e, w.st + w.T);
+    w.s = pe;
+    const int rt = w.grp * a.gang + w.member;
+    if (rt >= a.n_rt) continue;
+    pc.b = w.b;
+    pc.rt = rt;
+    pc.L = w.L;
+    pc.known = true;
+    pc.split = (int)(s0 / w.A - w.st / w.A);
+    pc.ns = (int)((w.st + w.T - 1) / w.A - w.st / w.A + 1);
+    pc.k_begin = (int)(s0 - w.st) * kBN;
+    pc.k_end = len_bad(a, w.L) ? 1 : min(w.L + a.q, (int)(pe - w.st) * kBN);
+    return true;
+  }
 }
 
 // The merge of one row tile's partials inside the split kernel.  The split
@@ -704,8 +860,28 @@ __device__ __forceinline__ void fused_merge(const VerifyArgs& a, int b, int rt, 
 // wave then holds half the accumulators and does half the value
 // MFMAs; the duplicated score MFMAs are spare capacity when the memory stream
 // is the bound.
-template <typename T, int R, int P, bool DIRECT, int CS>
-__global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a) {
+// The kernel's arguments, read again from the kernel argument segment
+// through an opaque pointer (the one argument, a VerifyArgs, sits at its
+// start): values derived from them are then computed where they are used,
+// once per piece, rather than hoisted out of the piece loop and held in
+// registers across every piece.
+__device__ __forceinline__ VerifyArgs reread_args() {
+  typedef const __attribute__((address_space(4))) uint32_t cu32;
+  cu32* src = (cu32*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(src));
+  static_assert(sizeof(VerifyArgs) % 4 == 0, "argument words");
+  uint32_t w[sizeof(VerifyArgs) / 4];
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(VerifyArgs) / 4); ++i) w[i] = src[i];
+  VerifyArgs a;
+  __builtin_memcpy(&a, w, sizeof(VerifyArgs));
+  return a;
+}
+
+// BAL: the balanced schedule (a workgroup walks several pieces; a separate
+// instantiation, so that the one-piece kernels keep their registers).
+template <typename T, int R, int P, bool DIRECT, int CS, bool BAL = false>
+__global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_in) {
   typedef Mfma<T> MM;
   typedef typename MM::frag frag;
   constexpr int D = R + P;
@@ -775,23 +951,78 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // g = g' * group_mul mod (B * max_splits), group_mul coprime to the group
   // count, so that each XCD's block of units mixes sequences and splits
   // (with adaptive splits a short sequence's high splits have no work).
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  int rt, split, b, L_known = 0;
-  if (a.compact) {
-    const Piece pc = compact_piece(a, lane);
-    if (!pc.work) return;
-    rt = __builtin_amdgcn_readfirstlane(pc.rt);
-    split = __builtin_amdgcn_readfirstlane(pc.split);
-    b = __builtin_amdgcn_readfirstlane(pc.b);
-    L_known = __builtin_amdgcn_readfirstlane(pc.L);
-  } else {
-    const int u = xcd_remap(blockIdx.x, gridDim.x);
-    rt = u % a.n_rt;
-    const int g = (int)((int64_t)(u / a.n_rt) * a.group_mul % ((int64_t)a.B * a.max_splits));
-    split = g % a.max_splits;
-    b = g / a.max_splits;
+  // Pieces: one per workgroup, except in the balanced schedule, where a
+  // workgroup walks its ranges piece by piece (the workgroup meets at a
+  // barrier between pieces, so that no wave reuses LDS another still reads).
+  // The walk's state lives in LDS between pieces (two slots, by piece
+  // parity: every wave reads the current one after the barrier, the first
+  // thread writes the next), so no register holds it across a piece.
+  static_assert(!BAL || (!DIRECT && (CS == 1 || CS == 2)), "balanced schedule: layouts 1 and 2, partials");
+  __shared__ BalWalk s_walk[BAL ? 2 : 1];
+  bool more = true;
+  if constexpr (BAL) {
+    BalWalk w0;
+    more = bal_init(a_in, w0, threadIdx.x & 63);
+    if (threadIdx.x == 0) s_walk[0] = w0;
+    __syncthreads();
   }
+#pragma unroll 1
+  for (int iter = 0; BAL ? more : iter < 1; ++iter) {
+  // Balanced schedule: the arguments and the thread index are taken afresh
+  // for every piece (the index through an opaque zero), so that what the
+  // body derives from them is computed inside the loop, not hoisted out of it
+  // and held in registers across every piece.
+  // (the one-piece kernels read the argument itself, whose loads the
+  // compiler may repeat instead of holding their values)
+  VerifyArgs a_piece;
+  if constexpr (BAL) a_piece = reread_args();
+  const VerifyArgs& a = BAL ? a_piece : a_in;
+  int opaque0 = 0;
+  if constexpr (BAL) asm volatile("s_mov_b32 %0, 0" : "=s"(opaque0));
+  const int tid = (int)threadIdx.x + opaque0;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  PieceDesc pc;
+  if constexpr (BAL) {
+    if (iter > 0) __syncthreads();
+    BalWalk walk;
+    {
+      const BalWalk& sw = s_walk[iter & 1];
+      walk.A = uniform64(sw.A);
+      walk.U = uniform64(sw.U);
+      walk.s = uniform64(sw.s);
+      walk.e = uniform64(sw.e);
+      walk.st = uniform64(sw.st);
+      walk.j = __builtin_amdgcn_readfirstlane(sw.j);
+      walk.b = __builtin_amdgcn_readfirstlane(sw.b);
+      walk.grp = __builtin_amdgcn_readfirstlane(sw.grp);
+      walk.L = __builtin_amdgcn_readfirstlane(sw.L);
+      walk.T = __builtin_amdgcn_readfirstlane(sw.T);
+      walk.member = __builtin_amdgcn_readfirstlane(sw.member);
+    }
+    if (!bal_next(a, walk, lane, pc)) break;
+    if (tid == 0) s_walk[(iter + 1) & 1] = walk;
+  } else {
+    more = false;
+    if (a.compact) {
+      const Piece cp = compact_piece(a, lane);
+      if (!cp.work) return;
+      pc.rt = __builtin_amdgcn_readfirstlane(cp.rt);
+      pc.split = __builtin_amdgcn_readfirstlane(cp.split);
+      pc.b = __builtin_amdgcn_readfirstlane(cp.b);
+      pc.L = __builtin_amdgcn_readfirstlane(cp.L);
+      pc.known = true;
+    } else {
+      const int u = xcd_remap(blockIdx.x, gridDim.x);
+      pc.rt = u % a.n_rt;
+      const int g = (int)((int64_t)(u / a.n_rt) * a.group_mul % ((int64_t)a.B * a.max_splits));
+      pc.split = g % a.max_splits;
+      pc.b = g / a.max_splits;
+      pc.L = 0;
+      pc.known = false;
+    }
+    pc.k_begin = pc.k_end = pc.ns = 0;
+  }
+  const int rt = pc.rt, split = pc.split, b = pc.b;
   const int r = lane & 31, hh = lane >> 5;
   // row block, output column half (and depth half), key stream
   const int rb = KS ? (wave >> 1) : wave / CSC, chalf = KS ? 0 : wave % CSC, kp = KS ? (wave & 1) : 0;
@@ -808,12 +1039,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // the split's first key as for a sequence of the longest length the
   // launch allows (right for it and for every split of fixed size; the
   // speculative copies below use it)
-  const bool L_bad_known = a.compact && (L_known < 0 || L_known > a.max_prefix_len ||
-                                         (int64_t)L_known + a.q > a.capacity);
-  const int k_spec = a.compact ? (L_bad_known ? 0
-                                              : split_range(L_known + a.q, split, a.split_keys, a.max_splits,
-                                                            a.tiles_max).k_begin)
-                               : split * a.split_keys;
+  const bool L_bad_known = pc.known && len_bad(a, pc.L);
+  const int k_spec = !pc.known ? split * a.split_keys
+                     : L_bad_known ? 0
+                     : BAL ? pc.k_begin
+                           : split_range(pc.L + a.q, split, a.split_keys, a.max_splits, a.tiles_max).k_begin;
   int k_begin = k_spec;
   const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
   const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
@@ -824,7 +1054,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
   // capacity (the host keeps split_keys rows of either region under 2^31
   // bytes); every row a copy reads is one of them.
   auto span_of = [&](int kb) {
-    return max((int64_t)0, min((int64_t)a.split_keys, a.capacity - (int64_t)kb));
+    return max((int64_t)0, min((int64_t)a.span_keys, a.capacity - (int64_t)kb));
   };
   i32x4 rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
   i32x4 rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
@@ -910,12 +1140,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     vw0 = vr[0];
     vw1 = a.W > 1 ? vr[1] : 0ull;
   }
-  const int L = a.compact ? L_known : ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
+  const int L = pc.known ? pc.L : ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
 
-  const bool bad = L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
+  const bool bad = len_bad(a, L);
   const int N = L + a.q;
-  const SplitRange sr = split_range(bad ? 1 : N, split, a.split_keys, a.max_splits, a.tiles_max);
+  SplitRange sr;
+  if (BAL) {
+    sr.k_begin = pc.k_begin;
+    sr.k_end = pc.k_end;
+    sr.ns = pc.ns;
+  } else {
+    sr = split_range(bad ? 1 : N, split, a.split_keys, a.max_splits, a.tiles_max);
+  }
   k_begin = sr.k_begin;
+  // (compaction and the balanced schedule run no workgroup for the splits a
+  // sequence does not use: the workgroups of its first split mark them empty)
+  const bool fill_unused = BAL || a.compact;
 
   if (bad || k_begin >= N) wait_vmem_lds<0>();   // no copy may outlive the workgroup
   if (bad) {
@@ -927,16 +1167,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
         T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
         for (int d = 0; d < R; ++d) o[d] = (T)0.0f;
       } else {
-        // (compaction gives a skipped sequence one split: it writes them all)
-        for (int k = split; k < (a.compact ? a.max_splits : split + 1); ++k)
+        // (a skipped sequence has one split there: it writes them all)
+        for (int k = split; k < (fill_unused ? a.max_splits : split + 1); ++k)
           a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
       }
     }
-    return;
+    continue;
   }
-  if (!DIRECT && a.compact && !a.fuse && split == 0 && row_ok && hh == 0 && chalf == 0 && kp == 0) {
-    // compaction runs no workgroup for the splits this sequence does not
-    // use: their partials are marked empty here
+  if (!DIRECT && fill_unused && !a.fuse && split == 0 && row_ok && hh == 0 && chalf == 0 && kp == 0) {
     for (int k = sr.ns; k < a.max_splits; ++k) a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
   }
   if (k_begin >= N) {
@@ -944,7 +1182,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
     // merge over all max_splits splits is always right
     if (!DIRECT && !a.fuse && row_ok && hh == 0 && chalf == 0 && kp == 0)
       a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = -INFINITY;
-    return;
+    continue;
   }
   const int k_end = sr.k_end;
   const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
@@ -1490,12 +1728,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a)
       fused_merge<T, R>(a, b, rt, split, ns_b, BM, reinterpret_cast<float*>(&s_tiles[0][0]), tid);
     }
   }
+  }   // pieces
 }
 
 // WIDE: one (sequence, block, column group) per workgroup; used when there
 // are more splits than one wave loads in one round trip.  Otherwise one item
 // per wave.
-template <typename T, typename PT, bool WIDE>
+template <typename T, typename PT, bool WIDE, bool GATE>
 __global__ __launch_bounds__(256) void merge_kernel(
     const PT* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
     int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys, int tiles_max,
@@ -1517,8 +1756,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
     // (a skipped sequence wrote empty partials: any count is right)
     ns = L >= 0 && L <= 0x7FFFFFFF - q ? split_range(L + q, 0, split_keys, max_splits, tiles_max).ns : max_splits;
   }
-  merge_item<T, PT, WIDE, false>(part_o, part_lse, max_splits, ns, M, H, R, n_blk, b, blk, cg, out, out_sb, out_st,
-                                 out_sh, lse, s_st, wave, lane);
+  merge_item<T, PT, WIDE, false, GATE>(part_o, part_lse, max_splits, ns, M, H, R, n_blk, b, blk, cg, out, out_sb,
+                                       out_st, out_sh, lse, s_st, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1564,6 +1803,9 @@ static int validate(const kdt_verify_desc* d) {
   if (d->layout < 0 || d->layout > 4) return KDT_ERR_INVALID_ARG;
   if (d->partials_f32 != 0 && d->partials_f32 != 1) return KDT_ERR_INVALID_ARG;
   if (d->merge_mode != 0 && d->merge_mode != 1) return KDT_ERR_INVALID_ARG;
+  if (d->schedule < 0 || d->schedule > 2 || d->gang_size < 0) return KDT_ERR_INVALID_ARG;
+  if (d->schedule == 2 && d->split_keys != 0) return KDT_ERR_INVALID_ARG;
+  if ((int64_t)d->max_prefix_len + d->q_len > 0x7FFFFFFF - kBN) return KDT_ERR_UNSUPPORTED;
   if (!(d->softmax_scale > 0.0f) || !isfinite(d->softmax_scale)) return KDT_ERR_INVALID_ARG;
   if (d->q_len > KDT_MAX_Q_LEN) return KDT_ERR_UNSUPPORTED;
   if (!shape_supported(d->dtype, d->R, d->P)) return KDT_ERR_UNSUPPORTED;
@@ -1626,6 +1868,28 @@ static double launch_cost(int64_t wgs, int64_t splits, int64_t tiles, int R, int
   return rounds * (t * t_tile + t_start) + merge;
 }
 
+// Modelled time of the balanced schedule: one round, every gang doing A key
+// tiles in `pieces` pieces, each paying a start-up, plus the merge of `parts`
+// partial row tiles of `splits` slots (gated loads: one more round trip), plus
+// a share of the time the cache takes to stream `reads` times past the compute
+// units (each row-tile group reads every key once; the members of a gang share
+// one read through their XCD's L2; measured: gangs of one row tile, every
+// workgroup reading its keys alone, ran 6-8% slower than gangs of 5 to 11).
+// Same constants as launch_cost otherwise.
+static double balanced_cost(int64_t A, double pieces, int64_t parts, int64_t splits, int64_t reads,
+                            double cache_bytes, int R, int P, int layout, int part_bytes) {
+  const int rows = layout_rows(layout);
+  const double t_tile = layout == 4 ? 1.7 * 1.1 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+  const double t_start = layout == 4 ? 6.0 : 4.0;
+  const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
+  const double t_merge = 3.0, t_merge_batch = 2.0;
+  const int64_t batches = splits > 16 ? (splits + 63) / 64 : 1;
+  const double t_fetch = 0.15 * (double)reads * cache_bytes / 8.0e6;   // us at 8 TB/s
+  return A * t_tile + pieces * t_start + parts * t_part + t_merge + t_merge_batch * (double)(batches + 1) + t_fetch;
+}
+
+constexpr int kBalancedMaxB = 4096;      // the walk scans the prefix lengths in every workgroup
+
 static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   const int rc = validate(d);
   if (rc != KDT_OK) return rc;
@@ -1679,16 +1943,59 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
       if (d->split_keys) break;
     }
   }
+  // The balanced schedule: every layout and gang size, one round of
+  // workgroups.  Chosen over splits only where the model says it is faster
+  // (the fused merge, on request, needs splits).
+  int64_t bal_g = 0, bal_G = 0, bal_S = 0, bal_A = 0;
+  const bool bal_ok = d->split_keys == 0 && d->schedule != 1 && d->B <= kBalancedMaxB &&
+                      (d->schedule == 2 || d->merge_mode == 0);
+  if (bal_ok) {
+    const int cus = device_cus();
+    const int64_t lim = max_sk / kBN;            // key tiles one piece may span
+    double bal_best = d->schedule == 2 ? 1e300 : best;
+    for (int layout = 1; layout <= 2; ++layout) {
+      if (d->layout && layout != d->layout) continue;
+      const int64_t n_rt = (M + layout_rows(layout) - 1) / layout_rows(layout);
+      for (int64_t g = 1; g <= n_rt && g <= cus; ++g) {
+        if (d->gang_size && g != d->gang_size) continue;
+        const int64_t G = cus / g;
+        const int64_t n_grp = (n_rt + g - 1) / g;
+        const int64_t U = n_grp * total_tiles;
+        const int64_t A = std::min(lim, std::max<int64_t>(1, (U + G - 1) / G));
+        const int64_t S = std::max<int64_t>({2, (tiles_max + A - 1) / A + 1, (tiles_max + lim - 1) / lim + 1});
+        const int64_t streams = (int64_t)d->B * n_grp;
+        const double pieces = 1.0 + (double)streams / (double)G;
+        const int64_t parts = std::min(G + streams, streams * S) * g;
+        const double kv_bytes = (double)total_keys * (double)(d->R + d->P) * elem_size(d->dtype);
+        const double c = balanced_cost(A, pieces, parts, S, n_grp, kv_bytes, d->R, d->P, layout,
+                                       elem_size(part_dtype)) *
+                         (double)((U + G - 1) / G > lim ? ((U + G - 1) / G + lim - 1) / lim : 1);
+        if (c < bal_best * 0.999) {
+          bal_best = c;
+          bal_g = g;
+          bal_G = G;
+          bal_S = S;
+          bal_A = A;
+          best_layout = layout;
+        }
+      }
+    }
+    // (on request: layouts 1 and 2 only, and a gang no larger than the row tiles)
+    if (d->schedule == 2 && !bal_g) return d->layout > 2 ? KDT_ERR_UNSUPPORTED : KDT_ERR_INVALID_ARG;
+  }
   p->layout = best_layout;
   p->part_dtype = part_dtype;
+  p->gang_size = (int32_t)bal_g;
+  p->gangs = (int32_t)bal_G;
+  if (bal_g) sk = bal_A * kBN;
   if (sk <= 0) return KDT_ERR_UNSUPPORTED;   // no split size fits the row offsets
-  const int64_t ns = (n_max + sk - 1) / sk;
+  const int64_t ns = bal_g ? bal_S : (n_max + sk - 1) / sk;
   if (ns > 0x7FFFFFFF / 2) return KDT_ERR_UNSUPPORTED;
   p->split_keys = (int32_t)(sk > 0x7FFFFFFF ? 0x7FFFFFFF : sk);
   p->max_splits = (int32_t)ns;
-  p->tiles_max = adaptive && ns > 1 ? (int32_t)tiles_max : 0;
+  p->tiles_max = adaptive && ns > 1 && !bal_g ? (int32_t)tiles_max : 0;
   p->rows = M;
-  p->direct = ns == 1 ? 1 : 0;
+  p->direct = ns == 1 && !bal_g ? 1 : 0;
   const int64_t n_part_rows = (int64_t)d->B * ns * M;
   const int64_t o_bytes = (int64_t)d->B * ns * ((M + 31) / 32) * 32 * d->R * elem_size(part_dtype);
   p->part_o_offset = 0;
@@ -1698,7 +2005,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   // be resident at once (one workgroup per compute unit)
   const int64_t n_rt = (M + layout_rows(p->layout) - 1) / layout_rows(p->layout);
   const int64_t grid = (int64_t)d->B * n_rt * ns;
-  p->fused_merge = (!p->direct && d->merge_mode == 1 && grid <= device_cus()) ? 1 : 0;
+  p->fused_merge = (!p->direct && !bal_g && d->merge_mode == 1 && grid <= device_cus()) ? 1 : 0;
   p->counter_offset = ((int64_t)p->partials_bytes + 255) / 256 * 256;
   p->workspace_bytes = p->direct ? 0 : (size_t)(p->counter_offset + (int64_t)d->B * n_rt * 4);
   return KDT_OK;
@@ -1752,6 +2059,15 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.tiles_max = p.tiles_max;
   a.group_mul = group_stride((int64_t)d->B * p.max_splits);
   a.compact = p.tiles_max > 0 && d->B > 1;
+  a.gang = p.gang_size;
+  a.gangs = p.gangs;
+  a.n_grp = p.gang_size > 0 ? (a.n_rt + p.gang_size - 1) / p.gang_size : 0;
+  {
+    // a piece's cache rows of either region stay under 2^31 bytes from its first
+    const int64_t row_bytes = std::max(d->c_kv_ss, d->k_pe_ss) * elem_size(d->dtype);
+    const int64_t max_sk = row_bytes > 0 ? 0x7FFFFFFF / row_bytes / kBN * kBN : 0x7FFFFFE0;
+    a.span_keys = p.gang_size > 0 ? (int)std::min<int64_t>(max_sk, 0x7FFFFFE0) : p.split_keys;
+  }
   a.max_prefix_len = d->max_prefix_len;
   const int64_t es = elem_size(d->dtype);
   a.q_rows_uniform = d->q_lat_st == (int64_t)d->H * d->q_lat_sh && d->q_pe_st == (int64_t)d->H * d->q_pe_sh &&
@@ -1761,9 +2077,17 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
 
 template <typename T, int R, int P>
 static int launch_split(const VerifyArgs& a, bool direct, hipStream_t s) {
-  const int64_t grid = (int64_t)a.B * a.n_rt * a.max_splits;
+  const int64_t grid = a.gang ? (int64_t)a.gangs * a.gang : (int64_t)a.B * a.n_rt * a.max_splits;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
   const bool cs2 = a.layout == 2;
+  if (a.gang) {
+    if (direct || (a.layout != 1 && a.layout != 2)) return KDT_ERR_UNSUPPORTED;
+    if (cs2)
+      hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 2, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((verify_split_kernel<T, R, P, false, 1, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    return launch_status();
+  }
   if constexpr (R == 512 && P == 64 && sizeof(T) == 2) {
     if (a.layout == 3) {
       if (direct)
@@ -1800,36 +2124,46 @@ static int dispatch_split(int dtype, int R, int P, const VerifyArgs& a, bool dir
 
 template <typename PT>
 static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, const float* pl, int max_splits,
-                          const int32_t* prefix_lens, int split_keys, int tiles_max, void* out, int64_t osb,
-                          int64_t ost, int64_t osh, float* lse, hipStream_t s) {
+                          const int32_t* prefix_lens, int split_keys, int tiles_max, bool gate, void* out,
+                          int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
   const int n_blk = (q * H + 31) / 32;
   const int64_t items = (int64_t)B * n_blk * (R / (2 * PartLoad<PT>::NV));
   // more splits than one wave loads in one round trip: a workgroup per item
   const bool wide = max_splits > 16;
   const int64_t grid = wide ? items : (items + 3) / 4;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
-#define KDT_MERGE_LAUNCH(TO, W)                                                                              \
-  hipLaunchKernelGGL((merge_kernel<TO, PT, W>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, q, \
-                     H, R, n_blk, prefix_lens, split_keys, tiles_max, static_cast<TO*>(out), osb, ost, osh, lse)
+#define KDT_MERGE_LAUNCH(TO, W, GT)                                                                          \
+  hipLaunchKernelGGL((merge_kernel<TO, PT, W, GT>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, \
+                     q, H, R, n_blk, prefix_lens, split_keys, tiles_max, static_cast<TO*>(out), osb, ost, osh, lse)
   if (dtype == KDT_BF16) {
-    if (wide) KDT_MERGE_LAUNCH(__bf16, true);
-    else KDT_MERGE_LAUNCH(__bf16, false);
+    if (gate) {
+      if (wide) KDT_MERGE_LAUNCH(__bf16, true, true);
+      else KDT_MERGE_LAUNCH(__bf16, false, true);
+    } else {
+      if (wide) KDT_MERGE_LAUNCH(__bf16, true, false);
+      else KDT_MERGE_LAUNCH(__bf16, false, false);
+    }
   } else {
-    if (wide) KDT_MERGE_LAUNCH(float, true);
-    else KDT_MERGE_LAUNCH(float, false);
+    if (gate) {
+      if (wide) KDT_MERGE_LAUNCH(float, true, true);
+      else KDT_MERGE_LAUNCH(float, false, true);
+    } else {
+      if (wide) KDT_MERGE_LAUNCH(float, true, false);
+      else KDT_MERGE_LAUNCH(float, false, false);
+    }
   }
 #undef KDT_MERGE_LAUNCH
   return launch_status();
 }
 
 static int launch_merge(int dtype, int B, int q, int H, int R, int part_dtype, const void* po, const float* pl,
-                        int max_splits, const int32_t* prefix_lens, int split_keys, int tiles_max, void* out,
-                        int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
+                        int max_splits, const int32_t* prefix_lens, int split_keys, int tiles_max, bool gate,
+                        void* out, int64_t osb, int64_t ost, int64_t osh, float* lse, hipStream_t s) {
   if (part_dtype == KDT_BF16)
     return launch_merge_t(dtype, B, q, H, R, static_cast<const __bf16*>(po), pl, max_splits, prefix_lens,
-                          split_keys, tiles_max, out, osb, ost, osh, lse, s);
+                          split_keys, tiles_max, gate, out, osb, ost, osh, lse, s);
   return launch_merge_t(dtype, B, q, H, R, static_cast<const float*>(po), pl, max_splits, prefix_lens, split_keys,
-                        tiles_max, out, osb, ost, osh, lse, s);
+                        tiles_max, gate, out, osb, ost, osh, lse, s);
 }
 
 // The verify with a given workspace (NULL when the plan is direct).
@@ -1837,8 +2171,12 @@ static int verify_run(const kdt_verify_desc* d, const kdt_verify_plan& p, void* 
   const VerifyArgs a = make_args(d, p, p.direct ? nullptr : workspace, p.fused_merge != 0);
   int r = dispatch_split(d->dtype, d->R, d->P, a, p.direct != 0, s);
   if (r != KDT_OK || p.direct || p.fused_merge) return r;
+  // (balanced schedule: every slot of a row is merged, the empty ones skipped
+  // by their log-sum-exp)
+  const bool bal = p.gang_size > 0;
   return launch_merge(d->dtype, d->B, d->q_len, d->H, d->R, p.part_dtype, a.part_o, a.part_lse, p.max_splits,
-                      d->prefix_lens, p.split_keys, p.tiles_max, d->out, d->out_sb, d->out_st, d->out_sh, d->lse, s);
+                      d->prefix_lens, bal ? 0 : p.split_keys, bal ? 0 : p.tiles_max, bal, d->out, d->out_sb,
+                      d->out_st, d->out_sh, d->lse, s);
 }
 
 // Workspace of kdt_verify_attn_noalloc: a fixed device array, one per GPU
@@ -1921,6 +2259,6 @@ extern "C" int kdt_merge_partials(int32_t dtype, int32_t B, int32_t q_len, int32
   if (!kdt::aligned16(part_o) || !kdt::aligned16(out) || (R % vec) || out_sb % vec || out_st % vec ||
       out_sh % vec || out_sb < 0 || out_st < 0 || out_sh < 0)
     return KDT_ERR_UNSUPPORTED;
-  return kdt::launch_merge(dtype, B, q_len, H, R, part_dtype, part_o, part_lse, max_splits, prefix_lens, split_keys, 0,
+  return kdt::launch_merge(dtype, B, q_len, H, R, part_dtype, part_o, part_lse, max_splits, prefix_lens, split_keys, 0, false,
                            out, out_sb, out_st, out_sh, lse, static_cast<hipStream_t>(stream));
 }

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdt.so")
 
 KDT_F32, KDT_BF16 = 0, 1
-ABI_VERSION = 4                       # the KDT_ABI_VERSION this binding was written for
+ABI_VERSION = 5                       # the KDT_ABI_VERSION this binding was written for
 KDT_SEQ_BAD_TREE, KDT_SEQ_BAD_LEN, KDT_SEQ_BAD_INDEX = 1, 2, 4
 MAX_Q_LEN = 128
 
@@ -41,7 +41,7 @@ class VerifyDesc(ctypes.Structure):
         ("split_keys", _c_i32), ("layout", _c_i32), ("partials_f32", _c_i32),
         ("parents", _c_p),
         ("merge_mode", _c_i32), ("merge_wait_us", _c_i32),
-        ("total_prefix_len", _c_i64),
+        ("total_prefix_len", _c_i64), ("schedule", _c_i32), ("gang_size", _c_i32),
     ]
 
 
@@ -50,7 +50,7 @@ class VerifyPlan(ctypes.Structure):
         ("split_keys", _c_i32), ("max_splits", _c_i32), ("rows", _c_i32), ("direct", _c_i32),
         ("layout", _c_i32), ("part_dtype", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64),
         ("workspace_bytes", ctypes.c_size_t), ("partials_bytes", ctypes.c_size_t), ("fused_merge", _c_i32),
-        ("tiles_max", _c_i32), ("counter_offset", _c_i64),
+        ("tiles_max", _c_i32), ("counter_offset", _c_i64), ("gang_size", _c_i32), ("gangs", _c_i32),
     ]
 
 
@@ -146,7 +146,7 @@ def build_visibility(parents: torch.Tensor, vis=None, depth=None, seq_status=Non
 
 def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
                  seq_status, split_keys, layout=0, partials_f32=False, parents=None, merge_mode=0, merge_wait_us=0,
-                 total_prefix_len=0):
+                 total_prefix_len=0, schedule=0, gang_size=0):
     B, q, H, R = q_lat.shape
     P = q_pe.shape[-1]
     d = VerifyDesc()
@@ -171,12 +171,14 @@ def _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_p
     d.merge_mode = int(merge_mode)
     d.merge_wait_us = int(merge_wait_us)
     d.total_prefix_len = int(total_prefix_len)
+    d.schedule = int(schedule)
+    d.gang_size = int(gang_size)
     return d
 
 
 def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
                     seq_status, split_keys, layout=0, partials_f32=False, parents=None, merge_mode=0,
-                    merge_wait_us=0, total_prefix_len=0):
+                    merge_wait_us=0, total_prefix_len=0, schedule=0, gang_size=0):
     for t in (q_lat, q_pe, c_kv, k_pe):
         if t.stride(-1) != 1:
             raise ValueError("innermost dimension must be contiguous")
@@ -198,7 +200,7 @@ def _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, ma
         lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
     d = _verify_desc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len, out, lse,
                      seq_status, split_keys, layout, partials_f32, parents, merge_mode, merge_wait_us,
-                     total_prefix_len)
+                     total_prefix_len, schedule, gang_size)
     return d, out, lse
 
 
@@ -210,18 +212,21 @@ def verify_plan(desc: VerifyDesc) -> VerifyPlan:
 
 def verify_attn(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
                 lse=None, workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
-                parents=None, merge_mode=0, merge_wait_us=0, total_prefix_len=0):
+                parents=None, merge_mode=0, merge_wait_us=0, total_prefix_len=0, schedule=0, gang_size=0):
     """Tree-verify attention.  c_kv [B, S, R] and k_pe [B, S, P] may be views of
     one fused [B, S, R+P] cache.  vis may be None when parents [B, q] int32 is
     given (the split kernel then derives the masks).  merge_mode 1 merges the
     splits inside the split kernel (when the launch fits the device); a
     caller-given workspace must then have been allocated zeroed (its merge
     state words; every call leaves their counts at zero).  Without a workspace
-    a zeroed one is allocated per call.  Returns
+    a zeroed one is allocated per call.  total_prefix_len (the sum of the
+    prefix lengths, 0 = unknown) sizes the launch; schedule 1 forces splits,
+    2 the balanced schedule (gang_size row tiles per gang, 0 = the library's
+    choice).  Returns
     (out [B, q, H, R], lse [B, q, H])."""
     d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
                                   out, lse, seq_status, split_keys, layout, partials_f32, parents, merge_mode,
-                                  merge_wait_us, total_prefix_len)
+                                  merge_wait_us, total_prefix_len, schedule, gang_size)
     p = verify_plan(d)
     if p.workspace_bytes and (workspace is None or workspace.numel() * workspace.element_size() < p.workspace_bytes):
         workspace = torch.zeros(p.workspace_bytes, dtype=torch.uint8, device=q_lat.device)
@@ -235,13 +240,13 @@ NOALLOC_MAX_WORKSPACE = 32 << 20              # KDT_NOALLOC_MAX_WORKSPACE
 
 def verify_attn_noalloc(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None, out=None,
                         lse=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
-                        parents=None, total_prefix_len=0):
+                        parents=None, total_prefix_len=0, schedule=0, gang_size=0):
     """kdt_verify_attn_noalloc: the same as verify_attn, with the library's own
     fixed device workspace (no allocation; calls on one GPU must not
     overlap).  out and lse should be given when nothing may be allocated."""
     d, out, lse = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
                                   out, lse, seq_status, split_keys, layout, partials_f32, parents,
-                                  total_prefix_len=total_prefix_len)
+                                  total_prefix_len=total_prefix_len, schedule=schedule, gang_size=gang_size)
     _check("kdt_verify_attn_noalloc", lib().kdt_verify_attn_noalloc(ctypes.byref(d), _stream(stream)))
     return out, lse
 
@@ -283,13 +288,13 @@ def tile_partials(rows_major):
 
 def verify_partials(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len=None,
                     workspace=None, seq_status=None, split_keys=0, stream=None, layout=0, partials_f32=False,
-                    parents=None, total_prefix_len=0):
+                    parents=None, total_prefix_len=0, schedule=0, gang_size=0):
     """Split stage only.  Returns (part_o, part_lse, plan): part_o
     [B, S, NBLK, 32*R] in the tiled layout (see untile_partials), bf16 for
     bf16 inputs unless partials_f32, else float32; part_lse float32 [B, S, q*H]."""
     d, _, _ = _verify_prepare(q_lat, q_pe, c_kv, k_pe, prefix_lens, vis, softmax_scale, max_prefix_len,
                               None, None, seq_status, split_keys, layout, partials_f32, parents,
-                              total_prefix_len=total_prefix_len)
+                              total_prefix_len=total_prefix_len, schedule=schedule, gang_size=gang_size)
     p = verify_plan(d)
     B, R, M, S = q_lat.shape[0], q_lat.shape[3], p.rows, p.max_splits
     need = max(int(p.partials_bytes), 1)
