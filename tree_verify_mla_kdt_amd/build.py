@@ -36,19 +36,43 @@ def flags() -> list[str]:
     ]
 
 
+# sources whose device assembly is checked for inline-asm MFMA hazards
+ASM_CHECKED = ["kdt_verify.hip"]
+
+
 def build(verbose: bool = False) -> str:
+    from . import asm_check
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *flags(), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
+    # the device assembly of the checked sources, compiled alongside
+    lib_flags = [f for f in flags() if f != "-shared"]
+    asm_jobs = []
+    for name in ASM_CHECKED:
+        out = os.path.join(HERE, f".{name}.s")
+        acmd = [hipcc(), *lib_flags, "-S", "--offload-device-only", os.path.join(CSRC, name), "-o", out]
+        asm_jobs.append((name, out, subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                      text=True)))
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (res.stderr or "").splitlines()
                     if "packed-fp32-ops" not in l)
     if res.returncode != 0:
+        for _, _, proc in asm_jobs:
+            proc.wait()
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    for name, out, proc in asm_jobs:
+        _, aerr = proc.communicate()
+        if proc.returncode != 0:
+            raise RuntimeError(f"hipcc -S {name} failed ({proc.returncode}):\n{aerr}")
+        with open(out) as f:
+            problems = asm_check.check(f.read())
+        os.remove(out)
+        if problems:
+            raise RuntimeError(f"{name}: inline-asm MFMA hazards in the compiled code:\n" + "\n".join(problems[:20]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -98,6 +98,27 @@ struct Mfma<__bf16> {
   __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // The score chain's form: the 32x32 tile it accumulates stays in ordinary
+  // VGPRs.  (The compiler's own form puts it in accumulation registers, which
+  // the output blocks fill, and moves one output block out and back every key
+  // tile.)  Written as inline asm, which the compiler's hazard checks do not
+  // see, so: the chain accumulates back to back into the same registers, which
+  // the hardware allows; the destination never overlaps the A or B operand
+  // (early clobber, or tied to C); and score_ready() must separate the last
+  // MFMA from the first vector read of the tile.
+  __device__ static __forceinline__ f32x16 mma_first_v(frag a, frag b) {
+    f32x16 d;
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+  }
+  __device__ static __forceinline__ void mma_acc_v(frag a, frag b, f32x16& c) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+  // 24 wait states: more than a 32x32x16 MFMA's result needs before a vector
+  // instruction reads it
+  __device__ static __forceinline__ void score_ready(f32x16& c) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+  }
   __device__ static __forceinline__ frag pack(const float* p) {
     frag f;
 #pragma unroll
@@ -958,6 +979,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
   // parity: every wave reads the current one after the barrier, the first
   // thread writes the next), so no register holds it across a piece.
   static_assert(!BAL || (!DIRECT && (CS == 1 || CS == 2)), "balanced schedule: layouts 1 and 2, partials");
+  constexpr bool SCORE_VGPR = KW == 8 && !(BAL && CS == 2);
   __shared__ BalWalk s_walk[BAL ? 2 : 1];
   bool more = true;
   if constexpr (BAL) {
@@ -1360,6 +1382,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+    // (bf16: the tile stays in VGPRs; see Mfma<__bf16>::mma_acc_v.  Not in
+    // the balanced 64-row kernel, where the compiler parks query fragments in
+    // accumulation registers and copies them back right before their MFMA.)
+    auto score_mma = [&](const frag& x, const frag& y, int j) __attribute__((always_inline)) {
+      if constexpr (SCORE_VGPR) {
+        if (j == 0) s = MM::mma_first_v(x, y);
+        else MM::mma_acc_v(x, y, s);
+      } else {
+        s = MM::mma(x, y, s);
+      }
+    };
 #pragma unroll
     for (int j = 0; j < NSTEP; ++j) {
       const frag cur = kf[j % QPF];
@@ -1369,9 +1402,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
         // the slot refilled now is the one this step consumes: take it first
         const frag qcur = j < NQF ? qf[j < NQF ? j : 0] : qq[j % QPF];
         if (j + QPF >= NQF && j + QPF < NSTEP) qq[(j + QPF) % QPF] = *qpe_src(j + QPF - NQF);
-        s = MM::mma(cur, qcur, s);
+        score_mma(cur, qcur, j);
       } else {
-        s = MM::mma(cur, qf[j], s);
+        score_mma(cur, qf[j], j);
       }
       fence_mem_mfma();
       if constexpr (KS) {
@@ -1384,6 +1417,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
         }
       }
     }
+    if constexpr (SCORE_VGPR) MM::score_ready(s);
     if constexpr (DS) {
       // add the partner's half of the contraction (the pair's waves hold the
       // same rows and keys; a + b is the same on both)
