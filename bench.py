@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -77,6 +78,12 @@ def parse():
                     help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases of a --kernel-only "
                          "--eager run and of a --copy-calibration run into "
                          "profiles/traffic_verify_split_<workload>.json")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
+                    help="no GPU: print a markdown summary of a rocprofv3 --kernel-trace --stats --output-format "
+                         "csv run of this script (its kernel_stats.csv and the bench line it printed)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DB",
+                    help="no GPU: print the split kernel's shader counters (means per dispatch) from rocprofv3 "
+                         "--pmc databases of --kernel-only --eager runs, with derived rates")
     ap.add_argument("--calibration-mb", type=int, default=256,
                     help="size of the --copy-calibration run that --write-traffic reads")
     return ap.parse_args()
@@ -127,6 +134,98 @@ def write_traffic(args):
     print(json.dumps(rec))
 
 
+def short_kernel_name(name: str) -> str:
+    """Readable form of a (possibly mangled) kernel name: template
+    arguments of the split and merge kernels spelled out."""
+    m = re.match(r"_ZN3kdt19verify_split_kernelI(DF16b|f)Li(\d+)ELi(\d+)ELb([01])ELi(\d)ELb([01])E", name)
+    if m:
+        t, R, P, direct, cs, bal = m.groups()
+        t = "bf16" if t == "DF16b" else "f32"
+        return (f"verify_split_kernel<{t}, R={R}, P={P}, {'direct' if direct == '1' else 'partials'}, "
+                f"layout {cs}{', balanced' if bal == '1' else ''}>")
+    m = re.match(r"_ZN3kdt12merge_kernelI(DF16b|f)(DF16b|f)Lb([01])ELb([01])E", name)
+    if m:
+        o, pt, wide, gate = m.groups()
+        dt = lambda x: "bf16" if x == "DF16b" else "f32"
+        return (f"merge_kernel<out {dt(o)}, partials {dt(pt)}{', wide' if wide == '1' else ''}"
+                f"{', gated' if gate == '1' else ''}>")
+    m = re.match(r"_ZN3kdt18absorb_gemm_kernelILi(\d+)ELi(\d+)E", name)
+    if m:
+        return f"absorb_gemm_kernel<{m.group(1)}, {m.group(2)}>"
+    return name.split("(")[0].replace("void ", "")
+
+
+def trace_summary(args):
+    import csv
+    stats_csv, log = args.trace_summary
+    rows = list(csv.DictReader(open(stats_csv)))
+    bench = None
+    for line in open(log):
+        if line.startswith('{"metric"'):
+            bench = json.loads(line)
+    print("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    if bench:
+        c, rf = bench["config"], bench["roofline"]
+        print()
+        print(f"Bench line of the same run: step {bench['ms_per_step'] * 1e3:.1f} us, "
+              f"{bench['value']:.4g} {bench['unit']}; one kdt_verify_attn call {bench['verify_attn_us']['median']:.1f} us "
+              f"(median); split kernel {rf['kernel_ms'] * 1e3:.1f} us by HIP events "
+              f"({rf['bound']} bound: {rf['achieved']:.1f} of {rf['peak']:.0f} {rf['unit']}, "
+              f"frac {rf['frac']:.3f}); layout {c['layout']}, {c['splits']} splits of {c['split_keys']} keys, "
+              f"schedule {c.get('schedule', 'splits')}, partials {c['partials']}, merge {c['merge']}.")
+
+
+def pmc_means(db: str, kernel_substr: str) -> dict:
+    """Every counter of a rocprofv3 --pmc database: mean over the dispatches
+    of the matching kernels of the counter summed over its instances."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    names = {r[0]: r[1] for r in con.execute("select dispatch_id, name from kernels")}
+    per = {}
+    for cn, did, v in con.execute("select counter_name, dispatch_id, counter_value from pmc_events"):
+        if kernel_substr in names.get(did, ""):
+            per.setdefault(cn, {}).setdefault(did, 0.0)
+            per[cn][did] += float(v)
+    return {cn: sum(d.values()) / len(d) for cn, d in per.items()}
+
+
+def counter_summary(args):
+    c = {}
+    for db in args.counter_summary:
+        c.update(pmc_means(db, "verify_split_kernel"))
+    waves = c.get("SQ_WAVES", 0.0)
+    print("| counter | mean per dispatch | per wave |")
+    print("|---|---|---|")
+    for k in sorted(c):
+        print(f"| {k} | {c[k]:.4g} | {c[k] / waves:.4g} |" if waves else f"| {k} | {c[k]:.4g} | |")
+    print()
+    if "GRBM_GUI_ACTIVE" in c:
+        cyc = c["GRBM_GUI_ACTIVE"] / 8.0
+        print(f"* kernel cycles (GRBM_GUI_ACTIVE per XCD): {cyc:.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            print(f"* MFMA pipe busy over the whole kernel: SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x 1024 SIMDs)"
+                  f" = {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.3f}")
+    if waves and "SQ_INSTS_MFMA" in c:
+        print(f"* MFMA instructions per wave: {c['SQ_INSTS_MFMA'] / waves:.1f}")
+    if waves and "SQ_INSTS_VALU" in c:
+        print(f"* instructions per wave: {c['SQ_INSTS_VALU'] / waves:.0f} VALU (MFMA included), "
+              f"{c.get('SQ_INSTS_SALU', 0) / waves:.0f} SALU, {c.get('SQ_INSTS_LDS', 0) / waves:.0f} LDS")
+    if "SQ_WAVE_CYCLES" in c:
+        wc = c["SQ_WAVE_CYCLES"]
+        parts = []
+        for k, what in (("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_WAIT_ANY", "waiting on any dependency"),
+                        ("SQ_WAIT_INST_LDS", "waiting to issue an LDS instruction")):
+            if k in c:
+                parts.append(f"{what} {c[k] / wc:.3f}")
+        print("* share of wave cycles: " + "; ".join(parts))
+    if "SQ_LDS_BANK_CONFLICT" in c:
+        print(f"* LDS bank conflicts: {c['SQ_LDS_BANK_CONFLICT']:.0f}")
+
+
 def source_hash() -> str:
     """Hash of the sources the split-attention kernel is compiled from: stored
     traffic counts are used only while this still matches."""
@@ -153,6 +252,12 @@ def main():
     args = parse()
     if args.write_traffic:
         write_traffic(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
+        return
+    if args.counter_summary:
+        counter_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
