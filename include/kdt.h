@@ -218,17 +218,19 @@ typedef struct {
  * (so a merge over all max_splits splits is always right).
  * Balanced schedule (gang_size > 0; stream-K style): the row tiles of a
  * sequence form groups of gang_size consecutive tiles, and every (sequence,
- * group) pair is a stream of ceil((prefix_lens[b] + q_len) / 32) key-tile
- * units (one for a sequence with an invalid prefix length).  The streams, laid
- * end to end in sequence order, U units in all, are cut into ranges of A =
- * max(ceil(U / gangs), ceil(T_max / (max_splits - 1))) units (T_max the
- * longest stream among valid sequences; A is at most the key tiles one piece
- * may span); range j goes to gang j mod gangs, a gang being gang_size
- * workgroups that each take one row tile of the group and move through the
- * same keys together.  The grid is gangs * gang_size workgroups, one per
- * compute unit, so the work is even however the lengths are mixed.  The part
- * of a stream inside range j is partial j - floor(s / A) of the stream's
- * rows, s its first unit.  Merge such partials with split_keys == 0.
+ * group) pair is a stream of piece_units units (the start-up of its first
+ * piece) followed by T_b = ceil((prefix_lens[b] + q_len) / 32) key-tile units
+ * (a sequence with an invalid prefix length: one unit).  The streams, laid end
+ * to end in sequence order, U units in all, are cut into ranges of A =
+ * max(ceil(U / gangs), ceil(T_max / (max_splits - 1))) units (T_max the most
+ * key tiles of a valid sequence; A is at most the key tiles one piece may
+ * span); range j goes to gang j mod gangs, a gang being gang_size workgroups
+ * that each take one row tile of the group and move through the same keys
+ * together.  The grid is gangs * gang_size workgroups, one per compute unit,
+ * so the work is even however the lengths are mixed.  The key tiles of a
+ * stream inside range j are partial j - floor(r / A) of the stream's rows, r
+ * its first key-tile unit; a range holding only start-up units of a stream
+ * holds no piece of it.  Merge such partials with split_keys == 0.
  * Merge state (when the merge is fused): one 32-bit word per row tile, uint32
  * [B, NRT] at counter_offset, NRT = ceil(q_len*H / rows per workgroup of the
  * layout): two counts and a generation bit.  The words must be zero before
@@ -253,6 +255,8 @@ typedef struct {
   int64_t counter_offset;      /* bytes into the workspace of the merge counters */
   int32_t gang_size;           /* > 0: the balanced schedule (above), row tiles per gang; 0: splits */
   int32_t gangs;               /* balanced schedule: gangs in the launch */
+  int32_t piece_units;         /* balanced schedule: start-up units charged to every stream (below) */
+  int32_t reserved;
 } kdt_verify_plan;
 
 int kdt_verify_get_plan(const kdt_verify_desc* d, kdt_verify_plan* plan);

@@ -140,7 +140,8 @@ def test_balanced_schedule_plan():
     assert p.direct == 0 and p.tiles_max == 0 and p.fused_merge == 0 and p.max_splits >= 2
     T = -(-(4096 + 65) // 32)
     n_rt = -(-(65 * 16) // (128 if p.layout == 1 else 64))
-    U = -(-n_rt // p.gang_size) * T
+    assert p.piece_units > 0
+    U = -(-n_rt // p.gang_size) * (T + p.piece_units)
     A = -(-U // p.gangs)
     assert p.max_splits == max(2, -(-T // A) + 1)
     for g in (1, 3, 9):

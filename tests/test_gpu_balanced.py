@@ -40,23 +40,25 @@ def _check_full(inp, out, lse, what):
     check_close(inp.cfg.dtype, to_f64(out), ro, lse.cpu().numpy().astype(np.float64), rl, what)
 
 
-def balanced_ranges(lens, q, n_rt, gang, gangs, max_splits, max_prefix_len, capacity):
+def balanced_ranges(lens, q, n_rt, gang, gangs, max_splits, max_prefix_len, capacity, piece_units):
     """The balance rule, restated: [(b, grp, split, first tile, end tile)] for
     every piece (end tiles clipped to the stream)."""
     ceil = lambda x, y: -(-x // y)
     bad = [L < 0 or L > max_prefix_len or L + q > capacity for L in lens]
     T = [1 if bd else ceil(L + q, 32) for L, bd in zip(lens, bad)]
+    c = [0 if bd else piece_units for bd in bad]            # start-up units before the key tiles
     n_grp = ceil(n_rt, gang)
-    U = n_grp * sum(T)
+    U = n_grp * (sum(T) + sum(c))
     tmax = max([t for t, bd in zip(T, bad) if not bd] + [1])
     A = max(ceil(U, gangs), ceil(tmax, max_splits - 1), 1)
     out, st = [], 0
     for b, t in enumerate(T):
         for grp in range(n_grp):
-            for j in range(st // A, (st + t - 1) // A + 1):
-                s0, s1 = max(st, j * A), min(st + t, (j + 1) * A)
-                out.append((b, grp, j - st // A, s0 - st, s1 - st))
-            st += t
+            r = st + c[b]                                  # first key-tile unit
+            for j in range(r // A, (r + t - 1) // A + 1):
+                s0, s1 = max(r, j * A), min(r + t, (j + 1) * A)
+                out.append((b, grp, j - r // A, s0 - r, s1 - r))
+            st += c[b] + t
     return out, A
 
 
@@ -172,8 +174,9 @@ def test_partials_follow_the_balance_rule_and_merge_over_all_slots(layout, gang)
     q, H = cfg.q_len, cfg.H
     BM = 128 if p.layout == 1 else 64
     n_rt = -(-M // BM)
+    assert p.piece_units > 0
     pieces, _ = balanced_ranges([int(x) for x in inp.prefix_lens], q, n_rt, p.gang_size, p.gangs, S,
-                                g.max_prefix_len, g.c_kv.shape[1])
+                                g.max_prefix_len, g.c_kv.shape[1], p.piece_units)
     po = kdt.untile_partials(part_o, M).float().cpu().numpy().astype(np.float64)
     pl = part_lse.cpu().numpy().astype(np.float64)
     vis, _ = oracle.build_visibility(inp.parents)

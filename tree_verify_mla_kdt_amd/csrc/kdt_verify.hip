@@ -170,6 +170,7 @@ struct VerifyArgs {
   // keys together, n_grp = such groups per sequence, gangs = gangs in the
   // launch (the grid is gangs * gang workgroups)
   int gang, n_grp, gangs;
+  int piece_units;      // balanced schedule: units a stream's start-up costs, in key tiles
   int span_keys;        // the most keys of one piece (cache rows one buffer descriptor spans)
   int q_rows_uniform;   // query rows m = t * H + h sit at one byte stride (q_lat and q_pe)
   int part_bf16;        // partial outputs in bf16 (else float32)
@@ -664,11 +665,15 @@ struct PieceDesc {
 __device__ __forceinline__ bool len_bad(const VerifyArgs& a, int L) {
   return L < 0 || L > a.max_prefix_len || (int64_t)L + a.q > a.capacity;
 }
-// units of one stream of sequence b: its key tiles (one for a sequence with
-// an invalid prefix length, whose workgroups flag it and write the empty
-// result)
-__device__ __forceinline__ int units_of(const VerifyArgs& a, int L) {
+// key tiles of a sequence of prefix length L (one for an invalid length,
+// whose workgroups flag it and write the empty result)
+__device__ __forceinline__ int tiles_of(const VerifyArgs& a, int L) {
   return len_bad(a, L) ? 1 : (L + a.q - 1) / kBN + 1;
+}
+// units of one stream of sequence b: its start-up (piece_units) and its key
+// tiles; a sequence with an invalid length is one unit
+__device__ __forceinline__ int units_of(const VerifyArgs& a, int L) {
+  return len_bad(a, L) ? 1 : a.piece_units + (L + a.q - 1) / kBN + 1;
 }
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)x);
@@ -678,20 +683,22 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 
 // Work-balanced schedule (stream-K style).  The row tiles of a sequence are
 // cut into n_grp groups of `gang` (the last may be short), and each
-// (sequence, group) pair is a stream of T_b units, one per key tile of the
-// sequence.  The streams are laid end to end, sequence-major, U units in
-// all, and gang j of the launch's G gangs takes units [j A, min(U, (j + 1) A))
-// with A = ceil(U / G), raised so that no stream meets more than max_splits
-// gangs (A >= ceil(T_max / (max_splits - 1))) and capped at span_keys / 32
-// (then gang j also takes the ranges of gangs j + G, j + 2 G, ... after its
-// own).  A gang is `gang` workgroups that are consecutive after xcd_remap,
+// (sequence, group) pair is a stream of units: piece_units for the start-up
+// its first piece costs, then one per key tile of the sequence.  The
+// streams are laid end to end, sequence-major, U units in all, and gang j of
+// the launch's G gangs takes units [j A, min(U, (j + 1) A)) with A =
+// ceil(U / G), raised so that no stream's key tiles meet more than
+// max_splits gangs (A >= ceil(T_max / (max_splits - 1)), T_max the most key
+// tiles of a sequence) and capped at span_keys / 32 (then gang j also takes
+// the ranges of gangs j + G, j + 2 G, ... after its own).  A range that ends
+// inside a stream's start-up units holds no piece of it.  A gang is `gang` workgroups that are consecutive after xcd_remap,
 // so they share an XCD and its L2: member m does row tile grp * gang + m of
 // every stream the gang's range meets, so the members read the same keys at
 // about the same time.  Where a range crosses from one stream into the
 // next, its workgroups finish one piece (one partial) and start the next.
 // The piece of a stream that gang j does is the stream's partial
-// j - floor(first unit / A), and a stream has floor(last unit / A) -
-// floor(first unit / A) + 1 of them.  Every wave walks the ranges itself
+// j - floor(r / A), r the stream's first key-tile unit, and a stream has
+// floor(last unit / A) - floor(r / A) + 1 of them.  Every wave walks the ranges itself
 // from the prefix lengths (64 sequences per pass); all values are uniform.
 struct BalWalk {
   int64_t A, U;    // units per gang, units in all
@@ -738,7 +745,7 @@ __device__ __forceinline__ bool bal_init(const VerifyArgs& a, BalWalk& w, int la
     const int j = j0 + lane;
     const int L = j < a.B ? a.prefix_lens[j] : 0;
     int64_t c = j < a.B ? units_of(a, L) : 0;
-    int tm = c;
+    int tm = j < a.B ? tiles_of(a, L) : 1;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       c += __shfl_xor(c, d);
@@ -786,15 +793,18 @@ __device__ __forceinline__ bool bal_next(const VerifyArgs& a, BalWalk& w, int la
     const int64_t pe = min(w.e, w.st + w.T);
     w.s = pe;
     const int rt = w.grp * a.gang + w.member;
-    if (rt >= a.n_rt) continue;
+    const bool bad = len_bad(a, w.L);
+    const int64_t rs = w.st + (bad ? 0 : a.piece_units);    // the stream's first key-tile unit
+    if (rt >= a.n_rt || pe <= rs) continue;
+    const int64_t k0 = max(s0, rs);
     pc.b = w.b;
     pc.rt = rt;
     pc.L = w.L;
     pc.known = true;
-    pc.split = (int)(s0 / w.A - w.st / w.A);
-    pc.ns = (int)((w.st + w.T - 1) / w.A - w.st / w.A + 1);
-    pc.k_begin = (int)(s0 - w.st) * kBN;
-    pc.k_end = len_bad(a, w.L) ? 1 : min(w.L + a.q, (int)(pe - w.st) * kBN);
+    pc.split = (int)(k0 / w.A - rs / w.A);
+    pc.ns = (int)((w.st + w.T - 1) / w.A - rs / w.A + 1);
+    pc.k_begin = (int)(k0 - rs) * kBN;
+    pc.k_end = bad ? 1 : min(w.L + a.q, (int)(pe - rs) * kBN);
     return true;
   }
 }
@@ -1462,6 +1472,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = s[v];
     if (kt + kBN > L || kt + kBN > k_end) {   // only tiles reaching the tree or the split end
+      // (an empty volatile asm: without it the compiler turns this branch
+      // into selects that every tile then executes, some 200 instructions
+      // between the score and the value MFMAs)
+      asm volatile("");
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kk = kt + c_row(v, hh);
@@ -1471,21 +1485,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
         sv[v] = (kk < k_end && tree_ok) ? sv[v] : -INFINITY;
       }
     }
-    float mx = sv[0];
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float x = sv[0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = xhalf_max(mx) * a.scale_log2;
-    m_max = fmaxf(m_max, mx);
+      for (int v = 1; v < 16; ++v) x = fmaxf(x, sv[v]);
+      return xhalf_max(x) * a.scale_log2;
+    };
     // Only tiles where some row of the wave still lacks its reference take
-    // this (uniform) branch; elsewhere the weights below depend on the fixed
-    // reference alone and need not wait for the row max, which then only
-    // feeds the check that follows.
+    // this (uniform) branch: the row's running max, this tile included, sets
+    // it.  Elsewhere the weights depend on the fixed reference alone.
     if (__any(m_ref == -INFINITY)) {
-      if (m_ref == -INFINITY) m_ref = m_max;  // first visible key of this row
-    }
-    if (!dead && __any(m_max > m_ref + kRefSlack)) {
-      dead = true;
-      s_dead = 1;
+      const float mx0 = tile_max();
+      if (m_ref == -INFINITY) m_ref = fmaxf(m_max, mx0);   // first visible key of this row
     }
     const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
     float p[16];
@@ -1494,6 +1505,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
       p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], a.scale_log2, -m_use));
       l_run += p[v];
     }
+    // The running max and the check against the reference feed no weight of
+    // this tile, and no branch: they can overlap the value MFMAs.  A wave
+    // whose scores outgrow its reference records it in `dead`, which is read
+    // after the last tile.
+    m_max = fmaxf(m_max, tile_max());
+    dead = dead || __any(m_max > m_ref + kRefSlack);
 
     // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]; the value operand of
     // step i + VPF is read while step i's MFMA is issued (the first VPF were
@@ -1520,6 +1537,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
+      if (dead) s_dead = 1;
       __syncthreads();
       if (s_dead == 0) break;                 // common case: no redo
       // Depth split: every wave takes part in the score exchange (a
@@ -1910,10 +1928,21 @@ static double launch_cost(int64_t wgs, int64_t splits, int64_t tiles, int R, int
 // one read through their XCD's L2; measured: gangs of one row tile, every
 // workgroup reading its keys alone, ran 6-8% slower than gangs of 5 to 11).
 // Same constants as launch_cost otherwise.
+static double tile_time(int R, int P, int layout) {
+  const int rows = layout_rows(layout);
+  return layout == 4 ? 1.7 * 1.1 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+}
+
+// Balanced schedule: the start-up and epilogue of a piece (measured 10-11 us
+// in a full launch: the query loads of every workgroup at once dominate) in
+// key tiles; every stream is charged this many units before its key tiles.
+constexpr double kPieceUs = 10.0;
+static int piece_units(int R, int P, int layout) { return (int)std::ceil(kPieceUs / tile_time(R, P, layout)); }
+
 static double balanced_cost(int64_t A, double pieces, int64_t parts, int64_t splits, int64_t reads,
                             double cache_bytes, int R, int P, int layout, int part_bytes) {
   const int rows = layout_rows(layout);
-  const double t_tile = layout == 4 ? 1.7 * 1.1 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
+  const double t_tile = tile_time(R, P, layout);
   const double t_start = layout == 4 ? 6.0 : 4.0;
   const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 3.0, t_merge_batch = 2.0;
@@ -1994,11 +2023,11 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
         if (d->gang_size && g != d->gang_size) continue;
         const int64_t G = cus / g;
         const int64_t n_grp = (n_rt + g - 1) / g;
-        const int64_t U = n_grp * total_tiles;
+        const int64_t U = n_grp * (total_tiles + (int64_t)d->B * piece_units(d->R, d->P, layout));
         const int64_t A = std::min(lim, std::max<int64_t>(1, (U + G - 1) / G));
         const int64_t S = std::max<int64_t>({2, (tiles_max + A - 1) / A + 1, (tiles_max + lim - 1) / lim + 1});
         const int64_t streams = (int64_t)d->B * n_grp;
-        const double pieces = 1.0 + (double)streams / (double)G;
+        const double pieces = 1.0;              // (later pieces' start-ups are inside A)
         const int64_t parts = std::min(G + streams, streams * S) * g;
         const double kv_bytes = (double)total_keys * (double)(d->R + d->P) * elem_size(d->dtype);
         const double c = balanced_cost(A, pieces, parts, S, n_grp, kv_bytes, d->R, d->P, layout,
@@ -2021,6 +2050,7 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
   p->part_dtype = part_dtype;
   p->gang_size = (int32_t)bal_g;
   p->gangs = (int32_t)bal_G;
+  p->piece_units = bal_g ? piece_units(d->R, d->P, best_layout) : 0;
   if (bal_g) sk = bal_A * kBN;
   if (sk <= 0) return KDT_ERR_UNSUPPORTED;   // no split size fits the row offsets
   const int64_t ns = bal_g ? bal_S : (n_max + sk - 1) / sk;
@@ -2095,6 +2125,7 @@ static VerifyArgs make_args(const kdt_verify_desc* d, const kdt_verify_plan& p, 
   a.compact = p.tiles_max > 0 && d->B > 1;
   a.gang = p.gang_size;
   a.gangs = p.gangs;
+  a.piece_units = p.piece_units;
   a.n_grp = p.gang_size > 0 ? (a.n_rt + p.gang_size - 1) / p.gang_size : 0;
   {
     // a piece's cache rows of either region stay under 2^31 bytes from its first

@@ -51,6 +51,7 @@ class VerifyPlan(ctypes.Structure):
         ("layout", _c_i32), ("part_dtype", _c_i32), ("part_o_offset", _c_i64), ("part_lse_offset", _c_i64),
         ("workspace_bytes", ctypes.c_size_t), ("partials_bytes", ctypes.c_size_t), ("fused_merge", _c_i32),
         ("tiles_max", _c_i32), ("counter_offset", _c_i64), ("gang_size", _c_i32), ("gangs", _c_i32),
+        ("piece_units", _c_i32), ("reserved", _c_i32),
     ]
 
 
