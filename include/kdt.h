@@ -230,7 +230,10 @@ typedef struct {
  * so the work is even however the lengths are mixed.  The key tiles of a
  * stream inside range j are partial j - floor(r / A) of the stream's rows, r
  * its first key-tile unit; a range holding only start-up units of a stream
- * holds no piece of it.  Merge such partials with split_keys == 0.
+ * holds no piece of it.  Merge such partials with split_keys == 0.  The walk
+ * counts units in 32 bits: a batch whose units could exceed 2e9 (B times the
+ * longest stream) is not given the balanced schedule (KDT_ERR_UNSUPPORTED when
+ * it is asked for).
  * Merge state (when the merge is fused): one 32-bit word per row tile, uint32
  * [B, NRT] at counter_offset, NRT = ceil(q_len*H / rows per workgroup of the
  * layout): two counts and a generation bit.  The words must be zero before

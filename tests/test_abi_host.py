@@ -152,6 +152,10 @@ def test_balanced_schedule_plan():
     assert _plan(_desc(schedule=3))[0] == 1
     assert _plan(_desc(gang_size=-1))[0] == 1
     assert _plan(_desc(schedule=2, layout=4))[0] == 2                   # layouts 1 and 2 only
+    # units counted in 32 bits: 4096 sequences of up to 20M keys are too many
+    assert _plan(_desc(schedule=2, B=4096, max_prefix_len=20_000_000, capacity=20_000_065))[0] == 2
+    rc, p = _plan(_desc(B=4096, max_prefix_len=20_000_000, capacity=20_000_065))
+    assert rc == 0 and p.gang_size == 0
     rc, p = _plan(_desc(schedule=1))
     assert rc == 0 and p.gang_size == 0
 

@@ -675,11 +675,6 @@ __device__ __forceinline__ int tiles_of(const VerifyArgs& a, int L) {
 __device__ __forceinline__ int units_of(const VerifyArgs& a, int L) {
   return len_bad(a, L) ? 1 : a.piece_units + (L + a.q - 1) / kBN + 1;
 }
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
 
 // Work-balanced schedule (stream-K style).  The row tiles of a sequence are
 // cut into n_grp groups of `gang` (the last may be short), and each
@@ -701,25 +696,27 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // floor(last unit / A) - floor(r / A) + 1 of them.  Every wave walks the ranges itself
 // from the prefix lengths (64 sequences per pass); all values are uniform.
 struct BalWalk {
-  int64_t A, U;    // units per gang, units in all
-  int64_t s, e;    // next unit, end of the current range
-  int64_t st;      // first unit of the current stream
+  int A, U;        // units per gang, units in all (the host keeps U below 2^31)
+  int s, e;        // next unit, end of the current range
+  int st;          // first unit of the current stream
   int j;           // current gang
   int b, grp, L, T;  // current stream: sequence, row-tile group, prefix length, units
   int member;
 };
 
+__device__ __forceinline__ int udiv(int x, int y) { return (int)((uint32_t)x / (uint32_t)y); }
+
 // the stream holding unit w.s
 __device__ __forceinline__ void bal_locate(const VerifyArgs& a, BalWalk& w, int lane) {
-  int64_t base = 0;     // units of the sequences before this pass's
+  int base = 0;     // units of the sequences before this pass's
   for (int j0 = 0; j0 < a.B; j0 += 64) {
     const int j = j0 + lane;
     const int L = j < a.B ? a.prefix_lens[j] : 0;
-    const int64_t c = j < a.B ? (int64_t)a.n_grp * units_of(a, L) : 0;
-    int64_t incl = c;
+    const int c = j < a.B ? a.n_grp * units_of(a, L) : 0;
+    int incl = c;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int64_t y = __shfl_up(incl, d);
+      const int y = __shfl_up(incl, d);
       if (lane >= d) incl += y;
     }
     const uint64_t past = __ballot(base + incl > w.s);
@@ -728,44 +725,44 @@ __device__ __forceinline__ void bal_locate(const VerifyArgs& a, BalWalk& w, int 
       w.b = j0 + k;
       w.L = __builtin_amdgcn_readfirstlane(__shfl(L, k));
       w.T = units_of(a, w.L);
-      const int64_t sb = uniform64(base + __shfl(incl, k) - __shfl(c, k));
-      w.grp = (int)((w.s - sb) / w.T);
-      w.st = sb + (int64_t)w.grp * w.T;
+      const int sb = __builtin_amdgcn_readfirstlane(base + __shfl(incl, k) - __shfl(c, k));
+      w.grp = udiv(w.s - sb, w.T);
+      w.st = sb + w.grp * w.T;
       return;
     }
-    base += uniform64(__shfl(incl, 63));
+    base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
   }
 }
 
 // Sets up workgroup blockIdx.x's walk; false if it has no work.
 __device__ __forceinline__ bool bal_init(const VerifyArgs& a, BalWalk& w, int lane) {
-  int64_t useq = 0;
+  int useq = 0;
   int tmax = 1;
   for (int j0 = 0; j0 < a.B; j0 += 64) {
     const int j = j0 + lane;
     const int L = j < a.B ? a.prefix_lens[j] : 0;
-    int64_t c = j < a.B ? units_of(a, L) : 0;
+    int c = j < a.B ? units_of(a, L) : 0;
     int tm = j < a.B ? tiles_of(a, L) : 1;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       c += __shfl_xor(c, d);
       tm = max(tm, __shfl_xor(tm, d));
     }
-    useq += uniform64(c);
+    useq += __builtin_amdgcn_readfirstlane(c);
     tmax = max(tmax, __builtin_amdgcn_readfirstlane(tm));
   }
-  w.U = (int64_t)a.n_grp * useq;
-  const int64_t G = a.gangs;
-  int64_t A = (w.U + G - 1) / G;
-  A = max(A, (int64_t)((tmax + a.max_splits - 2) / (a.max_splits - 1)));
-  A = min(A, (int64_t)(a.span_keys / kBN));
-  w.A = max(A, (int64_t)1);
+  w.U = a.n_grp * useq;
+  const int G = a.gangs;
+  int A = udiv(w.U + G - 1, G);
+  A = max(A, udiv(tmax + a.max_splits - 2, a.max_splits - 1));
+  A = min(A, a.span_keys / kBN);
+  w.A = max(A, 1);
   const int u = xcd_remap(blockIdx.x, gridDim.x);
-  w.j = u / a.gang;
+  w.j = udiv(u, a.gang);
   w.member = u - w.j * a.gang;
-  w.s = (int64_t)w.j * w.A;
-  if (w.s >= w.U) return false;
-  w.e = min(w.U, w.s + w.A);
+  if ((int64_t)w.j * w.A >= w.U) return false;
+  w.s = w.j * w.A;
+  w.e = min(w.U - w.s, w.A) + w.s;
   bal_locate(a, w, lane);
   return true;
 }
@@ -776,9 +773,9 @@ __device__ __forceinline__ bool bal_next(const VerifyArgs& a, BalWalk& w, int la
   while (true) {
     if (w.s >= w.e) {
       w.j += a.gangs;
-      w.s = (int64_t)w.j * w.A;
-      if (w.s >= w.U) return false;
-      w.e = min(w.U, w.s + w.A);
+      if ((int64_t)w.j * w.A >= w.U) return false;
+      w.s = w.j * w.A;
+      w.e = min(w.U - w.s, w.A) + w.s;
       bal_locate(a, w, lane);
     } else if (w.s >= w.st + w.T) {
       w.st += w.T;
@@ -789,22 +786,22 @@ __device__ __forceinline__ bool bal_next(const VerifyArgs& a, BalWalk& w, int la
         w.T = units_of(a, w.L);
       }
     }
-    const int64_t s0 = w.s;
-    const int64_t pe = min(w.e, w.st + w.T);
+    const int s0 = w.s;
+    const int pe = min(w.e, w.st + w.T);
     w.s = pe;
     const int rt = w.grp * a.gang + w.member;
     const bool bad = len_bad(a, w.L);
-    const int64_t rs = w.st + (bad ? 0 : a.piece_units);    // the stream's first key-tile unit
+    const int rs = w.st + (bad ? 0 : a.piece_units);    // the stream's first key-tile unit
     if (rt >= a.n_rt || pe <= rs) continue;
-    const int64_t k0 = max(s0, rs);
+    const int k0 = max(s0, rs);
     pc.b = w.b;
     pc.rt = rt;
     pc.L = w.L;
     pc.known = true;
-    pc.split = (int)(k0 / w.A - rs / w.A);
-    pc.ns = (int)((w.st + w.T - 1) / w.A - rs / w.A + 1);
-    pc.k_begin = (int)(k0 - rs) * kBN;
-    pc.k_end = bad ? 1 : min(w.L + a.q, (int)(pe - rs) * kBN);
+    pc.split = udiv(k0, w.A) - udiv(rs, w.A);
+    pc.ns = udiv(w.st + w.T - 1, w.A) - udiv(rs, w.A) + 1;
+    pc.k_begin = (k0 - rs) * kBN;
+    pc.k_end = bad ? 1 : min(w.L + a.q, (pe - rs) * kBN);
     return true;
   }
 }
@@ -1019,11 +1016,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
     BalWalk walk;
     {
       const BalWalk& sw = s_walk[iter & 1];
-      walk.A = uniform64(sw.A);
-      walk.U = uniform64(sw.U);
-      walk.s = uniform64(sw.s);
-      walk.e = uniform64(sw.e);
-      walk.st = uniform64(sw.st);
+      walk.A = __builtin_amdgcn_readfirstlane(sw.A);
+      walk.U = __builtin_amdgcn_readfirstlane(sw.U);
+      walk.s = __builtin_amdgcn_readfirstlane(sw.s);
+      walk.e = __builtin_amdgcn_readfirstlane(sw.e);
+      walk.st = __builtin_amdgcn_readfirstlane(sw.st);
       walk.j = __builtin_amdgcn_readfirstlane(sw.j);
       walk.b = __builtin_amdgcn_readfirstlane(sw.b);
       walk.grp = __builtin_amdgcn_readfirstlane(sw.grp);
@@ -2024,6 +2021,8 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
         const int64_t G = cus / g;
         const int64_t n_grp = (n_rt + g - 1) / g;
         const int64_t U = n_grp * (total_tiles + (int64_t)d->B * piece_units(d->R, d->P, layout));
+        // (the walk counts units in 32 bits: every sequence at its longest must fit)
+        if ((double)n_grp * d->B * (double)(tiles_max + piece_units(d->R, d->P, layout)) > 2.0e9) continue;
         const int64_t A = std::min(lim, std::max<int64_t>(1, (U + G - 1) / G));
         const int64_t S = std::max<int64_t>({2, (tiles_max + A - 1) / A + 1, (tiles_max + lim - 1) / lim + 1});
         const int64_t streams = (int64_t)d->B * n_grp;
@@ -2043,8 +2042,12 @@ static int make_plan(const kdt_verify_desc* d, kdt_verify_plan* p) {
         }
       }
     }
-    // (on request: layouts 1 and 2 only, and a gang no larger than the row tiles)
-    if (d->schedule == 2 && !bal_g) return d->layout > 2 ? KDT_ERR_UNSUPPORTED : KDT_ERR_INVALID_ARG;
+    // (on request: layouts 1 and 2 only, a gang no larger than the row tiles,
+    // and lengths the walk can count in 32 bits)
+    if (d->schedule == 2 && !bal_g) {
+      const bool too_long = (double)d->B * (double)(tiles_max + piece_units(d->R, d->P, 1)) > 2.0e9;
+      return d->layout > 2 || too_long ? KDT_ERR_UNSUPPORTED : KDT_ERR_INVALID_ARG;
+    }
   }
   p->layout = best_layout;
   p->part_dtype = part_dtype;
