@@ -1877,18 +1877,6 @@ static int validate(const kdt_verify_desc* d) {
 static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 
 // Modelled time (microseconds) of one launch, split kernel plus merge, for a
-// layout and split size.  Workgroups run one per compute unit, so G of them
-// take ceil(G / kCU) rounds; a round costs its key tiles plus a start-up (the
-// burst of query and first-tile loads), every partial costs its write and its
-// read in the merge, and splitting at all adds the merge launch plus one
-// memory round trip per batch of splits the merge loads at once (sixteen per
-// wave; up to sixty-four when a workgroup's four waves share the splits of
-// one item).  The constants are fitted to a measured grid of split sizes and
-// layouts over six workloads at R = 512, P = 64 (a 128-row tile of 32 keys
-// about 1.7 us, a start-up about 4 us, a 128-row float32 partial about 0.15 us)
-// and scale with the contraction work of one wave and with the bytes a
-// partial holds.
-// Modelled time (microseconds) of one launch, split kernel plus merge, for a
 // layout, split size and count: `wgs` split workgroups with work (one per
 // compute unit, so ceil(wgs / kCU) rounds) of at most `tiles` key tiles each;
 // a round costs its tiles plus a start-up (the burst of query and first-tile
@@ -1898,8 +1886,10 @@ static int layout_rows(int layout) { return layout >= 2 ? kBM / 2 : kBM; }
 // when a workgroup's four waves share the splits of one item).  The constants
 // are fitted to a measured grid of split sizes and layouts over six workloads
 // at R = 512, P = 64 (a 128-row tile of 32 keys about 1.7 us, a start-up about
-// 4 us, a 128-row float32 partial about 0.15 us) and scale with the
-// contraction work of one wave and with the bytes a partial holds.
+// 4 us) and scale with the contraction work of one wave and with the bytes a
+// partial holds.  The partial's cost, 0.10 us for 128 float32 rows, was
+// refitted once partials were bf16 and the loop faster: at max_budget 14
+// splits of 320 keys then beat 11 of 384 (step 34.7 against 35.5 us).
 static double launch_cost(int64_t wgs, int64_t splits, int64_t tiles, int R, int P, int layout, int part_bytes) {
   const int rows = layout_rows(layout);
   // layout 4: two key tiles per step, each wave doing layout 1's work for its
@@ -1907,7 +1897,7 @@ static double launch_cost(int64_t wgs, int64_t splits, int64_t tiles, int R, int
   // the two streams at the end
   const double t_tile = layout == 4 ? 1.7 * 1.1 / 2.0 : 1.7 * ((double)R + P + (double)R * rows / kBM) / (2.0 * R + P);
   const double t_start = layout == 4 ? 6.0 : 4.0;
-  const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
+  const double t_part = 0.10 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 3.0, t_merge_batch = 2.0;
   const int64_t rounds = (wgs + kCU - 1) / kCU;
   const int64_t batches = splits > 16 ? (splits + 63) / 64 : 1;
@@ -1941,7 +1931,7 @@ static double balanced_cost(int64_t A, double pieces, int64_t parts, int64_t spl
   const int rows = layout_rows(layout);
   const double t_tile = tile_time(R, P, layout);
   const double t_start = layout == 4 ? 6.0 : 4.0;
-  const double t_part = 0.15 * rows / kBM * R / 512.0 * part_bytes / 4.0;
+  const double t_part = 0.10 * rows / kBM * R / 512.0 * part_bytes / 4.0;
   const double t_merge = 3.0, t_merge_batch = 2.0;
   const int64_t batches = splits > 16 ? (splits + 63) / 64 : 1;
   const double t_fetch = 0.15 * (double)reads * cache_bytes / 8.0e6;   // us at 8 TB/s
