@@ -125,8 +125,9 @@ def test_partials_follow_the_adaptive_rule_and_merge_over_all_splits():
 
 def test_fused_merge_with_adaptive_splits():
     require_gpu()
+    # (lengths the fused merge can take: every split workgroup resident at once)
     cfg = synth.Config("adaptive_fused", 63, "bf16", B=6, H=16, R=512, P=64, q_len=17,
-                       prefix=("uniform", 100, 3000), tree="uniform")
+                       prefix=("uniform", 100, 1200), tree="uniform")
     inp = synth.generate(cfg)
     g = GpuInputs(inp)
     hint = int(inp.prefix_lens.sum())

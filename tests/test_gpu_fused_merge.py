@@ -20,6 +20,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(g, ws, **kw):
+    # (the fused merge is a split-schedule option: the separate merge it is
+    # compared with must see the same splits, not the balanced schedule)
+    kw.setdefault("schedule", 1)
     out, lse = kdt.verify_attn(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, None, g.cfg.softmax_scale,
                                max_prefix_len=g.max_prefix_len, workspace=ws, parents=g.parents, **kw)
     torch.cuda.synchronize()
@@ -27,6 +30,7 @@ def _run(g, ws, **kw):
 
 
 def _plan(g, **kw):
+    kw.setdefault("schedule", 1)
     d, _, _ = kdt._verify_prepare(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, None, g.cfg.softmax_scale,
                                   g.max_prefix_len, None, None, None, kw.pop("split_keys", 0), parents=g.parents,
                                   **kw)

@@ -437,13 +437,14 @@ struct PartLoad<__bf16> {
 // device-coherent loads.  GATE: a split's partial row is loaded only once its
 // log-sum-exp has shown it is not empty (for partial buffers where most of
 // the max_splits slots of a row are empty; one more memory round trip).
-template <typename T, typename PT, bool WIDE, bool COH, bool GATE = false>
+template <typename T, typename PT, bool WIDE, bool COH, bool GATE = false, int U = 16>
 __device__ __forceinline__ void merge_item(const PT* __restrict__ part_o, const float* __restrict__ part_lse,
                                            int max_splits, int ns, int M, int H, int R, int n_blk, int b, int blk,
                                            int cg, T* __restrict__ out, int64_t out_sb, int64_t out_st,
                                            int64_t out_sh, float* __restrict__ lse, float* s_st, int wave,
                                            int lane) {
-  constexpr int U = 16;
+  // (U: splits loaded in one round trip; fewer for launches with few splits,
+  // whose registers then leave room for more waves)
   constexpr int NV = PartLoad<PT>::NV;
   constexpr int CW = 2 * NV;                    // columns per item
   typedef typename PartLoad<PT>::raw raw;
@@ -1783,7 +1784,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
 // WIDE: one (sequence, block, column group) per workgroup; used when there
 // are more splits than one wave loads in one round trip.  Otherwise one item
 // per wave.
-template <typename T, typename PT, bool WIDE, bool GATE>
+template <typename T, typename PT, bool WIDE, bool GATE, int U>
 __global__ __launch_bounds__(256) void merge_kernel(
     const PT* __restrict__ part_o, const float* __restrict__ part_lse, int max_splits,
     int B, int q, int H, int R, int n_blk, const int32_t* __restrict__ prefix_lens, int split_keys, int tiles_max,
@@ -1805,7 +1806,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
     // (a skipped sequence wrote empty partials: any count is right)
     ns = L >= 0 && L <= 0x7FFFFFFF - q ? split_range(L + q, 0, split_keys, max_splits, tiles_max).ns : max_splits;
   }
-  merge_item<T, PT, WIDE, false, GATE>(part_o, part_lse, max_splits, ns, M, H, R, n_blk, b, blk, cg, out, out_sb,
+  merge_item<T, PT, WIDE, false, GATE, U>(part_o, part_lse, max_splits, ns, M, H, R, n_blk, b, blk, cg, out, out_sb,
                                        out_st, out_sh, lse, s_st, wave, lane);
 }
 
@@ -2190,26 +2191,27 @@ static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, c
   const bool wide = max_splits > 16;
   const int64_t grid = wide ? items : (items + 3) / 4;
   if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
-#define KDT_MERGE_LAUNCH(TO, W, GT)                                                                          \
-  hipLaunchKernelGGL((merge_kernel<TO, PT, W, GT>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, B, \
-                     q, H, R, n_blk, prefix_lens, split_keys, tiles_max, static_cast<TO*>(out), osb, ost, osh, lse)
+  // splits per round trip: the fewest of 4, 8 and 16 that hold every split
+  // (the sums then run in the same order whatever the choice)
+  const int u = wide ? 16 : (max_splits <= 4 ? 4 : (max_splits <= 8 ? 8 : 16));
+#define KDT_MERGE_LAUNCH(TO, W, GT, UU)                                                                      \
+  hipLaunchKernelGGL((merge_kernel<TO, PT, W, GT, UU>), dim3((unsigned)grid), dim3(256), 0, s, po, pl, max_splits, \
+                     B, q, H, R, n_blk, prefix_lens, split_keys, tiles_max, static_cast<TO*>(out), osb, ost, osh, lse)
+#define KDT_MERGE_U(TO, GT)                                 \
+  do {                                                      \
+    if (wide) KDT_MERGE_LAUNCH(TO, true, GT, 16);           \
+    else if (u == 4) KDT_MERGE_LAUNCH(TO, false, GT, 4);    \
+    else if (u == 8) KDT_MERGE_LAUNCH(TO, false, GT, 8);    \
+    else KDT_MERGE_LAUNCH(TO, false, GT, 16);               \
+  } while (0)
   if (dtype == KDT_BF16) {
-    if (gate) {
-      if (wide) KDT_MERGE_LAUNCH(__bf16, true, true);
-      else KDT_MERGE_LAUNCH(__bf16, false, true);
-    } else {
-      if (wide) KDT_MERGE_LAUNCH(__bf16, true, false);
-      else KDT_MERGE_LAUNCH(__bf16, false, false);
-    }
+    if (gate) KDT_MERGE_U(__bf16, true);
+    else KDT_MERGE_U(__bf16, false);
   } else {
-    if (gate) {
-      if (wide) KDT_MERGE_LAUNCH(float, true, true);
-      else KDT_MERGE_LAUNCH(float, false, true);
-    } else {
-      if (wide) KDT_MERGE_LAUNCH(float, true, false);
-      else KDT_MERGE_LAUNCH(float, false, false);
-    }
+    if (gate) KDT_MERGE_U(float, true);
+    else KDT_MERGE_U(float, false);
   }
+#undef KDT_MERGE_U
 #undef KDT_MERGE_LAUNCH
   return launch_status();
 }
