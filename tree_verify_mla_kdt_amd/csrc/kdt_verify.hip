@@ -998,766 +998,721 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
   }
 #pragma unroll 1
   for (int iter = 0; BAL ? more : iter < 1; ++iter) {
-  // Balanced schedule: the arguments and the thread index are taken afresh
-  // for every piece (the index through an opaque zero), so that what the
-  // body derives from them is computed inside the loop, not hoisted out of it
-  // and held in registers across every piece.
-  // (the one-piece kernels read the argument itself, whose loads the
-  // compiler may repeat instead of holding their values)
-  VerifyArgs a_piece;
-  if constexpr (BAL) a_piece = reread_args();
-  const VerifyArgs& a = BAL ? a_piece : a_in;
-  int opaque0 = 0;
-  if constexpr (BAL) asm volatile("s_mov_b32 %0, 0" : "=s"(opaque0));
-  const int tid = (int)threadIdx.x + opaque0;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  PieceDesc pc;
-  if constexpr (BAL) {
-    if (iter > 0) __syncthreads();
-    BalWalk walk;
-    {
-      const BalWalk& sw = s_walk[iter & 1];
-      walk.A = __builtin_amdgcn_readfirstlane(sw.A);
-      walk.U = __builtin_amdgcn_readfirstlane(sw.U);
-      walk.s = __builtin_amdgcn_readfirstlane(sw.s);
-      walk.e = __builtin_amdgcn_readfirstlane(sw.e);
-      walk.st = __builtin_amdgcn_readfirstlane(sw.st);
-      walk.j = __builtin_amdgcn_readfirstlane(sw.j);
-      walk.b = __builtin_amdgcn_readfirstlane(sw.b);
-      walk.grp = __builtin_amdgcn_readfirstlane(sw.grp);
-      walk.L = __builtin_amdgcn_readfirstlane(sw.L);
-      walk.T = __builtin_amdgcn_readfirstlane(sw.T);
-      walk.member = __builtin_amdgcn_readfirstlane(sw.member);
-    }
-    if (!bal_next(a, walk, lane, pc)) break;
-    if (tid == 0) s_walk[(iter + 1) & 1] = walk;
-  } else {
-    more = false;
-    if (a.compact) {
-      const Piece cp = compact_piece(a, lane);
-      if (!cp.work) return;
-      pc.rt = __builtin_amdgcn_readfirstlane(cp.rt);
-      pc.split = __builtin_amdgcn_readfirstlane(cp.split);
-      pc.b = __builtin_amdgcn_readfirstlane(cp.b);
-      pc.L = __builtin_amdgcn_readfirstlane(cp.L);
-      pc.known = true;
+    // Balanced schedule: the arguments and the thread index are taken afresh
+    // for every piece (the index through an opaque zero), so that what the
+    // body derives from them is computed inside the loop, not hoisted out of it
+    // and held in registers across every piece.
+    // (the one-piece kernels read the argument itself, whose loads the
+    // compiler may repeat instead of holding their values)
+    VerifyArgs a_piece;
+    if constexpr (BAL) a_piece = reread_args();
+    const VerifyArgs& a = BAL ? a_piece : a_in;
+    int opaque0 = 0;
+    if constexpr (BAL) asm volatile("s_mov_b32 %0, 0" : "=s"(opaque0));
+    const int tid = (int)threadIdx.x + opaque0;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    PieceDesc pc;
+    if constexpr (BAL) {
+      if (iter > 0) __syncthreads();
+      BalWalk walk;
+      {
+        const BalWalk& sw = s_walk[iter & 1];
+        walk.A = __builtin_amdgcn_readfirstlane(sw.A);
+        walk.U = __builtin_amdgcn_readfirstlane(sw.U);
+        walk.s = __builtin_amdgcn_readfirstlane(sw.s);
+        walk.e = __builtin_amdgcn_readfirstlane(sw.e);
+        walk.st = __builtin_amdgcn_readfirstlane(sw.st);
+        walk.j = __builtin_amdgcn_readfirstlane(sw.j);
+        walk.b = __builtin_amdgcn_readfirstlane(sw.b);
+        walk.grp = __builtin_amdgcn_readfirstlane(sw.grp);
+        walk.L = __builtin_amdgcn_readfirstlane(sw.L);
+        walk.T = __builtin_amdgcn_readfirstlane(sw.T);
+        walk.member = __builtin_amdgcn_readfirstlane(sw.member);
+      }
+      if (!bal_next(a, walk, lane, pc)) break;
+      if (tid == 0) s_walk[(iter + 1) & 1] = walk;
     } else {
-      const int u = xcd_remap(blockIdx.x, gridDim.x);
-      pc.rt = u % a.n_rt;
-      const int g = (int)((int64_t)(u / a.n_rt) * a.group_mul % ((int64_t)a.B * a.max_splits));
-      pc.split = g % a.max_splits;
-      pc.b = g / a.max_splits;
-      pc.L = 0;
-      pc.known = false;
-    }
-    pc.k_begin = pc.k_end = pc.ns = 0;
-  }
-  const int rt = pc.rt, split = pc.split, b = pc.b;
-  const int r = lane & 31, hh = lane >> 5;
-  // row block, output column half (and depth half), key stream
-  const int rb = KS ? (wave >> 1) : wave / CSC, chalf = KS ? 0 : wave % CSC, kp = KS ? (wave & 1) : 0;
-  const int c0 = DS ? chalf * NQF : 0;          // first score step of this wave
-  const int m = rt * BM + rb * 32 + r;        // this lane's query row
-  const bool row_ok = m < a.M;
-  const int t = row_ok ? m / a.H : 0;
-  const int h = row_ok ? m - t * a.H : 0;
-
-  // Start-up order: the speculative copies of the first two key tiles, so
-  // the key stream starts at once, then the query fragments and visibility
-  // words, then the prefix length (a scalar load: the index is uniform, so
-  // waiting for it waits for no vector load).  All four latencies overlap.
-  // the split's first key as for a sequence of the longest length the
-  // launch allows (right for it and for every split of fixed size; the
-  // speculative copies below use it)
-  const bool L_bad_known = pc.known && len_bad(a, pc.L);
-  const int k_spec = !pc.known ? split * a.split_keys
-                     : L_bad_known ? 0
-                     : BAL ? pc.k_begin
-                           : split_range(pc.L + a.q, split, a.split_keys, a.max_splits, a.tiles_max).k_begin;
-  int k_begin = k_spec;
-  const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
-  const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
-  const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
-  const uint32_t pe_ss = (uint32_t)(a.k_pe_ss * (int64_t)sizeof(T));
-  // One buffer descriptor per region for the whole split, so that a tile
-  // copy only adds its row offset.  It spans the split's rows below the cache
-  // capacity (the host keeps split_keys rows of either region under 2^31
-  // bytes); every row a copy reads is one of them.
-  auto span_of = [&](int kb) {
-    return max((int64_t)0, min((int64_t)a.span_keys, a.capacity - (int64_t)kb));
-  };
-  i32x4 rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
-  i32x4 rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
-  // Copy of key tile `tile` (first key k_begin + tile * kBN) into the tile
-  // buffer at LDS address lds, with its first `nrows` rows real; later rows
-  // repeat row nrows - 1.
-  auto stage_rows = [&](int tile, uint32_t lds, int nrows) {
-    const uint32_t r0 = (uint32_t)(tile * kBN);
-    stage_region<kBN, RC>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane);
-    stage_region<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane);
-  };
-  // Speculative copies of the first two tiles as if the split were full:
-  // rows below the cache capacity are always inside the caller's buffer, so
-  // this is safe before the prefix length is known; it is right whenever the
-  // split really covers both tiles (every split but a sequence's last).
-  const bool spec = (int64_t)k_begin + 2 * kBN <= a.capacity;
-  // Parents (when the masks are derived here) are loaded first, so that by
-  // the time any later copy has been waited for they have landed too.
-  int par_v[2] = {-1, -1};
-  if (a.parents) {
-    const int32_t* pp = a.parents + (int64_t)b * a.q;
-    par_v[0] = lane < a.q ? pp[lane] : -1;
-    par_v[1] = lane + 64 < a.q ? pp[lane + 64] : -1;
-  }
-  if (spec) {
-    stage_rows(0, lds_addr(s_tiles[0]), kBN);
-    stage_rows(1, lds_addr(s_tiles[1]), kBN);
-  }
-
-  // The query fragments and visibility words do not depend on the prefix
-  // length.  Padding rows (m >= M) load token 0 / head 0: an output column of
-  // either contraction depends only on its own query column, and padding rows
-  // are never written, so no masking is needed.
-  //
-  // In the 64-row layout (bf16) the workgroup's query rows are copied like
-  // two key tiles, into the two ring buffers the first tiles leave free, and
-  // each wave then reads its fragments with the score operand's LDS pattern:
-  // 1 KB contiguous per copy instead of 32 scattered rows per load.
-  constexpr bool Q_VIA_LDS = (CS == 2 || KS) && (KW == 8) && (NBUF == 4);
-  static_assert(!Q_VIA_LDS || BM == 2 * kBN, "query staging: two 32-row blocks per workgroup");
-  const bool q_lds = Q_VIA_LDS && a.q_rows_uniform;
-  frag qf[NQF];
-  if (q_lds) {
-    const uint32_t ql_ss = (uint32_t)(a.q_lat_sh * (int64_t)sizeof(T));
-    const uint32_t qp_ss = (uint32_t)(a.q_pe_sh * (int64_t)sizeof(T));
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int row0 = rt * BM + blk * kBN;
-      const int nr = min(kBN, a.M - row0);    // rows of this block that exist
-      const int base_row = nr > 0 ? row0 : rt * BM;
-      const int nrows = nr > 0 ? nr : 1;
-      const char* ql = reinterpret_cast<const char*>(a.q_lat) +
-                       (b * a.q_lat_sb + (int64_t)base_row * a.q_lat_sh) * (int64_t)sizeof(T);
-      const char* qp = reinterpret_cast<const char*>(a.q_pe) +
-                       (b * a.q_pe_sb + (int64_t)base_row * a.q_pe_sh) * (int64_t)sizeof(T);
-      stage_region<kBN, RC>(make_rsrc(ql, (uint32_t)nrows * ql_ss), 0, ql_ss, nrows, lds_addr(s_tiles[2 + blk]),
-                            wave, lane);
-      stage_region<kBN, PC>(make_rsrc(qp, (uint32_t)nrows * qp_ss), 0, qp_ss, nrows,
-                            lds_addr(s_tiles[2 + blk]) + LAT_BYTES, wave, lane);
-    }
-  } else {
-    const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
-    const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
-#pragma unroll
-    for (int j = 0; j < NQF; ++j) {
-      const int c = c0 + j;
-      if (c < R / KMF) qf[j] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
-      else qf[j] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
-    }
-    if constexpr (QPE) {
-      // the rope fragments go to LDS (one wave of each row block writes them)
-      if (kp == 0) {
-#pragma unroll
-        for (int i = 0; i < NQR; ++i)
-          *reinterpret_cast<frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16) =
-              *reinterpret_cast<const frag*>(qp + i * KMF + hh * KW);
-      }
-    }
-  }
-  uint64_t vw0 = ~0ull, vw1 = ~0ull;
-  if (row_ok && a.vis) {
-    const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
-    vw0 = vr[0];
-    vw1 = a.W > 1 ? vr[1] : 0ull;
-  }
-  const int L = pc.known ? pc.L : ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
-
-  const bool bad = len_bad(a, L);
-  const int N = L + a.q;
-  SplitRange sr;
-  if (BAL) {
-    sr.k_begin = pc.k_begin;
-    sr.k_end = pc.k_end;
-    sr.ns = pc.ns;
-  } else {
-    sr = split_range(bad ? 1 : N, split, a.split_keys, a.max_splits, a.tiles_max);
-  }
-  k_begin = sr.k_begin;
-  // (compaction and the balanced schedule run no workgroup for the splits a
-  // sequence does not use: the workgroups of its first split mark them empty)
-  const bool fill_unused = BAL || a.compact;
-
-  if (bad || k_begin >= N) wait_vmem_lds<0>();   // no copy may outlive the workgroup
-  if (bad) {
-    // skipped sequence: zero output, lse = -inf (direct) or an empty partial
-    if (tid == 0 && rt == 0 && split == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_LEN);
-    if (row_ok && hh == 0 && chalf == 0 && (!a.fuse || split == 0)) {
-      if (DIRECT || a.fuse) {
-        a.lse[(int64_t)b * a.M + m] = -INFINITY;
-        T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
-        for (int d = 0; d < R; ++d) o[d] = (T)0.0f;
+      more = false;
+      if (a.compact) {
+        const Piece cp = compact_piece(a, lane);
+        if (!cp.work) return;
+        pc.rt = __builtin_amdgcn_readfirstlane(cp.rt);
+        pc.split = __builtin_amdgcn_readfirstlane(cp.split);
+        pc.b = __builtin_amdgcn_readfirstlane(cp.b);
+        pc.L = __builtin_amdgcn_readfirstlane(cp.L);
+        pc.known = true;
       } else {
-        // (a skipped sequence has one split there: it writes them all)
-        for (int k = split; k < (fill_unused ? a.max_splits : split + 1); ++k)
-          a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
+        const int u = xcd_remap(blockIdx.x, gridDim.x);
+        pc.rt = u % a.n_rt;
+        const int g = (int)((int64_t)(u / a.n_rt) * a.group_mul % ((int64_t)a.B * a.max_splits));
+        pc.split = g % a.max_splits;
+        pc.b = g / a.max_splits;
+        pc.L = 0;
+        pc.known = false;
       }
+      pc.k_begin = pc.k_end = pc.ns = 0;
     }
-    continue;
-  }
-  if (!DIRECT && fill_unused && !a.fuse && split == 0 && row_ok && hh == 0 && chalf == 0 && kp == 0) {
-    for (int k = sr.ns; k < a.max_splits; ++k) a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
-  }
-  if (k_begin >= N) {
-    // this split does not exist for sequence b: an empty partial, so that a
-    // merge over all max_splits splits is always right
-    if (!DIRECT && !a.fuse && row_ok && hh == 0 && chalf == 0 && kp == 0)
-      a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = -INFINITY;
-    continue;
-  }
-  const int k_end = sr.k_end;
-  const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
-  const bool spec_ok = spec && k_begin == k_spec && k_begin + 2 * kBN <= k_end;
-  if (k_begin != k_spec) {
-    // (adaptive splits of a shorter sequence: the speculative copies read
-    // other rows, and are waited for and replaced below)
-    rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
-    rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
-  }
+    const int rt = pc.rt, split = pc.split, b = pc.b;
+    const int r = lane & 31, hh = lane >> 5;
+    // row block, output column half (and depth half), key stream
+    const int rb = KS ? (wave >> 1) : wave / CSC, chalf = KS ? 0 : wave % CSC, kp = KS ? (wave & 1) : 0;
+    const int c0 = DS ? chalf * NQF : 0;          // first score step of this wave
+    const int m = rt * BM + rb * 32 + r;        // this lane's query row
+    const bool row_ok = m < a.M;
+    const int t = row_ok ? m / a.H : 0;
+    const int h = row_ok ? m - t * a.H : 0;
 
-  auto stage = [&](int tile, uint32_t lds) { stage_rows(tile, lds, min(kBN, k_end - (k_begin + tile * kBN))); };
-  // The same copy, one wave-load at a time (pieces 0 .. NPIECE - 1), so that
-  // the copies can be issued between value MFMAs: a wave waiting for the
-  // texture unit to accept a copy then still has MFMAs in flight.
-  constexpr int LAT_PIECES = region_wave_loads<kBN, RC>();
-  constexpr int NPIECE = LAT_PIECES + region_wave_loads<kBN, PC>();
-  auto stage_piece = [&](int tile, int nrows, uint32_t lds, int piece) __attribute__((always_inline)) {
-    const uint32_t r0 = (uint32_t)(tile * kBN);
-    if (piece < LAT_PIECES)
-      stage_one<kBN, RC, KS>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane, piece);
-    else
-      stage_one<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane, piece - LAT_PIECES);
-  };
-
-
-
-  // Per-lane LDS byte offsets inside a tile buffer (bf16 only; the fp32 path
-  // computes its addresses inline).
-  //  * score operand, step c: chunk 2c + hh of key r.  With a swizzle over LSW
-  //    chunks, 2c + hh = LSW * (c / QB) + (2 * (c % QB) + hh) for QB = LSW / 2
-  //    and the swizzle only touches the second part, so the address is
-  //    qk_lat[c % QB] + 16 * LSW * (c / QB).
-  //  * value operand, transposing read: in each 16-lane group, lane 4e + q
-  //    loads columns d0 + 4q .. d0 + 4q + 3 of key k_e and lane j then holds
-  //    column d0 + j of keys k_0..k_3.  Operand row d = 32 * db + r; slots 0-3
-  //    are keys c_row(8c + 0..3, hh), slots 4-7 keys c_row(8c + 4..7, hh).
-  //    The 16-byte chunk is 4 * db + x with x < 4, and (4 db + x) ^ s =
-  //    4 (db ^ s2) + (x ^ s01) for s2 = s >> 2, s01 = s & 3; db ^ s2 only
-  //    changes the low two bits of db.  The keys are 16c + (8 half + 4 hh +
-  //    e) and the swizzle depends on the key modulo 16 only, so c moves the
-  //    address by whole 16-key blocks: pv_base[half][db % 4] + 64 * db +
-  //    c * (16 rows of the region).
-  constexpr int LSW = (RC % 16 == 0) ? 16 : 8;
-  constexpr int QB = LSW / 2;
-  int qk_lat[QB], qk_pe[4];
-  int pv_base[2][4];
-  if constexpr (KW == 8) {
-    static_assert(P / KMF <= 4 && RC % 8 == 0, "bf16 score addressing");
-    const int sr = swz_of<RC>(r);
-#pragma unroll
-    for (int j = 0; j < QB; ++j) qk_lat[j] = r * RC * 16 + (((2 * j + hh) ^ sr) << 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)   // rope region: chunk 2j + hh exists only while it is < PC
-      qk_pe[j] = LAT_BYTES + region_off<PC>(r, (2 * j + hh) < PC ? (2 * j + hh) : 0);
-    const int g = lane >> 4, sl = lane & 15;
-    const int e = sl >> 2, qd = sl & 3;
-    const int x = 2 * (g & 1) + (qd >> 1);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k = c_row(4 * half + e, hh);
-      const int sk = swz_of<RC>(k), s2 = sk >> 2, s01 = sk & 3;
-      const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) pv_base[half][d4] = base + 64 * ((d4 ^ s2) - d4);
+    // Start-up order: the speculative copies of the first two key tiles, so
+    // the key stream starts at once, then the query fragments and visibility
+    // words, then the prefix length (a scalar load: the index is uniform, so
+    // waiting for it waits for no vector load).  All four latencies overlap.
+    // the split's first key as for a sequence of the longest length the
+    // launch allows (right for it and for every split of fixed size; the
+    // speculative copies below use it)
+    const bool L_bad_known = pc.known && len_bad(a, pc.L);
+    const int k_spec = !pc.known ? split * a.split_keys
+                       : L_bad_known ? 0
+                       : BAL ? pc.k_begin
+                             : split_range(pc.L + a.q, split, a.split_keys, a.max_splits, a.tiles_max).k_begin;
+    int k_begin = k_spec;
+    const char* kv_lat = reinterpret_cast<const char*>(a.c_kv) + (b * a.c_kv_sb) * (int64_t)sizeof(T);
+    const char* kv_pe = reinterpret_cast<const char*>(a.k_pe) + (b * a.k_pe_sb) * (int64_t)sizeof(T);
+    const uint32_t lat_ss = (uint32_t)(a.c_kv_ss * (int64_t)sizeof(T));
+    const uint32_t pe_ss = (uint32_t)(a.k_pe_ss * (int64_t)sizeof(T));
+    // One buffer descriptor per region for the whole split, so that a tile
+    // copy only adds its row offset.  It spans the split's rows below the cache
+    // capacity (the host keeps split_keys rows of either region under 2^31
+    // bytes); every row a copy reads is one of them.
+    auto span_of = [&](int kb) {
+      return max((int64_t)0, min((int64_t)a.span_keys, a.capacity - (int64_t)kb));
+    };
+    i32x4 rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
+    i32x4 rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
+    // Copy of key tile `tile` (first key k_begin + tile * kBN) into the tile
+    // buffer at LDS address lds, with its first `nrows` rows real; later rows
+    // repeat row nrows - 1.
+    auto stage_rows = [&](int tile, uint32_t lds, int nrows) {
+      const uint32_t r0 = (uint32_t)(tile * kBN);
+      stage_region<kBN, RC>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane);
+      stage_region<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane);
+    };
+    // Speculative copies of the first two tiles as if the split were full:
+    // rows below the cache capacity are always inside the caller's buffer, so
+    // this is safe before the prefix length is known; it is right whenever the
+    // split really covers both tiles (every split but a sequence's last).
+    const bool spec = (int64_t)k_begin + 2 * kBN <= a.capacity;
+    // Parents (when the masks are derived here) are loaded first, so that by
+    // the time any later copy has been waited for they have landed too.
+    int par_v[2] = {-1, -1};
+    if (a.parents) {
+      const int32_t* pp = a.parents + (int64_t)b * a.q;
+      par_v[0] = lane < a.q ? pp[lane] : -1;
+      par_v[1] = lane + 64 < a.q ? pp[lane + 64] : -1;
     }
-  }
+    if (spec) {
+      stage_rows(0, lds_addr(s_tiles[0]), kBN);
+      stage_rows(1, lds_addr(s_tiles[1]), kBN);
+    }
 
-  // Visibility words from parent pointers, only where this split reaches the
-  // tree (keys L .. N - 1): every wave runs the pointer doubling for the
-  // sequence in its own LDS area and reads its tokens' rows.
-  auto derive_vis = [&]() {
-    if (!a.parents || k_end <= L) return;
-    uint64_t m0[2], m1[2];
-    const int va = KS ? 0 : wave;
-    if (!KS || wave == 0) {
-      const bool bad_tree = wave_ancestor_masks(par_v, a.q, s_vm[va], s_vj[va], lane, m0, m1);
-      if (__any(bad_tree) && lane == 0 && wave == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_TREE);
-    }
-    if constexpr (KS) {
-      wait_lds();
-      tile_barrier();
-    }
-    if (row_ok) {
-      vw0 = s_vm[va][2 * t];
-      vw1 = s_vm[va][2 * t + 1];
-    }
-  };
-
-  if constexpr (Q_VIA_LDS) {
+    // The query fragments and visibility words do not depend on the prefix
+    // length.  Padding rows (m >= M) load token 0 / head 0: an output column of
+    // either contraction depends only on its own query column, and padding rows
+    // are never written, so no masking is needed.
+    //
+    // In the 64-row layout (bf16) the workgroup's query rows are copied like
+    // two key tiles, into the two ring buffers the first tiles leave free, and
+    // each wave then reads its fragments with the score operand's LDS pattern:
+    // 1 KB contiguous per copy instead of 32 scattered rows per load.
+    constexpr bool Q_VIA_LDS = (CS == 2 || KS) && (KW == 8) && (NBUF == 4);
+    static_assert(!Q_VIA_LDS || BM == 2 * kBN, "query staging: two 32-row blocks per workgroup");
+    const bool q_lds = Q_VIA_LDS && a.q_rows_uniform;
+    frag qf[NQF];
     if (q_lds) {
-      // the query copies (and the first tiles, issued before them) have landed
-      wait_vmem_lds<0>();
-      tile_barrier();
-      derive_vis();
-      const char* qbuf = s_tiles[2 + rb];
+      const uint32_t ql_ss = (uint32_t)(a.q_lat_sh * (int64_t)sizeof(T));
+      const uint32_t qp_ss = (uint32_t)(a.q_pe_sh * (int64_t)sizeof(T));
 #pragma unroll
-      for (int c = 0; c < NCHUNK; ++c) {
-        const char* src = (c < R / KMF) ? qbuf + qk_lat[c % QB] + 16 * LSW * (c / QB) : qbuf + qk_pe[c - R / KMF];
-        if constexpr (KS) {
-          if (c < NQF) qf[c] = *reinterpret_cast<const frag*>(src);
-          else if (kp == 0)
-            *reinterpret_cast<frag*>(s_qpe + ((rb * NQR + (c - NQF)) * 64 + lane) * 16) =
-                *reinterpret_cast<const frag*>(src);
-        } else {
-          qf[c] = *reinterpret_cast<const frag*>(src);
-        }
+      for (int blk = 0; blk < 2; ++blk) {
+        const int row0 = rt * BM + blk * kBN;
+        const int nr = min(kBN, a.M - row0);    // rows of this block that exist
+        const int base_row = nr > 0 ? row0 : rt * BM;
+        const int nrows = nr > 0 ? nr : 1;
+        const char* ql = reinterpret_cast<const char*>(a.q_lat) +
+                         (b * a.q_lat_sb + (int64_t)base_row * a.q_lat_sh) * (int64_t)sizeof(T);
+        const char* qp = reinterpret_cast<const char*>(a.q_pe) +
+                         (b * a.q_pe_sb + (int64_t)base_row * a.q_pe_sh) * (int64_t)sizeof(T);
+        stage_region<kBN, RC>(make_rsrc(ql, (uint32_t)nrows * ql_ss), 0, ql_ss, nrows, lds_addr(s_tiles[2 + blk]),
+                              wave, lane);
+        stage_region<kBN, PC>(make_rsrc(qp, (uint32_t)nrows * qp_ss), 0, qp_ss, nrows,
+                              lds_addr(s_tiles[2 + blk]) + LAT_BYTES, wave, lane);
       }
-      // every wave has its fragments before the buffers take key tiles again
-      wait_vmem_lds<0>();
-      tile_barrier();
-    }
-  }
-  if (!q_lds) derive_vis();
-
-  f32x16 acc[NBL];
+    } else {
+      const T* ql = reinterpret_cast<const T*>(a.q_lat) + b * a.q_lat_sb + t * a.q_lat_st + h * a.q_lat_sh;
+      const T* qp = reinterpret_cast<const T*>(a.q_pe) + b * a.q_pe_sb + t * a.q_pe_st + h * a.q_pe_sh;
 #pragma unroll
-  for (int i = 0; i < NBL; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-  // Softmax state of this lane's row (log2 domain).  m_ref is the reference
-  // the weights are taken against: fixed at the first tile with a visible key,
-  // it never moves while weights stay below 2^kRefSlack, so the accumulators
-  // are never rescaled.  m_max is the true running max.  If some row's max
-  // outgrows its reference by more than that, the wave's accumulation is void
-  // ("dead"): it keeps running its tiles (the copy schedule is shared by all
-  // waves) and tracking m_max, then redoes the split once with m_ref = m_max
-  // (the exact max), which cannot trigger again, discarding what it summed.
-  float m_ref = -INFINITY, m_max = -INFINITY;
-  float l_run = 0.0f;           // this lane's share of sum_j exp2(s_j - m_ref)
-  bool dead = false;            // wave-uniform
-
-  // One key tile: scores, softmax, value contraction.  `buf` is the tile's
-  // ring buffer; the tile's first key is kt.  The copy of the first st_rows
-  // rows of tile st_tile into st_buf is issued piece by piece between the
-  // value MFMAs.
-  // Key streams: the next pair of tiles (copied between this step's score
-  // MFMAs; rows 0 = no such tile).
-  int ks_t0 = 0, ks_t1 = 0, ks_r0 = 0, ks_r1 = 0;
-  // Key streams: accumulator block db of stream kp holds output column block
-  // col_block(db) = (db + 8 kp) mod 16, so that every wave keeps blocks 0-7
-  // and hands blocks 8-15 to its partner at the end (register indices fixed
-  // at compile time on both streams); the value operand of block db is read
-  // at LDS offset 64 db + rot_off[db >= 8] instead of 64 col_block(db).
-  const int rot_off[2] = {512 * kp, -512 * kp};
-  auto col_block = [&](int db) { return KS ? ((db + 8 * kp) & 15) : chalf * NBL + db; };
-  uint32_t ks_b0 = 0, ks_b1 = 0;          // (LDS addresses)
-  auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, uint32_t st_buf)
-                       __attribute__((always_inline)) {
-    const int kt = k_begin + tile * kBN;
-    // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T.
-    // The K fragments are read QPF steps ahead of the MFMA chain.
-    auto score_src = [&](int c) __attribute__((always_inline)) -> const char* {
-      if constexpr (KW == 8) {
-        // bf16: step c reads 16-byte chunk 2c + hh of the row
-        if (c < R / KMF) return buf + qk_lat[c % QB] + 16 * LSW * (c / QB);
-        return buf + qk_pe[c - R / KMF];
-      } else {
-        const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
-        if (c < R / KMF) return buf + region_off<RC>(r, byte >> 4) + (byte & 15);
-        return buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
+      for (int j = 0; j < NQF; ++j) {
+        const int c = c0 + j;
+        if (c < R / KMF) qf[j] = *reinterpret_cast<const frag*>(ql + c * KMF + hh * KW);
+        else qf[j] = *reinterpret_cast<const frag*>(qp + (c * KMF - R) + hh * KW);
       }
-    };
-    // (key streams hold no accumulator block in LDS, so their scores take
-    // registers and the operand queues are shorter)
-    constexpr int QPF0 = QPE ? 2 : KDT_SCORE_PREFETCH;
-    constexpr int QPF = NSTEP < QPF0 ? NSTEP : QPF0;
-    frag kf[QPF];
-#pragma unroll
-    for (int j = 0; j < QPF; ++j) kf[j] = *reinterpret_cast<const frag*>(score_src(c0 + j));
-    // this row block's rope fragments of the query, read from LDS QPF steps
-    // before their MFMA
-    auto qpe_src = [&](int i) { return reinterpret_cast<const frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16); };
-    frag qq[QPE ? QPF : 1];
-    f32x16 s;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = 0.0f;
-    // (bf16: the tile stays in VGPRs; see Mfma<__bf16>::mma_acc_v.  Not in
-    // the balanced 64-row kernel, where the compiler parks query fragments in
-    // accumulation registers and copies them back right before their MFMA.)
-    auto score_mma = [&](const frag& x, const frag& y, int j) __attribute__((always_inline)) {
-      if constexpr (SCORE_VGPR) {
-        if (j == 0) s = MM::mma_first_v(x, y);
-        else MM::mma_acc_v(x, y, s);
-      } else {
-        s = MM::mma(x, y, s);
-      }
-    };
-#pragma unroll
-    for (int j = 0; j < NSTEP; ++j) {
-      const frag cur = kf[j % QPF];
-      if (j + QPF < NSTEP) kf[j % QPF] = *reinterpret_cast<const frag*>(score_src(c0 + j + QPF));
       if constexpr (QPE) {
-        static_assert(!QPE || NQF >= QPF, "rope fragments are queued behind the register ones");
-        // the slot refilled now is the one this step consumes: take it first
-        const frag qcur = j < NQF ? qf[j < NQF ? j : 0] : qq[j % QPF];
-        if (j + QPF >= NQF && j + QPF < NSTEP) qq[(j + QPF) % QPF] = *qpe_src(j + QPF - NQF);
-        score_mma(cur, qcur, j);
-      } else {
-        score_mma(cur, qf[j], j);
-      }
-      fence_mem_mfma();
-      if constexpr (KS) {
-        // the next pair's copies, one wave-load at a time between these MFMAs
-        constexpr int NP2 = 2 * NPIECE;
+        // the rope fragments go to LDS (one wave of each row block writes them)
+        if (kp == 0) {
 #pragma unroll
-        for (int pc = j * NP2 / NSTEP; pc < (j + 1) * NP2 / NSTEP; ++pc) {
-          if (pc < NPIECE) stage_piece(ks_t0, ks_r0, ks_b0, pc);
-          else stage_piece(ks_t1, ks_r1, ks_b1, pc - NPIECE);
+          for (int i = 0; i < NQR; ++i)
+            *reinterpret_cast<frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16) =
+                *reinterpret_cast<const frag*>(qp + i * KMF + hh * KW);
         }
       }
     }
-    if constexpr (SCORE_VGPR) MM::score_ready(s);
-    if constexpr (DS) {
-      // add the partner's half of the contraction (the pair's waves hold the
-      // same rows and keys; a + b is the same on both)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) s_sx[(wave * 4 + g) * 64 + lane] = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
-      wait_lds();
-      tile_barrier();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 o = s_sx[((wave ^ 1) * 4 + g) * 64 + lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * g + e] += o[e];
-      }
+    uint64_t vw0 = ~0ull, vw1 = ~0ull;
+    if (row_ok && a.vis) {
+      const uint64_t* vr = a.vis + ((int64_t)b * a.q + t) * a.W;
+      vw0 = vr[0];
+      vw1 = a.W > 1 ? vr[1] : 0ull;
     }
-    // Value operand of contraction step c (16 keys), output block db.
-    auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
-      if constexpr (KW == 1) {
-        // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
-        const int col = ((chalf * NBL + db) * 32 + r) * (int)sizeof(T);
-        return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
-      } else {
-        // bf16: two transposing reads (lane bases computed before the loop)
-        const int dg = chalf * NBL + db;      // output column block (key streams: rotated, below)
-        const int o = (KS ? 64 * db + rot_off[db >= NBL / 2] : 64 * dg) + c * 16 * RC * 16;
-        const bf16x4 lo = lds_read_tr16(buf + pv_base[0][dg & 3] + o);
-        const bf16x4 hi = lds_read_tr16(buf + pv_base[1][dg & 3] + o);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    };
-    constexpr int STEPS = PV_STEPS * NBL;
-    constexpr int VPF = STEPS < KDT_VALUE_PREFETCH ? STEPS : KDT_VALUE_PREFETCH;
-    // The first value operands are requested now, so their LDS latency
-    // passes during the softmax instead of stalling the first value MFMA.
-    frag vq[VPF + 1];
-#pragma unroll
-    for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NBL, i % NBL);
+    const int L = pc.known ? pc.L : ((const __attribute__((address_space(4))) int32_t*)a.prefix_lens)[b];
 
-    // ---- online softmax for this lane's row (16 of the tile's 32 keys)
-    // Raw scores; the scale (positive) is applied to the row max and folded
-    // into each weight's exponent, one fused multiply-add per weight.
-    float sv[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sv[v] = s[v];
-    if (kt + kBN > L || kt + kBN > k_end) {   // only tiles reaching the tree or the split end
-      // (an empty volatile asm: without it the compiler turns this branch
-      // into selects that every tile then executes, some 200 instructions
-      // between the score and the value MFMAs)
-      asm volatile("");
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = kt + c_row(v, hh);
-        const int uu = kk - L;                                  // tree node if >= 0
-        const uint64_t w = uu < 64 ? vw0 : vw1;
-        const bool tree_ok = uu < 0 || ((w >> (uu & 63)) & 1ull);
-        sv[v] = (kk < k_end && tree_ok) ? sv[v] : -INFINITY;
-      }
+    const bool bad = len_bad(a, L);
+    const int N = L + a.q;
+    SplitRange sr;
+    if (BAL) {
+      sr.k_begin = pc.k_begin;
+      sr.k_end = pc.k_end;
+      sr.ns = pc.ns;
+    } else {
+      sr = split_range(bad ? 1 : N, split, a.split_keys, a.max_splits, a.tiles_max);
     }
-    auto tile_max = [&]() __attribute__((always_inline)) {
-      float x = sv[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) x = fmaxf(x, sv[v]);
-      return xhalf_max(x) * a.scale_log2;
-    };
-    // Only tiles where some row of the wave still lacks its reference take
-    // this (uniform) branch: the row's running max, this tile included, sets
-    // it.  Elsewhere the weights depend on the fixed reference alone.
-    if (__any(m_ref == -INFINITY)) {
-      const float mx0 = tile_max();
-      if (m_ref == -INFINITY) m_ref = fmaxf(m_max, mx0);   // first visible key of this row
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], a.scale_log2, -m_use));
-      l_run += p[v];
-    }
-    // The running max and the check against the reference feed no weight of
-    // this tile, and no branch: they can overlap the value MFMAs.  A wave
-    // whose scores outgrow its reference records it in `dead`, which is read
-    // after the last tile.
-    m_max = fmaxf(m_max, tile_max());
-    dead = dead || __any(m_max > m_ref + kRefSlack);
+    k_begin = sr.k_begin;
+    // (compaction and the balanced schedule run no workgroup for the splits a
+    // sequence does not use: the workgroups of its first split mark them empty)
+    const bool fill_unused = BAL || a.compact;
 
-    // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]; the value operand of
-    // step i + VPF is read while step i's MFMA is issued (the first VPF were
-    // requested before the softmax).
-    frag pfr[PV_STEPS];
-#pragma unroll
-    for (int c = 0; c < PV_STEPS; ++c) pfr[c] = MM::pack(p + c * KW);
-#pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      const int c = i / NBL, db = i % NBL;
-      if (i + VPF < STEPS) vq[(i + VPF) % (VPF + 1)] = value_frag((i + VPF) / NBL, (i + VPF) % NBL);
-      acc[db] = MM::mma(vq[i % (VPF + 1)], pfr[c], acc[db]);
-      fence_mem_mfma();
-      // copy pieces [i * NPIECE / STEPS, (i + 1) * NPIECE / STEPS) follow this MFMA
-      if constexpr (!KS) {
-#pragma unroll
-        for (int pc = i * NPIECE / STEPS; pc < (i + 1) * NPIECE / STEPS; ++pc)
-          stage_piece(st_tile, st_rows, st_buf, pc);
-      }
-    }
-  };
-
-  if (tid == 0) s_dead = 0;
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) {
-      if (dead) s_dead = 1;
-      __syncthreads();
-      if (s_dead == 0) break;                 // common case: no redo
-      // Depth split: every wave takes part in the score exchange (a
-      // workgroup barrier), so all waves redo the split; rows that did not
-      // outgrow their reference recompute the same sums.
-      if (dead || DS) {
-#pragma unroll
-        for (int i = 0; i < NBL; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-        l_run = 0.0f;
-        if (dead) m_ref = m_max;
-      }
-    }
-    const bool compute = (pass == 0) || dead || DS;
-    dead = false;
-    // Tiles rotate through the NBUF buffers: the step for tile t waits for its
-    // copy and computes, issuing between its value MFMAs the copy of tile
-    // t + NBUF - 1 into the buffer the previous step has finished reading.
-    // Every step issues exactly one copy: once no tile is left, a dummy copy
-    // (row 0 of tile t, re-read into every row) goes to that buffer, which no
-    // later tile uses.  So exactly NBUF - 2 copies are always younger than the
-    // one a step waits for, and one wait count serves every step.
-    auto wait_tile = [&]() __attribute__((always_inline)) {
-      wait_vmem_lds<STAGE_LOADS * (NBUF - 2)>();
-      tile_barrier();
-    };
-    if constexpr (KS) {
-      // Key streams: step s computes tiles 2s (waves of stream 0) and 2s + 1
-      // (stream 1) from one buffer pair while the next pair's copies go to
-      // the other pair of buffers, which the step before has finished
-      // reading.  Each step waits for all of its own copies and meets the
-      // workgroup at one barrier, after which every copy of the pair has
-      // landed and every wave is done with the previous pair.
-      if (pass == 0 && spec_ok) {
-        wait_vmem_lds<0>();
-      } else {
-        wait_vmem_lds<0>();
-        stage(0, lds_addr(s_tiles[0]));
-        if (n_tiles > 1) stage(1, lds_addr(s_tiles[1]));
-      }
-      const int n_steps = (n_tiles + 1) / 2;
-      auto tile_rows = [&](int tt) { return tt < n_tiles ? min(kBN, k_end - (k_begin + tt * kBN)) : 0; };
-#pragma unroll 1
-      for (int s0 = 0; s0 < n_steps; s0 += 2) {
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int st = s0 + hs;
-          if (st >= n_steps) break;
-          wait_vmem_lds<0>();
-          tile_barrier();
-          // the next pair; past the last tile a dummy copy (row 0 of tile 0,
-          // always inside the split) goes to a buffer no later step reads,
-          // so the copies between the score MFMAs need no branch
-          const int r0 = tile_rows(2 * st + 2), r1 = tile_rows(2 * st + 3);
-          ks_t0 = r0 > 0 ? 2 * st + 2 : 0;
-          ks_t1 = r1 > 0 ? 2 * st + 3 : 0;
-          ks_r0 = r0 > 0 ? r0 : 1;
-          ks_r1 = r1 > 0 ? r1 : 1;
-          ks_b0 = lds_addr(s_tiles[2 - 2 * hs]);
-          ks_b1 = lds_addr(s_tiles[3 - 2 * hs]);
-          const int tt = 2 * st + kp;
-          if (compute && tt < n_tiles) {
-            tile_body(tt, s_tiles[2 * hs + kp], 0, 0, 0u);
-          } else {
-            stage_rows(ks_t0, ks_b0, ks_r0);
-            stage_rows(ks_t1, ks_b1, ks_r1);
-          }
+    if (bad || k_begin >= N) wait_vmem_lds<0>();   // no copy may outlive the workgroup
+    if (bad) {
+      // skipped sequence: zero output, lse = -inf (direct) or an empty partial
+      if (tid == 0 && rt == 0 && split == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_LEN);
+      if (row_ok && hh == 0 && chalf == 0 && (!a.fuse || split == 0)) {
+        if (DIRECT || a.fuse) {
+          a.lse[(int64_t)b * a.M + m] = -INFINITY;
+          T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
+          for (int d = 0; d < R; ++d) o[d] = (T)0.0f;
+        } else {
+          // (a skipped sequence has one split there: it writes them all)
+          for (int k = split; k < (fill_unused ? a.max_splits : split + 1); ++k)
+            a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
         }
       }
-      wait_vmem_lds<0>();
       continue;
     }
-    // The first tile, the query fragments and the visibility words are all
-    // waited for here, visibly to the compiler, so that it places no wait for
-    // them inside the loop (where it would also drain the tile copies).
-    if (pass == 0 && spec_ok) {
-      wait_vmem_lds<0>();                     // the speculative copies were right
-    } else {
-      wait_vmem_lds<0>();                     // speculative copies land before their buffers are reused
-      stage(0, lds_addr(s_tiles[0]));
-      if (n_tiles > 1) stage(1, lds_addr(s_tiles[1]));
-      else stage_rows(0, lds_addr(s_tiles[1]), 1);
+    if (!DIRECT && fill_unused && !a.fuse && split == 0 && row_ok && hh == 0 && chalf == 0 && kp == 0) {
+      for (int k = sr.ns; k < a.max_splits; ++k) a.part_lse[((int64_t)b * a.max_splits + k) * a.M + m] = -INFINITY;
     }
-#pragma unroll
-    for (int k = 2; k < NBUF - 1; ++k) {
-      if (k < n_tiles) stage(k, lds_addr(s_tiles[k]));
-      else stage_rows(0, lds_addr(s_tiles[k]), 1);
+    if (k_begin >= N) {
+      // this split does not exist for sequence b: an empty partial, so that a
+      // merge over all max_splits splits is always right
+      if (!DIRECT && !a.fuse && row_ok && hh == 0 && chalf == 0 && kp == 0)
+        a.part_lse[((int64_t)b * a.max_splits + split) * a.M + m] = -INFINITY;
+      continue;
     }
-#pragma unroll 1
-    for (int tile = 0; tile < n_tiles; tile += NBUF) {
+    const int k_end = sr.k_end;
+    const int n_tiles = (k_end - k_begin + kBN - 1) / kBN;
+    const bool spec_ok = spec && k_begin == k_spec && k_begin + 2 * kBN <= k_end;
+    if (k_begin != k_spec) {
+      // (adaptive splits of a shorter sequence: the speculative copies read
+      // other rows, and are waited for and replaced below)
+      rs_lat = make_rsrc(kv_lat + (int64_t)k_begin * lat_ss, (uint32_t)(span_of(k_begin) * lat_ss));
+      rs_pe = make_rsrc(kv_pe + (int64_t)k_begin * pe_ss, (uint32_t)(span_of(k_begin) * pe_ss));
+    }
+
+    auto stage = [&](int tile, uint32_t lds) { stage_rows(tile, lds, min(kBN, k_end - (k_begin + tile * kBN))); };
+    // The same copy, one wave-load at a time (pieces 0 .. NPIECE - 1), so that
+    // the copies can be issued between value MFMAs: a wave waiting for the
+    // texture unit to accept a copy then still has MFMAs in flight.
+    constexpr int LAT_PIECES = region_wave_loads<kBN, RC>();
+    constexpr int NPIECE = LAT_PIECES + region_wave_loads<kBN, PC>();
+    auto stage_piece = [&](int tile, int nrows, uint32_t lds, int piece) __attribute__((always_inline)) {
+      const uint32_t r0 = (uint32_t)(tile * kBN);
+      if (piece < LAT_PIECES)
+        stage_one<kBN, RC, KS>(rs_lat, r0 * lat_ss, lat_ss, nrows, lds, wave, lane, piece);
+      else
+        stage_one<kBN, PC>(rs_pe, r0 * pe_ss, pe_ss, nrows, lds + LAT_BYTES, wave, lane, piece - LAT_PIECES);
+    };
+
+
+
+    // Per-lane LDS byte offsets inside a tile buffer (bf16 only; the fp32 path
+    // computes its addresses inline).
+    //  * score operand, step c: chunk 2c + hh of key r.  With a swizzle over LSW
+    //    chunks, 2c + hh = LSW * (c / QB) + (2 * (c % QB) + hh) for QB = LSW / 2
+    //    and the swizzle only touches the second part, so the address is
+    //    qk_lat[c % QB] + 16 * LSW * (c / QB).
+    //  * value operand, transposing read: in each 16-lane group, lane 4e + q
+    //    loads columns d0 + 4q .. d0 + 4q + 3 of key k_e and lane j then holds
+    //    column d0 + j of keys k_0..k_3.  Operand row d = 32 * db + r; slots 0-3
+    //    are keys c_row(8c + 0..3, hh), slots 4-7 keys c_row(8c + 4..7, hh).
+    //    The 16-byte chunk is 4 * db + x with x < 4, and (4 db + x) ^ s =
+    //    4 (db ^ s2) + (x ^ s01) for s2 = s >> 2, s01 = s & 3; db ^ s2 only
+    //    changes the low two bits of db.  The keys are 16c + (8 half + 4 hh +
+    //    e) and the swizzle depends on the key modulo 16 only, so c moves the
+    //    address by whole 16-key blocks: pv_base[half][db % 4] + 64 * db +
+    //    c * (16 rows of the region).
+    constexpr int LSW = (RC % 16 == 0) ? 16 : 8;
+    constexpr int QB = LSW / 2;
+    int qk_lat[QB], qk_pe[4];
+    int pv_base[2][4];
+    if constexpr (KW == 8) {
+      static_assert(P / KMF <= 4 && RC % 8 == 0, "bf16 score addressing");
+      const int sr = swz_of<RC>(r);
 #pragma unroll
-      for (int k = 0; k < NBUF; ++k) {
-        const int t = tile + k;
-        if (t >= n_tiles) break;
-        wait_tile();
-        const bool real = t + NBUF - 1 < n_tiles;
-        const int st = real ? t + NBUF - 1 : t;
-        const int st_rows = real ? min(kBN, k_end - (k_begin + st * kBN)) : 1;
-        const uint32_t sb = lds_addr(s_tiles[(k + NBUF - 1) % NBUF]);
-        if (compute) tile_body(t, s_tiles[k], st, st_rows, sb);
-        else stage_rows(st, sb, st_rows);
+      for (int j = 0; j < QB; ++j) qk_lat[j] = r * RC * 16 + (((2 * j + hh) ^ sr) << 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)   // rope region: chunk 2j + hh exists only while it is < PC
+        qk_pe[j] = LAT_BYTES + region_off<PC>(r, (2 * j + hh) < PC ? (2 * j + hh) : 0);
+      const int g = lane >> 4, sl = lane & 15;
+      const int e = sl >> 2, qd = sl & 3;
+      const int x = 2 * (g & 1) + (qd >> 1);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int k = c_row(4 * half + e, hh);
+        const int sk = swz_of<RC>(k), s2 = sk >> 2, s01 = sk & 3;
+        const int base = k * RC * 16 + ((x ^ s01) << 4) + 8 * (qd & 1);
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) pv_base[half][d4] = base + 64 * ((d4 ^ s2) - d4);
       }
     }
-    wait_vmem_lds<0>();                       // the last (dummy) copies land before anything else
-  }
 
-  // Key streams: the two waves of a row block share the output, stream s
-  // writing column half s.  Each leaves the other half of its accumulators,
-  // its reference and its sum in the (now idle) tile ring for its partner,
-  // then rescales both streams to the larger reference as it writes its half
-  // (the partner's accumulators are read block by block in the loops below).
-  constexpr int XS = (NBL / 2 * 16 + 2) * 64; // floats per wave
-  float* xw = reinterpret_cast<float*>(&s_tiles[0][0]) + wave * XS;
-  const float* xr = reinterpret_cast<const float*>(&s_tiles[0][0]) + (wave ^ 1) * XS;
-  float f0 = 1.0f, f1 = 0.0f;
-  if constexpr (KS) {
-    tile_barrier();                           // every wave is done with the ring
+    // Visibility words from parent pointers, only where this split reaches the
+    // tree (keys L .. N - 1): every wave runs the pointer doubling for the
+    // sequence in its own LDS area and reads its tokens' rows.
+    auto derive_vis = [&]() {
+      if (!a.parents || k_end <= L) return;
+      uint64_t m0[2], m1[2];
+      const int va = KS ? 0 : wave;
+      if (!KS || wave == 0) {
+        const bool bad_tree = wave_ancestor_masks(par_v, a.q, s_vm[va], s_vj[va], lane, m0, m1);
+        if (__any(bad_tree) && lane == 0 && wave == 0) flag_seq(a.seq_status, b, KDT_SEQ_BAD_TREE);
+      }
+      if constexpr (KS) {
+        wait_lds();
+        tile_barrier();
+      }
+      if (row_ok) {
+        vw0 = s_vm[va][2 * t];
+        vw1 = s_vm[va][2 * t + 1];
+      }
+    };
+
+    if constexpr (Q_VIA_LDS) {
+      if (q_lds) {
+        // the query copies (and the first tiles, issued before them) have landed
+        wait_vmem_lds<0>();
+        tile_barrier();
+        derive_vis();
+        const char* qbuf = s_tiles[2 + rb];
 #pragma unroll
-    for (int db = NBL / 2; db < NBL; ++db) {  // (blocks 0-7 are the half this wave keeps)
-      // straight from the accumulation registers; the four groups of block
-      // db sit 1 KB apart, each lane's 16 bytes consecutive across lanes
-      const uint32_t ad = lds_addr(xw + (((db & 7) * 4) * 64 + lane) * 4);
-      asm volatile(
-          "ds_write_b128 %0, %1\n\t"
-          "ds_write_b128 %0, %2 offset:1024\n\t"
-          "ds_write_b128 %0, %3 offset:2048\n\t"
-          "ds_write_b128 %0, %4 offset:3072"
-          :
-          : "v"(ad), "a"(__builtin_shufflevector(acc[db], acc[db], 0, 1, 2, 3)),
-            "a"(__builtin_shufflevector(acc[db], acc[db], 4, 5, 6, 7)),
-            "a"(__builtin_shufflevector(acc[db], acc[db], 8, 9, 10, 11)),
-            "a"(__builtin_shufflevector(acc[db], acc[db], 12, 13, 14, 15))
-          : "memory");
-      __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < NCHUNK; ++c) {
+          const char* src = (c < R / KMF) ? qbuf + qk_lat[c % QB] + 16 * LSW * (c / QB) : qbuf + qk_pe[c - R / KMF];
+          if constexpr (KS) {
+            if (c < NQF) qf[c] = *reinterpret_cast<const frag*>(src);
+            else if (kp == 0)
+              *reinterpret_cast<frag*>(s_qpe + ((rb * NQR + (c - NQF)) * 64 + lane) * 16) =
+                  *reinterpret_cast<const frag*>(src);
+          } else {
+            qf[c] = *reinterpret_cast<const frag*>(src);
+          }
+        }
+        // every wave has its fragments before the buffers take key tiles again
+        wait_vmem_lds<0>();
+        tile_barrier();
+      }
     }
-    xw[NBL / 2 * 16 * 64 + lane] = m_ref;
-    xw[NBL / 2 * 16 * 64 + 64 + lane] = l_run;
-    wait_lds();                               // (also the asm stores above)
-    tile_barrier();
-    const float m1 = xr[NBL / 2 * 16 * 64 + lane], l1 = xr[NBL / 2 * 16 * 64 + 64 + lane];
-    const float mt = fmaxf(m_ref, m1);
-    f0 = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - mt);
-    f1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - mt);
-    l_run = l_run * f0 + l1 * f1;
-    m_ref = mt;
-  }
-  // the accumulator blocks this wave writes (key streams: blocks 0-7, its
-  // column half)
-  auto own_block = [&](int db) { return !KS || db < NBL / 2; };
-  // ---- epilogue: normalise and write (direct) or write the partial
-  const float l_tot = xhalf_sum(l_run);
-  const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_v = l_tot > 0.0f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
-  // key streams: the normalisation folded into the two streams' factors
-  f0 *= inv;
-  f1 *= inv;
-  // normalised output (db, 4 g + e) of this lane, both key streams combined
-  auto out_of = [&](int db, int g, f32x4& v) __attribute__((always_inline)) {
-    if constexpr (KS) {
-      // the partner's accumulator block db + 8 (the same output columns)
-      const f32x4 o = *reinterpret_cast<const f32x4*>(xr + (((db & 7) * 4 + g) * 64 + lane) * 4);
+    if (!q_lds) derive_vis();
+
+    f32x16 acc[NBL];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * f0 + o[e] * f1;
-    } else {
+    for (int i = 0; i < NBL; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * inv;
-    }
-  };
-  // a sequence with one split needs no merge: the fused launch writes its
-  // output directly too
-  const int ns_b = sr.ns;
-  const bool direct_now = DIRECT || (a.fuse && ns_b == 1);
-  if (direct_now) {
-    if (row_ok) {
-      T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
+      for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+    // Softmax state of this lane's row (log2 domain).  m_ref is the reference
+    // the weights are taken against: fixed at the first tile with a visible key,
+    // it never moves while weights stay below 2^kRefSlack, so the accumulators
+    // are never rescaled.  m_max is the true running max.  If some row's max
+    // outgrows its reference by more than that, the wave's accumulation is void
+    // ("dead"): it keeps running its tiles (the copy schedule is shared by all
+    // waves) and tracking m_max, then redoes the split once with m_ref = m_max
+    // (the exact max), which cannot trigger again, discarding what it summed.
+    float m_ref = -INFINITY, m_max = -INFINITY;
+    float l_run = 0.0f;           // this lane's share of sum_j exp2(s_j - m_ref)
+    bool dead = false;            // wave-uniform
+
+    // One key tile: scores, softmax, value contraction.  `buf` is the tile's
+    // ring buffer; the tile's first key is kt.  The copy of the first st_rows
+    // rows of tile st_tile into st_buf is issued piece by piece between the
+    // value MFMAs.
+    // Key streams: the next pair of tiles (copied between this step's score
+    // MFMAs; rows 0 = no such tile).
+    int ks_t0 = 0, ks_t1 = 0, ks_r0 = 0, ks_r1 = 0;
+    // Key streams: accumulator block db of stream kp holds output column block
+    // col_block(db) = (db + 8 kp) mod 16, so that every wave keeps blocks 0-7
+    // and hands blocks 8-15 to its partner at the end (register indices fixed
+    // at compile time on both streams); the value operand of block db is read
+    // at LDS offset 64 db + rot_off[db >= 8] instead of 64 col_block(db).
+    const int rot_off[2] = {512 * kp, -512 * kp};
+    auto col_block = [&](int db) { return KS ? ((db + 8 * kp) & 15) : chalf * NBL + db; };
+    uint32_t ks_b0 = 0, ks_b1 = 0;          // (LDS addresses)
+    auto tile_body = [&](const int tile, const char* buf, const int st_tile, const int st_rows, uint32_t st_buf)
+                         __attribute__((always_inline)) {
+      const int kt = k_begin + tile * kBN;
+      // ---- scores S^T[key][row]: A = K tile (the lane's key is r), B = Q^T.
+      // The K fragments are read QPF steps ahead of the MFMA chain.
+      auto score_src = [&](int c) __attribute__((always_inline)) -> const char* {
+        if constexpr (KW == 8) {
+          // bf16: step c reads 16-byte chunk 2c + hh of the row
+          if (c < R / KMF) return buf + qk_lat[c % QB] + 16 * LSW * (c / QB);
+          return buf + qk_pe[c - R / KMF];
+        } else {
+          const int byte = (c * KMF + hh * KW) * (int)sizeof(T);   // byte offset inside the row
+          if (c < R / KMF) return buf + region_off<RC>(r, byte >> 4) + (byte & 15);
+          return buf + LAT_BYTES + region_off<PC>(r, (byte >> 4) - RC) + (byte & 15);
+        }
+      };
+      // (key streams hold no accumulator block in LDS, so their scores take
+      // registers and the operand queues are shorter)
+      constexpr int QPF0 = QPE ? 2 : KDT_SCORE_PREFETCH;
+      constexpr int QPF = NSTEP < QPF0 ? NSTEP : QPF0;
+      frag kf[QPF];
 #pragma unroll
-      for (int db = 0; db < NBL; ++db) {
-        if (!own_block(db)) continue;
+      for (int j = 0; j < QPF; ++j) kf[j] = *reinterpret_cast<const frag*>(score_src(c0 + j));
+      // this row block's rope fragments of the query, read from LDS QPF steps
+      // before their MFMA
+      auto qpe_src = [&](int i) { return reinterpret_cast<const frag*>(s_qpe + ((rb * NQR + i) * 64 + lane) * 16); };
+      frag qq[QPE ? QPF : 1];
+      f32x16 s;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+      // (bf16: the tile stays in VGPRs; see Mfma<__bf16>::mma_acc_v.  Not in
+      // the balanced 64-row kernel, where the compiler parks query fragments in
+      // accumulation registers and copies them back right before their MFMA.)
+      auto score_mma = [&](const frag& x, const frag& y, int j) __attribute__((always_inline)) {
+        if constexpr (SCORE_VGPR) {
+          if (j == 0) s = MM::mma_first_v(x, y);
+          else MM::mma_acc_v(x, y, s);
+        } else {
+          s = MM::mma(x, y, s);
+        }
+      };
+#pragma unroll
+      for (int j = 0; j < NSTEP; ++j) {
+        const frag cur = kf[j % QPF];
+        if (j + QPF < NSTEP) kf[j % QPF] = *reinterpret_cast<const frag*>(score_src(c0 + j + QPF));
+        if constexpr (QPE) {
+          static_assert(!QPE || NQF >= QPF, "rope fragments are queued behind the register ones");
+          // the slot refilled now is the one this step consumes: take it first
+          const frag qcur = j < NQF ? qf[j < NQF ? j : 0] : qq[j % QPF];
+          if (j + QPF >= NQF && j + QPF < NSTEP) qq[(j + QPF) % QPF] = *qpe_src(j + QPF - NQF);
+          score_mma(cur, qcur, j);
+        } else {
+          score_mma(cur, qf[j], j);
+        }
+        fence_mem_mfma();
+        if constexpr (KS) {
+          // the next pair's copies, one wave-load at a time between these MFMAs
+          constexpr int NP2 = 2 * NPIECE;
+#pragma unroll
+          for (int pc = j * NP2 / NSTEP; pc < (j + 1) * NP2 / NSTEP; ++pc) {
+            if (pc < NPIECE) stage_piece(ks_t0, ks_r0, ks_b0, pc);
+            else stage_piece(ks_t1, ks_r1, ks_b1, pc - NPIECE);
+          }
+        }
+      }
+      if constexpr (SCORE_VGPR) MM::score_ready(s);
+      if constexpr (DS) {
+        // add the partner's half of the contraction (the pair's waves hold the
+        // same rows and keys; a + b is the same on both)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) s_sx[(wave * 4 + g) * 64 + lane] = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
+        wait_lds();
+        tile_barrier();
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 av;
-          out_of(db, g, av);
-          const float v4[4] = {av[0], av[1], av[2], av[3]};
-          store4<T>(o + col_block(db) * 32 + 8 * g + 4 * hh, v4);
+          const f32x4 o = s_sx[((wave ^ 1) * 4 + g) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * g + e] += o[e];
         }
-        if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
       }
-      if (hh == 0 && chalf == 0 && kp == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
-    }
-  } else if (!DIRECT) {
-    if (row_ok) {
-      // Partials stay in accumulator order: the wave's 32 rows form one block
-      // of 32 x R values in which every store instruction writes one contiguous
-      // 1 KB run (float32: register group (db, g) of every lane; bf16: groups
-      // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).  Streaming,
-      // device-coherent stores: the merge reads them from other compute units.
-      const int blk = rt * (BM / 32) + rb;
-      const int64_t base = (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R);
-      if (a.part_bf16) {
-        __bf16* o = static_cast<__bf16*>(a.part_o) + base;
-#pragma unroll
-        for (int db = 0; db < NBL; ++db) {
-          if (!own_block(db)) continue;
-#pragma unroll
-          for (int gp = 0; gp < 2; ++gp) {
-            f32x4 a0, a1;
-            out_of(db, 2 * gp, a0);
-            out_of(db, 2 * gp + 1, a1);
-            bf16x8 v8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v8[e] = (__bf16)a0[e];
-              v8[4 + e] = (__bf16)a1[e];
-            }
-            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (2 * col_block(db) + gp)), v8);
-          }
-          if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+      // Value operand of contraction step c (16 keys), output block db.
+      auto value_frag = [&](int c, int db) __attribute__((always_inline)) -> frag {
+        if constexpr (KW == 1) {
+          // fp32: lane (r, hh) needs V[key c_row(c, hh)][32*db + r]
+          const int col = ((chalf * NBL + db) * 32 + r) * (int)sizeof(T);
+          return *reinterpret_cast<const T*>(buf + region_off<RC>(c_row(c, hh), col >> 4) + (col & 15));
+        } else {
+          // bf16: two transposing reads (lane bases computed before the loop)
+          const int dg = chalf * NBL + db;      // output column block (key streams: rotated, below)
+          const int o = (KS ? 64 * db + rot_off[db >= NBL / 2] : 64 * dg) + c * 16 * RC * 16;
+          const bf16x4 lo = lds_read_tr16(buf + pv_base[0][dg & 3] + o);
+          const bf16x4 hi = lds_read_tr16(buf + pv_base[1][dg & 3] + o);
+          return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+      };
+      constexpr int STEPS = PV_STEPS * NBL;
+      constexpr int VPF = STEPS < KDT_VALUE_PREFETCH ? STEPS : KDT_VALUE_PREFETCH;
+      // The first value operands are requested now, so their LDS latency
+      // passes during the softmax instead of stalling the first value MFMA.
+      frag vq[VPF + 1];
+#pragma unroll
+      for (int i = 0; i < VPF; ++i) vq[i] = value_frag(i / NBL, i % NBL);
+
+      // ---- online softmax for this lane's row (16 of the tile's 32 keys)
+      // Raw scores; the scale (positive) is applied to the row max and folded
+      // into each weight's exponent, one fused multiply-add per weight.
+      float sv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = s[v];
+      if (kt + kBN > L || kt + kBN > k_end) {   // only tiles reaching the tree or the split end
+        // (an empty volatile asm: without it the compiler turns this branch
+        // into selects that every tile then executes, some 200 instructions
+        // between the score and the value MFMAs)
+        asm volatile("");
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = kt + c_row(v, hh);
+          const int uu = kk - L;                                  // tree node if >= 0
+          const uint64_t w = uu < 64 ? vw0 : vw1;
+          const bool tree_ok = uu < 0 || ((w >> (uu & 63)) & 1ull);
+          sv[v] = (kk < k_end && tree_ok) ? sv[v] : -INFINITY;
+        }
+      }
+      auto tile_max = [&]() __attribute__((always_inline)) {
+        float x = sv[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) x = fmaxf(x, sv[v]);
+        return xhalf_max(x) * a.scale_log2;
+      };
+      // Only tiles where some row of the wave still lacks its reference take
+      // this (uniform) branch: the row's running max, this tile included, sets
+      // it.  Elsewhere the weights depend on the fixed reference alone.
+      if (__any(m_ref == -INFINITY)) {
+        const float mx0 = tile_max();
+        if (m_ref == -INFINITY) m_ref = fmaxf(m_max, mx0);   // first visible key of this row
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], a.scale_log2, -m_use));
+        l_run += p[v];
+      }
+      // The running max and the check against the reference feed no weight of
+      // this tile, and no branch: they can overlap the value MFMAs.  A wave
+      // whose scores outgrow its reference records it in `dead`, which is read
+      // after the last tile.
+      m_max = fmaxf(m_max, tile_max());
+      dead = dead || __any(m_max > m_ref + kRefSlack);
+
+      // ---- O^T[d][row] += V^T[d][key] * P^T[key][row]; the value operand of
+      // step i + VPF is read while step i's MFMA is issued (the first VPF were
+      // requested before the softmax).
+      frag pfr[PV_STEPS];
+#pragma unroll
+      for (int c = 0; c < PV_STEPS; ++c) pfr[c] = MM::pack(p + c * KW);
+#pragma unroll
+      for (int i = 0; i < STEPS; ++i) {
+        const int c = i / NBL, db = i % NBL;
+        if (i + VPF < STEPS) vq[(i + VPF) % (VPF + 1)] = value_frag((i + VPF) / NBL, (i + VPF) % NBL);
+        acc[db] = MM::mma(vq[i % (VPF + 1)], pfr[c], acc[db]);
+        fence_mem_mfma();
+        // copy pieces [i * NPIECE / STEPS, (i + 1) * NPIECE / STEPS) follow this MFMA
+        if constexpr (!KS) {
+#pragma unroll
+          for (int pc = i * NPIECE / STEPS; pc < (i + 1) * NPIECE / STEPS; ++pc)
+            stage_piece(st_tile, st_rows, st_buf, pc);
+        }
+      }
+    };
+
+    if (tid == 0) s_dead = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1) {
+        if (dead) s_dead = 1;
+        __syncthreads();
+        if (s_dead == 0) break;                 // common case: no redo
+        // Depth split: every wave takes part in the score exchange (a
+        // workgroup barrier), so all waves redo the split; rows that did not
+        // outgrow their reference recompute the same sums.
+        if (dead || DS) {
+#pragma unroll
+          for (int i = 0; i < NBL; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+          l_run = 0.0f;
+          if (dead) m_ref = m_max;
+        }
+      }
+      const bool compute = (pass == 0) || dead || DS;
+      dead = false;
+      // Tiles rotate through the NBUF buffers: the step for tile t waits for its
+      // copy and computes, issuing between its value MFMAs the copy of tile
+      // t + NBUF - 1 into the buffer the previous step has finished reading.
+      // Every step issues exactly one copy: once no tile is left, a dummy copy
+      // (row 0 of tile t, re-read into every row) goes to that buffer, which no
+      // later tile uses.  So exactly NBUF - 2 copies are always younger than the
+      // one a step waits for, and one wait count serves every step.
+      auto wait_tile = [&]() __attribute__((always_inline)) {
+        wait_vmem_lds<STAGE_LOADS * (NBUF - 2)>();
+        tile_barrier();
+      };
+      if constexpr (KS) {
+        // Key streams: step s computes tiles 2s (waves of stream 0) and 2s + 1
+        // (stream 1) from one buffer pair while the next pair's copies go to
+        // the other pair of buffers, which the step before has finished
+        // reading.  Each step waits for all of its own copies and meets the
+        // workgroup at one barrier, after which every copy of the pair has
+        // landed and every wave is done with the previous pair.
+        if (pass == 0 && spec_ok) {
+          wait_vmem_lds<0>();
+        } else {
+          wait_vmem_lds<0>();
+          stage(0, lds_addr(s_tiles[0]));
+          if (n_tiles > 1) stage(1, lds_addr(s_tiles[1]));
+        }
+        const int n_steps = (n_tiles + 1) / 2;
+        auto tile_rows = [&](int tt) { return tt < n_tiles ? min(kBN, k_end - (k_begin + tt * kBN)) : 0; };
+#pragma unroll 1
+        for (int s0 = 0; s0 < n_steps; s0 += 2) {
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const int st = s0 + hs;
+            if (st >= n_steps) break;
+            wait_vmem_lds<0>();
+            tile_barrier();
+            // the next pair; past the last tile a dummy copy (row 0 of tile 0,
+            // always inside the split) goes to a buffer no later step reads,
+            // so the copies between the score MFMAs need no branch
+            const int r0 = tile_rows(2 * st + 2), r1 = tile_rows(2 * st + 3);
+            ks_t0 = r0 > 0 ? 2 * st + 2 : 0;
+            ks_t1 = r1 > 0 ? 2 * st + 3 : 0;
+            ks_r0 = r0 > 0 ? r0 : 1;
+            ks_r1 = r1 > 0 ? r1 : 1;
+            ks_b0 = lds_addr(s_tiles[2 - 2 * hs]);
+            ks_b1 = lds_addr(s_tiles[3 - 2 * hs]);
+            const int tt = 2 * st + kp;
+            if (compute && tt < n_tiles) {
+              tile_body(tt, s_tiles[2 * hs + kp], 0, 0, 0u);
+            } else {
+              stage_rows(ks_t0, ks_b0, ks_r0);
+              stage_rows(ks_t1, ks_b1, ks_r1);
+            }
+          }
+        }
+        wait_vmem_lds<0>();
+        continue;
+      }
+      // The first tile, the query fragments and the visibility words are all
+      // waited for here, visibly to the compiler, so that it places no wait for
+      // them inside the loop (where it would also drain the tile copies).
+      if (pass == 0 && spec_ok) {
+        wait_vmem_lds<0>();                     // the speculative copies were right
       } else {
-        float* o = static_cast<float*>(a.part_o) + base;
+        wait_vmem_lds<0>();                     // speculative copies land before their buffers are reused
+        stage(0, lds_addr(s_tiles[0]));
+        if (n_tiles > 1) stage(1, lds_addr(s_tiles[1]));
+        else stage_rows(0, lds_addr(s_tiles[1]), 1);
+      }
+#pragma unroll
+      for (int k = 2; k < NBUF - 1; ++k) {
+        if (k < n_tiles) stage(k, lds_addr(s_tiles[k]));
+        else stage_rows(0, lds_addr(s_tiles[k]), 1);
+      }
+#pragma unroll 1
+      for (int tile = 0; tile < n_tiles; tile += NBUF) {
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k) {
+          const int t = tile + k;
+          if (t >= n_tiles) break;
+          wait_tile();
+          const bool real = t + NBUF - 1 < n_tiles;
+          const int st = real ? t + NBUF - 1 : t;
+          const int st_rows = real ? min(kBN, k_end - (k_begin + st * kBN)) : 1;
+          const uint32_t sb = lds_addr(s_tiles[(k + NBUF - 1) % NBUF]);
+          if (compute) tile_body(t, s_tiles[k], st, st_rows, sb);
+          else stage_rows(st, sb, st_rows);
+        }
+      }
+      wait_vmem_lds<0>();                       // the last (dummy) copies land before anything else
+    }
+
+    // Key streams: the two waves of a row block share the output, stream s
+    // writing column half s.  Each leaves the other half of its accumulators,
+    // its reference and its sum in the (now idle) tile ring for its partner,
+    // then rescales both streams to the larger reference as it writes its half
+    // (the partner's accumulators are read block by block in the loops below).
+    constexpr int XS = (NBL / 2 * 16 + 2) * 64; // floats per wave
+    float* xw = reinterpret_cast<float*>(&s_tiles[0][0]) + wave * XS;
+    const float* xr = reinterpret_cast<const float*>(&s_tiles[0][0]) + (wave ^ 1) * XS;
+    float f0 = 1.0f, f1 = 0.0f;
+    if constexpr (KS) {
+      tile_barrier();                           // every wave is done with the ring
+#pragma unroll
+      for (int db = NBL / 2; db < NBL; ++db) {  // (blocks 0-7 are the half this wave keeps)
+        // straight from the accumulation registers; the four groups of block
+        // db sit 1 KB apart, each lane's 16 bytes consecutive across lanes
+        const uint32_t ad = lds_addr(xw + (((db & 7) * 4) * 64 + lane) * 4);
+        asm volatile(
+            "ds_write_b128 %0, %1\n\t"
+            "ds_write_b128 %0, %2 offset:1024\n\t"
+            "ds_write_b128 %0, %3 offset:2048\n\t"
+            "ds_write_b128 %0, %4 offset:3072"
+            :
+            : "v"(ad), "a"(__builtin_shufflevector(acc[db], acc[db], 0, 1, 2, 3)),
+              "a"(__builtin_shufflevector(acc[db], acc[db], 4, 5, 6, 7)),
+              "a"(__builtin_shufflevector(acc[db], acc[db], 8, 9, 10, 11)),
+              "a"(__builtin_shufflevector(acc[db], acc[db], 12, 13, 14, 15))
+            : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      xw[NBL / 2 * 16 * 64 + lane] = m_ref;
+      xw[NBL / 2 * 16 * 64 + 64 + lane] = l_run;
+      wait_lds();                               // (also the asm stores above)
+      tile_barrier();
+      const float m1 = xr[NBL / 2 * 16 * 64 + lane], l1 = xr[NBL / 2 * 16 * 64 + 64 + lane];
+      const float mt = fmaxf(m_ref, m1);
+      f0 = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - mt);
+      f1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - mt);
+      l_run = l_run * f0 + l1 * f1;
+      m_ref = mt;
+    }
+    // the accumulator blocks this wave writes (key streams: blocks 0-7, its
+    // column half)
+    auto own_block = [&](int db) { return !KS || db < NBL / 2; };
+    // ---- epilogue: normalise and write (direct) or write the partial
+    const float l_tot = xhalf_sum(l_run);
+    const float m_fin = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse_v = l_tot > 0.0f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
+    // key streams: the normalisation folded into the two streams' factors
+    f0 *= inv;
+    f1 *= inv;
+    // normalised output (db, 4 g + e) of this lane, both key streams combined
+    auto out_of = [&](int db, int g, f32x4& v) __attribute__((always_inline)) {
+      if constexpr (KS) {
+        // the partner's accumulator block db + 8 (the same output columns)
+        const f32x4 o = *reinterpret_cast<const f32x4*>(xr + (((db & 7) * 4 + g) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * f0 + o[e] * f1;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * inv;
+      }
+    };
+    // a sequence with one split needs no merge: the fused launch writes its
+    // output directly too
+    const int ns_b = sr.ns;
+    const bool direct_now = DIRECT || (a.fuse && ns_b == 1);
+    if (direct_now) {
+      if (row_ok) {
+        T* o = reinterpret_cast<T*>(a.out) + b * a.out_sb + t * a.out_st + h * a.out_sh;
 #pragma unroll
         for (int db = 0; db < NBL; ++db) {
           if (!own_block(db)) continue;
@@ -1765,20 +1720,65 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
           for (int g = 0; g < 4; ++g) {
             f32x4 av;
             out_of(db, g, av);
-            store16_coherent(o, (uint32_t)(16 * lane + 1024 * (4 * col_block(db) + g)), av);
+            const float v4[4] = {av[0], av[1], av[2], av[3]};
+            store4<T>(o + col_block(db) * 32 + 8 * g + 4 * hh, v4);
           }
-          if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+          if constexpr (KS) __builtin_amdgcn_sched_barrier(0);   // one block's partner values at a time
+        }
+        if (hh == 0 && chalf == 0 && kp == 0) a.lse[(int64_t)b * a.M + m] = lse_v;
+      }
+    } else if (!DIRECT) {
+      if (row_ok) {
+        // Partials stay in accumulator order: the wave's 32 rows form one block
+        // of 32 x R values in which every store instruction writes one contiguous
+        // 1 KB run (float32: register group (db, g) of every lane; bf16: groups
+        // (db, 2p) and (db, 2p + 1) packed into 16 bytes per lane).  Streaming,
+        // device-coherent stores: the merge reads them from other compute units.
+        const int blk = rt * (BM / 32) + rb;
+        const int64_t base = (((int64_t)b * a.max_splits + split) * a.n_blk + blk) * (32 * R);
+        if (a.part_bf16) {
+          __bf16* o = static_cast<__bf16*>(a.part_o) + base;
+#pragma unroll
+          for (int db = 0; db < NBL; ++db) {
+            if (!own_block(db)) continue;
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              f32x4 a0, a1;
+              out_of(db, 2 * gp, a0);
+              out_of(db, 2 * gp + 1, a1);
+              bf16x8 v8;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v8[e] = (__bf16)a0[e];
+                v8[4 + e] = (__bf16)a1[e];
+              }
+              store16_coherent(o, (uint32_t)(16 * lane + 1024 * (2 * col_block(db) + gp)), v8);
+            }
+            if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          float* o = static_cast<float*>(a.part_o) + base;
+#pragma unroll
+          for (int db = 0; db < NBL; ++db) {
+            if (!own_block(db)) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 av;
+              out_of(db, g, av);
+              store16_coherent(o, (uint32_t)(16 * lane + 1024 * (4 * col_block(db) + g)), av);
+            }
+            if constexpr (KS) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
+      if (row_ok && hh == 0 && chalf == 0 && kp == 0)
+        __hip_atomic_store(a.part_lse + ((int64_t)b * a.max_splits + split) * a.M + m, lse_v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (a.fuse) {
+        fused_merge<T, R>(a, b, rt, split, ns_b, BM, reinterpret_cast<float*>(&s_tiles[0][0]), tid);
+      }
     }
-    if (row_ok && hh == 0 && chalf == 0 && kp == 0)
-      __hip_atomic_store(a.part_lse + ((int64_t)b * a.max_splits + split) * a.M + m, lse_v, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    if (a.fuse) {
-      fused_merge<T, R>(a, b, rt, split, ns_b, BM, reinterpret_cast<float*>(&s_tiles[0][0]), tid);
-    }
-  }
-  }   // pieces
+  }  // pieces
 }
 
 // WIDE: one (sequence, block, column group) per workgroup; used when there
