@@ -17,7 +17,7 @@
 //   Both run on v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32
 //   (fp32).
 // * A workgroup is 4 waves (one per SIMD) and owns a tile of rows of one
-//   sequence and one split of its key range, in one of three layouts:
+//   sequence and one split of its key range, in one of four layouts:
 //   1: 128 rows, each wave 32 rows and all R output columns (its latent Q
 //      fragments in registers for the whole key loop, its rope fragments
 //      read from LDS every tile, its 32 x R fp32 accumulators in the
@@ -53,18 +53,25 @@
 //   segment or the end of the split test bits.  The visibility words come from
 //   the caller, or, given parent pointers, from a pointer doubling that the
 //   workgroups whose split reaches the tree run before their key loop.
-// * Split-prefix: a sequence's keys are cut into splits of split_keys keys;
-//   each split writes a normalised partial (bf16 for bf16 inputs, float32 on
-//   request, with streaming stores) and its log-sum-exp, and the merge kernel
-//   recombines them.  With a single split the verify kernel writes the final
-//   output directly.
+// * Split-prefix: a sequence's keys are cut into splits (fixed size, or
+//   adaptive: in proportion to the sequence's length); each split writes a
+//   normalised partial (bf16 for bf16 inputs, float32 on request, with
+//   streaming stores) and its log-sum-exp, and the merge kernel recombines
+//   them.  With a single split the verify kernel writes the final output
+//   directly.  The balanced schedule instead cuts all sequences' key tiles,
+//   laid end to end, into equal ranges, one per gang of workgroups, which
+//   walk from one sequence into the next (bal_init / bal_next).
 // * Workgroup indices are remapped so the workgroups on one XCD take
-//   consecutive work units (all row tiles of one key split), which keeps
-//   their shared K/V stream in that XCD's L2.
+//   consecutive work units (all row tiles of one key split, or one gang),
+//   which keeps their shared K/V stream in that XCD's L2.
+// * The score MFMAs are inline asm with a VGPR destination (see
+//   Mfma<__bf16>::mma_acc_v); the build scans the compiled code for the one
+//   operand hazard the compiler does not guard there.
 #include <math.h>
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "kdt_common.hpp"
