@@ -222,3 +222,19 @@ def test_noalloc_with_balanced_schedule():
                                      schedule=2)
     o2, l2 = _run(g, total_prefix_len=hint, schedule=2)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("B,H,q,lens", [(1, 1, 128, [300]),          # one row tile, the widest tree
+                                        (3, 3, 100, [0, 40, 700]),    # a ragged row tile, an empty prefix
+                                        (2, 16, 65, [4096, 1]),
+                                        (5, 8, 9, [31, 32, 33, 64, 65])])   # lengths around the key tile
+@pytest.mark.parametrize("layout", [1, 2])
+def test_odd_shapes(B, H, q, lens, layout):
+    cfg = synth.Config("balanced_odd", 76, "bf16", B=B, H=H, R=512, P=64, q_len=q,
+                       prefix=("fixed", max(lens)), tree="uniform")
+    inp = synth.generate(cfg)
+    inp.prefix_lens[:] = np.asarray(lens, np.int32)
+    g = GpuInputs(inp)
+    for gang in (0, 1):
+        o, l = _run(g, total_prefix_len=int(sum(lens)), layout=layout, schedule=2, gang_size=gang)
+        _check_full(inp, o, l, f"B={B} H={H} q={q} lens={lens} layout {layout} gang {gang}")
