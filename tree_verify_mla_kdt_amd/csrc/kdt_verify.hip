@@ -572,7 +572,12 @@ __device__ __forceinline__ SplitRange split_range(int n_keys, int split, int spl
     r.k_end = min(n_keys, r.k_begin + split_keys);
   } else {
     const uint32_t T = (uint32_t)(n_keys - 1) / kBN + 1u;
-    const uint32_t want = (uint32_t)(((uint64_t)T * (uint64_t)max_splits + tiles_max - 1) / (uint64_t)tiles_max);
+    // (32-bit whenever T * max_splits + tiles_max fits: the 64-bit quotient is
+    // about 150 scalar instructions)
+    const uint32_t ms = (uint32_t)max_splits, tm = (uint32_t)tiles_max;
+    const uint32_t want = T <= (0xFFFFFFFFu - tm) / ms
+                              ? (T * ms + tm - 1u) / tm
+                              : (uint32_t)(((uint64_t)T * (uint64_t)ms + tm - 1) / (uint64_t)tm);
     const uint32_t tps = (T - 1) / max(want, 1u) + 1u;
     r.ns = (int)((T - 1) / tps + 1u);
     r.k_begin = (int)min((uint32_t)split * tps, T) * kBN;
@@ -1051,7 +1056,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_split_kernel(VerifyArgs a_
       } else {
         const int u = xcd_remap(blockIdx.x, gridDim.x);
         pc.rt = u % a.n_rt;
-        const int g = (int)((int64_t)(u / a.n_rt) * a.group_mul % ((int64_t)a.B * a.max_splits));
+        // (32-bit arithmetic whenever the product cannot overflow: the 64-bit
+        // remainder is about 150 scalar instructions before the first copy)
+        const int n_grp = a.B * a.max_splits, gq = u / a.n_rt;
+        const int g = n_grp <= 46340 ? (int)((uint32_t)gq * (uint32_t)a.group_mul % (uint32_t)n_grp)
+                                     : (int)((int64_t)gq * a.group_mul % n_grp);
         pc.split = g % a.max_splits;
         pc.b = g / a.max_splits;
         pc.L = 0;
@@ -1800,12 +1809,15 @@ __global__ __launch_bounds__(256) void merge_kernel(
   __shared__ float s_st[WIDE ? 4 * (NV + 2) * 64 : 1];
   const int n_cg = R / (2 * NV);
   const int wave = threadIdx.x >> 6;
-  const int64_t wid = WIDE ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  // (the host keeps the item count under 2^31, so the item index and its
+  // decomposition are 32-bit: 64-bit divisions would put a few hundred scalar
+  // instructions before the first load)
+  const uint32_t wid = WIDE ? blockIdx.x : blockIdx.x * (blockDim.x >> 6) + (uint32_t)wave;
   const int lane = threadIdx.x & 63;
-  if (wid >= (int64_t)B * n_blk * n_cg) return;  // (uniform over the workgroup when WIDE)
-  const int cg = (int)(wid % n_cg);
-  const int64_t bblk = wid / n_cg;
-  const int blk = (int)(bblk % n_blk), b = (int)(bblk / n_blk);
+  if (wid >= (uint32_t)B * (uint32_t)n_blk * (uint32_t)n_cg) return;  // (uniform over the workgroup when WIDE)
+  const int cg = (int)(wid % (uint32_t)n_cg);
+  const uint32_t bblk = wid / (uint32_t)n_cg;
+  const int blk = (int)(bblk % (uint32_t)n_blk), b = (int)(bblk / (uint32_t)n_blk);
   const int M = q * H;
   int ns = max_splits;
   if (split_keys > 0) {
@@ -2197,7 +2209,7 @@ static int launch_merge_t(int dtype, int B, int q, int H, int R, const PT* po, c
   // more splits than one wave loads in one round trip: a workgroup per item
   const bool wide = max_splits > 16;
   const int64_t grid = wide ? items : (items + 3) / 4;
-  if (grid > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
+  if (items > 0x7FFFFFFF) return KDT_ERR_UNSUPPORTED;
   // splits per round trip: the fewest of 4, 8 and 16 that hold every split
   // (the sums then run in the same order whatever the choice)
   const int u = wide ? 16 : (max_splits <= 4 ? 4 : (max_splits <= 8 ? 8 : 16));
