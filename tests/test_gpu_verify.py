@@ -402,6 +402,28 @@ def test_many_sequences_more_workgroups_than_units(layout):
         check_close("bf16", o, ro, l, rl, f"B=257 layout={layout} split_keys={sk}")
 
 
+def test_group_order_past_32_bit_products():
+    """More than 46340 (sequence, split) groups: the product behind the order
+    in which workgroups visit the groups no longer fits in 32 bits and the
+    kernel takes its 64-bit path; sampled rows across the batch, the last
+    sequences included, must still match the oracle."""
+    cfg = small_cfg(q=1, H=16, R=64, P=16, tree="chain", prefix=("uniform", 1, 512), B=2728, index=402)
+    inp = synth.generate(cfg)
+    inp.prefix_lens[-1] = 512                      # the longest length sets the split count
+    g = GpuInputs(inp)
+    d, _, _ = kdt._verify_prepare(g.q_lat, g.q_pe, g.c_kv, g.k_pe, g.prefix_lens, None, cfg.softmax_scale,
+                                  g.max_prefix_len, None, None, None, 32, parents=g.parents)
+    p = kdt.verify_plan(d)
+    assert p.max_splits * cfg.B > 46340 and p.gang_size == 0
+    o, l = run_gpu(g, split_keys=32)
+    rows = sorted(set(sample_rows(inp, 96, seed=7)) | {(b, 0, h) for b in (cfg.B - 2, cfg.B - 1) for h in (0, 15)})
+    ro, rl = oracle_rows(inp, rows)
+    go = np.stack([o[b, t, h] for (b, t, h) in rows])
+    gl = np.asarray([l[b, t, h] for (b, t, h) in rows])
+    check_close("bf16", go, ro, gl, rl, "B=2728 fixed splits of 32 keys")
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
 @pytest.mark.parametrize("layout", [1, 2, 3, 4])
 def test_tight_cache_capacity(layout):
     """The cache holds exactly max_b(L_b + q_len) rows, not a multiple of the
